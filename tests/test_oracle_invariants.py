@@ -1,0 +1,251 @@
+"""Oracle invariants, the range form against the dense form, and planted mistakes (CPU)."""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+from oracle import bd_oracle as orc
+from block_diffusion_attention_amd.workloads import (Meta, make_config, random_meta, random_workload)
+from helpers import read_golden_matrix
+
+
+def _wl(meta, seed, sigma=1.0):
+    return random_workload(np.random.default_rng(seed), meta, sigma=sigma, with_do=True)
+
+
+# ------------------------------------------------- range form == dense form
+
+def _tiny_metas():
+    for B in (1, 2, 3):
+        for n in range(0, 5):
+            C = n * B
+            for q0 in sorted({0, C, min(C, B)}):
+                cands = list(range(n + 1))
+                subsets = [[]] + [[b] for b in cands] + [list(p) for p in itertools.permutations(cands, 2)]
+                for cv in subsets:
+                    if (C - q0) + len(cv) * B == 0:
+                        continue
+                    yield Meta([C], [q0], [cv], B, 2, 1, 4)
+
+
+def test_range_form_equals_dense_exhaustive():
+    rng = np.random.default_rng(0)
+    count = 0
+    for meta in _tiny_metas():
+        wl = random_workload(rng, meta)
+        mask = orc.dense_mask(meta)
+        assert mask.any(axis=1).all(), "every query sees at least its own block"
+        assert orc.visible_pairs(meta) == int(mask.sum())
+        o1, l1 = orc.attention_fwd_dense(wl.q, wl.k, wl.v, meta, mask=mask)
+        o2, l2 = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+        g1 = orc.attention_bwd_dense(wl.q, wl.k, wl.v, wl.do, meta, mask=mask)
+        g2 = orc.attention_bwd(wl.q, wl.k, wl.v, wl.do, meta)
+        for a, b in zip(g2, g1):
+            np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+        count += 1
+    assert count > 200
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_range_form_equals_dense_random(seed):
+    rng = np.random.default_rng(300 + seed)
+    meta = random_meta(rng, hq=4, hkv=2, d=8, max_segments=4, max_blocks=6)
+    wl = random_workload(rng, meta)
+    mask = orc.dense_mask(meta)
+    assert orc.visible_pairs(meta) == int(mask.sum())
+    o1, l1 = orc.attention_fwd_dense(wl.q, wl.k, wl.v, meta, mask=mask)
+    o2, l2 = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+    for a, b in zip(orc.attention_bwd(wl.q, wl.k, wl.v, wl.do, meta),
+                    orc.attention_bwd_dense(wl.q, wl.k, wl.v, wl.do, meta, mask=mask)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ closed forms
+
+def _pairs_closed_form(meta):
+    """Visible pairs by counting blocks: clean block j sees j+1 blocks, canvas b sees b+1."""
+    B = meta.block_size
+    tot = 0
+    for C, q0, cv in zip(meta.ctx_len, meta.ctx_q_begin, meta.canvas_block_idx):
+        n = C // B
+        assert q0 in (0, C)
+        if q0 == 0:
+            tot += B * B * n * (n + 1) // 2
+        tot += B * B * sum(b + 1 for b in cv)
+    return tot
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_visible_pairs_of_named_workloads(k):
+    from block_diffusion_attention_amd.workloads import config_meta
+    meta = config_meta(k, np.random.default_rng(k))
+    assert orc.visible_pairs(meta) == _pairs_closed_form(meta)
+
+
+def test_named_workload_shapes():
+    assert make_config(1).meta.tq == 80 and make_config(1).meta.tk == 80
+    w2 = make_config(2, with_do=False)
+    assert (w2.meta.tq, w2.meta.tk) == (32, 2080)
+    assert w2.q.shape == (32, 32, 128) and w2.k.shape == (2080, 8, 128)
+    from block_diffusion_attention_amd.workloads import config_meta
+    m4 = config_meta(4, np.random.default_rng(4))
+    assert (m4.tq, m4.tk) == (4864, 4864)
+    assert len(set(m4.canvas_block_idx[0])) == 24
+    m5 = config_meta(5, np.random.default_rng(5))
+    assert m5.tq == 34816
+
+
+def test_values_are_bf16_exact():
+    w = make_config(2, with_do=False)
+    u = w.q.view(np.uint32)
+    assert (u & 0xFFFF == 0).all()
+
+
+# ------------------------------------------------------------ invariants
+
+def test_constant_values_give_constant_output():
+    meta = Meta([6, 4], [0, 4], [[1, 3], [2, 0]], 2, 4, 2, 8)
+    wl = _wl(meta, 1)
+    v1 = np.ones_like(wl.v)
+    o, _ = orc.attention_fwd(wl.q, wl.k, v1, meta)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)
+
+
+def test_lse_is_logsumexp_of_visible_scores():
+    meta = Meta([6], [0], [[1, 3]], 2, 2, 1, 8)
+    wl = _wl(meta, 2)
+    mask = orc.dense_mask(meta)
+    _, lse = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    sc = 1 / np.sqrt(8)
+    for h in range(2):
+        s = sc * (wl.q[:, h].astype(np.float64) @ wl.k[:, 0].astype(np.float64).T)
+        ref = logsumexp(np.where(mask, s, -np.inf), axis=1)
+        np.testing.assert_allclose(lse[:, h], ref, rtol=0, atol=1e-12)
+
+
+def test_packing_invariance_bitwise():
+    a = Meta([6], [0], [[1, 3]], 2, 4, 2, 8)
+    b = Meta([4], [4], [[2]], 2, 4, 2, 8)
+    ab = Meta([6, 4], [0, 4], [[1, 3], [2]], 2, 4, 2, 8)
+    wa, wb = _wl(a, 3), _wl(b, 4)
+    cat = lambda x, y: np.concatenate([x, y], 0)
+    oa, la = orc.attention_fwd(wa.q, wa.k, wa.v, a)
+    ob, lb = orc.attention_fwd(wb.q, wb.k, wb.v, b)
+    oab, lab = orc.attention_fwd(cat(wa.q, wb.q), cat(wa.k, wb.k), cat(wa.v, wb.v), ab)
+    assert (oab == cat(oa, ob)).all() and (lab == cat(la, lb)).all()
+    ga = orc.attention_bwd(wa.q, wa.k, wa.v, wa.do, a)
+    gb = orc.attention_bwd(wb.q, wb.k, wb.v, wb.do, b)
+    gab = orc.attention_bwd(cat(wa.q, wb.q), cat(wa.k, wb.k), cat(wa.v, wb.v), cat(wa.do, wb.do), ab)
+    for x, y, z in zip(ga, gb, gab):
+        assert (z == cat(x, y)).all()
+
+
+def test_canvas_order_invariance():
+    B, C = 2, 6
+    cv = [1, 3, 0]
+    perm = [2, 0, 1]
+    m1 = Meta([C], [0], [cv], B, 2, 1, 8)
+    m2 = Meta([C], [0], [[cv[p] for p in perm]], B, 2, 1, 8)
+    wl = _wl(m1, 5)
+
+    def permute_rows(x, base):
+        blocks = [x[base + c * B: base + (c + 1) * B] for c in range(len(cv))]
+        return np.concatenate([x[:base]] + [blocks[p] for p in perm], 0)
+
+    q2, k2, v2, do2 = permute_rows(wl.q, C), permute_rows(wl.k, C), permute_rows(wl.v, C), permute_rows(wl.do, C)
+    o1, l1 = orc.attention_fwd(wl.q, wl.k, wl.v, m1)
+    o2, l2 = orc.attention_fwd(q2, k2, v2, m2)
+    np.testing.assert_allclose(o2, permute_rows(o1, C), rtol=0, atol=1e-14)
+    g1 = orc.attention_bwd(wl.q, wl.k, wl.v, wl.do, m1)
+    g2 = orc.attention_bwd(q2, k2, v2, do2, m2)
+    for a, b in zip(g2, g1):
+        np.testing.assert_allclose(a, permute_rows(b, C), rtol=0, atol=1e-13)
+
+
+def test_key_shift_invariance():
+    meta = Meta([6], [0], [[2, 3]], 2, 2, 1, 8)
+    wl = _wl(meta, 6)
+    c = np.random.default_rng(7).standard_normal(8) * 3.0
+    o1, l1 = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    o2, l2 = orc.attention_fwd(wl.q, wl.k + c[None, None, :], wl.v, meta)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    shift = (wl.q.astype(np.float64) @ c) / np.sqrt(8)
+    np.testing.assert_allclose(l2 - l1, shift, rtol=0, atol=1e-12)
+
+
+def test_gradient_invariants():
+    meta = Meta([6, 4], [0, 0], [[1, 3], [2]], 2, 4, 2, 8)
+    wl = _wl(meta, 8)
+    dq, dk, dv = orc.attention_bwd(wl.q, wl.k, wl.v, wl.do, meta)
+    qo, ko = meta.q_offsets(), meta.k_offsets()
+    for s in range(2):
+        for g in range(2):
+            hs = slice(2 * g, 2 * g + 2)
+            sq, sk = slice(qo[s], qo[s + 1]), slice(ko[s], ko[s + 1])
+            np.testing.assert_allclose(dv[sk, g].sum(0), wl.do[sq, hs].astype(np.float64).sum((0, 1)), atol=1e-12)
+            lhs = (wl.q[sq, hs].astype(np.float64) * dq[sq, hs]).sum()
+            rhs = (wl.k[sk, g].astype(np.float64) * dk[sk, g]).sum()
+            np.testing.assert_allclose(lhs, rhs, atol=1e-12)
+    # all value rows equal -> dp is constant along each row -> ds = 0 -> dq = dk = 0
+    v_eq = np.broadcast_to(wl.v[:1], wl.v.shape).copy()
+    dq0, dk0, _ = orc.attention_bwd(wl.q, wl.k, v_eq, wl.do, meta)
+    assert np.abs(dq0).max() < 1e-14 and np.abs(dk0).max() < 1e-14
+
+
+# ------------------------------------- planted mistakes are caught by the pins
+
+def _mutant_sees_own_clean_block(qr, kr, B):
+    qs, qc, qp, qci, qb = qr
+    ks, kc, kp, kci, _ = kr
+    if qs == ks and qc and not kc:
+        return kp // B <= qb
+    return _ORIG_VISIBLE(qr, kr, B)
+
+
+def _mutant_token_causal(qr, kr, B):
+    qs, qc, qp, _, _ = qr
+    ks, kc, kp, _, _ = kr
+    if qs == ks and not qc and not kc:
+        return kp <= qp
+    return _ORIG_VISIBLE(qr, kr, B)
+
+
+def _mutant_canvases_see_each_other(qr, kr, B):
+    qs, qc, _, _, _ = qr
+    ks, kc, _, _, _ = kr
+    if qs == ks and qc and kc:
+        return True
+    return _ORIG_VISIBLE(qr, kr, B)
+
+
+_ORIG_VISIBLE = orc.visible
+
+
+@pytest.mark.parametrize("mutant", [_mutant_sees_own_clean_block, _mutant_token_causal,
+                                    _mutant_canvases_see_each_other])
+def test_golden_mask_catches_mutants(monkeypatch, mutant):
+    gold, _ = read_golden_matrix("mask_b2_two_canvases.txt")
+    monkeypatch.setattr(orc, "visible", mutant)
+    meta = Meta([4], [0], [[1, 2]], 2, 1, 1, 4)
+    assert not (orc.dense_mask(meta) == gold.astype(bool)).all()
+
+
+def test_dense_range_check_catches_range_mutant(monkeypatch):
+    orig = orc._groups
+
+    def bad_groups(meta, segments=None):
+        for s, qidx, kidx in orig(meta, segments):
+            if len(kidx) > 1:
+                kidx = kidx[:-1]      # drop one visible key
+            yield s, qidx, kidx
+    meta = Meta([4], [0], [[1, 2]], 2, 2, 1, 4)
+    wl = _wl(meta, 1)
+    ref, _ = orc.attention_fwd_dense(wl.q, wl.k, wl.v, meta)
+    monkeypatch.setattr(orc, "_groups", bad_groups)
+    got, _ = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    assert np.abs(got - ref).max() > 1e-3
