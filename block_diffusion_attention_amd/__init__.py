@@ -5,14 +5,12 @@ kernels for gfx950); ``binding`` marshals torch tensors into it. The binding
 is imported lazily so that host-only users (workload generation, planning
 tests) do not need a GPU.
 """
+import importlib
+
 __all__ = ["binding", "workloads"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding as _b
-        return _b
-    if name == "workloads":
-        from . import workloads as _w
-        return _w
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,210 @@
+"""ctypes binding of libbdattn.so (argument marshalling only).
+
+Every step of the attention runs in the library's HIP kernels; this module only
+turns torch tensors into pointers and the metadata into the C descriptor. There
+is no CPU fallback: if the library cannot be loaded, importing this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # loaded first so the library binds to the HIP runtime torch already mapped
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbdattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
+BF16, FP32 = 0, 1
+FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD = 1, 2, 4
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with block_diffusion_attention_amd/build.py")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("num_segments", ctypes.c_int32),
+        ("ctx_len", _i32p),
+        ("ctx_q_begin", _i32p),
+        ("canvas_offsets", _i32p),
+        ("canvas_block_idx", _i32p),
+        ("block_size", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_lib.bd_attn_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(_vp)]
+_lib.bd_attn_plan_sizes.argtypes = [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                    ctypes.POINTER(ctypes.c_int64)]
+_lib.bd_attn_plan_serialize.argtypes = [_vp, _vp, _sz]
+_lib.bd_attn_plan_upload.argtypes = [_vp, _vp, _vp]
+_lib.bd_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.bd_attn_bwd.argtypes = [_vp] * 13
+_lib.bd_attn_plan_destroy.argtypes = [_vp]
+_lib.bd_attn_last_error.restype = ctypes.c_char_p
+_lib.bd_attn_version.restype = ctypes.c_char_p
+for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
+           "bd_attn_fwd", "bd_attn_bwd", "bd_attn_plan_destroy"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
+            "bd_attn_fwd", "bd_attn_bwd", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version")
+
+
+class BdAttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"bd_attn status {status}: {msg}")
+        self.status = status
+
+
+def _check(st):
+    if st != OK:
+        raise BdAttnError(st, _lib.bd_attn_last_error().decode())
+
+
+def version() -> str:
+    return _lib.bd_attn_version().decode()
+
+
+def _arr(vals):
+    a = (ctypes.c_int32 * max(1, len(vals)))(*[int(x) for x in vals])
+    return a
+
+
+class Plan:
+    """A validated plan (host work lists) plus, once uploaded, its device copy."""
+
+    def __init__(self, meta, flags: int = 0):
+        self.meta = meta
+        self._keep = [_arr(meta.ctx_len), _arr(meta.ctx_q_begin), _arr(meta.canvas_offsets),
+                      _arr(meta.flat_canvas_block_idx)]
+        d = Desc()
+        d.num_segments = len(meta.ctx_len)
+        d.ctx_len = ctypes.cast(self._keep[0], _i32p)
+        d.ctx_q_begin = ctypes.cast(self._keep[1], _i32p)
+        d.canvas_offsets = ctypes.cast(self._keep[2], _i32p)
+        d.canvas_block_idx = ctypes.cast(self._keep[3], _i32p)
+        d.block_size = meta.block_size
+        d.num_q_heads = meta.num_q_heads
+        d.num_kv_heads = meta.num_kv_heads
+        d.head_dim = meta.head_dim
+        d.dtype = BF16 if meta.dtype == "bf16" else FP32
+        d.softmax_scale = float(meta.softmax_scale)
+        d.flags = flags
+        h = _vp()
+        _check(_lib.bd_attn_plan(ctypes.byref(d), ctypes.byref(h)))
+        self.handle = h
+        tq, tk = ctypes.c_int64(), ctypes.c_int64()
+        mb, wf, wb = _sz(), _sz(), _sz()
+        pairs = ctypes.c_int64()
+        _check(_lib.bd_attn_plan_sizes(h, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(mb),
+                                       ctypes.byref(wf), ctypes.byref(wb), ctypes.byref(pairs)))
+        self.tq, self.tk = tq.value, tk.value
+        self.meta_bytes, self.ws_fwd_bytes, self.ws_bwd_bytes = mb.value, wf.value, wb.value
+        self.visible_pairs = pairs.value
+        self.dtype = torch.bfloat16 if meta.dtype == "bf16" else torch.float32
+        self.meta_dev: Optional[torch.Tensor] = None
+        self.ws_fwd: Optional[torch.Tensor] = None
+        self.ws_bwd: Optional[torch.Tensor] = None
+
+    def host_blob(self):
+        buf = (ctypes.c_int32 * (self.meta_bytes // 4))()
+        _check(_lib.bd_attn_plan_serialize(self.handle, ctypes.cast(buf, _vp), self.meta_bytes))
+        return list(buf)
+
+    def upload(self, device="cuda"):
+        """Allocates (torch) and fills the device metadata buffer and workspaces."""
+        dev = torch.device(device)
+        self.meta_dev = torch.empty(max(16, self.meta_bytes), dtype=torch.uint8, device=dev)
+        _check(_lib.bd_attn_plan_upload(self.handle, _vp(self.meta_dev.data_ptr()), _stream(dev)))
+        # the copy reads the plan's host memory: finish it before anything can free the plan
+        torch.cuda.current_stream(dev).synchronize()
+        self.ws_fwd = torch.empty(max(16, self.ws_fwd_bytes), dtype=torch.uint8, device=dev) if self.ws_fwd_bytes else None
+        self.ws_bwd = torch.empty(max(16, self.ws_bwd_bytes), dtype=torch.uint8, device=dev)
+        return self
+
+    def __del__(self, _destroy=_lib.bd_attn_plan_destroy):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            _destroy(h)
+            self.handle = None
+
+
+def _stream(dev) -> _vp:
+    return _vp(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> _vp:
+    return _vp(0 if t is None else t.data_ptr())
+
+
+def _expect(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} cuda={t.is_cuda}")
+
+
+def fwd(plan: Plan, q, k, v, o=None, lse=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    m = plan.meta
+    _expect(q, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "q")
+    _expect(k, (plan.tk, m.num_kv_heads, m.head_dim), plan.dtype, "k")
+    _expect(v, (plan.tk, m.num_kv_heads, m.head_dim), plan.dtype, "v")
+    if plan.meta_dev is None:
+        plan.upload(q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((plan.tq, m.num_q_heads), dtype=torch.float32, device=q.device)
+    _check(_lib.bd_attn_fwd(plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                            _ptr(plan.ws_fwd), _stream(q.device)))
+    return o, lse
+
+
+def bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
+    m = plan.meta
+    _expect(do, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "do")
+    _expect(o, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "o")
+    _expect(lse, (plan.tq, m.num_q_heads), torch.float32, "lse")
+    if plan.meta_dev is None:
+        plan.upload(q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(_lib.bd_attn_bwd(plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(plan.ws_bwd), _stream(q.device)))
+    return dq, dk, dv
+
+
+class BdAttnFunction(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in libbdattn."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, plan):
+        o, lse = fwd(plan, q.contiguous(), k.contiguous(), v.contiguous())
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.plan = plan
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(ctx.plan, q, k, v, o, lse, do.contiguous())
+        return dq, dk, dv, None
+
+
+def attention(q, k, v, plan: Plan):
+    return BdAttnFunction.apply(q, k, v, plan)

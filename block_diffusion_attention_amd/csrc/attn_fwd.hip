@@ -1,0 +1,293 @@
+// Forward staircase block-diffusion attention for gfx950 (bf16 in, fp32 accumulate).
+//
+// One workgroup (4 waves) handles one query tile of up to 128 rows (tokens x
+// the query heads of one kv head, so the grouped heads share every K/V tile)
+// over the key tiles of its visible ranges: the clean context below the tile's
+// limit and, for a canvas, the canvas' own keys (ORL paper, section 3.2
+// "Staircase attention kernel"; appendix D.2 paragraph on the kernel: ranges
+// from per-document metadata, invisible tiles never visited, the predicate
+// only inside boundary tiles).
+//
+// Per wave, 32 query rows. Scores are computed transposed, S^T = K Q^T, with
+// the 32x32x16 MFMA so that each lane owns one query row: row maxima and sums
+// need one cross-half exchange instead of a 32-lane reduction, and the
+// probabilities feed the P V product straight from registers. V is staged in
+// LDS transposed (a 4x8 register transpose per loader thread) so that its MFMA
+// operand is one 16-byte LDS read.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace bdattn {
+
+namespace {
+
+template <int D>
+struct FwdTileLoader {
+  static constexpr int CH = D / 8;        // 16-byte chunks per row
+  static constexpr int KG = D / 32;       // keys per loader thread (64 keys x CH chunks / 256 threads)
+  int lc, lg;
+  u32x4 pk[KG], pv[KG];
+
+  __device__ void init(int tid) { lc = tid % CH; lg = tid / CH; }
+
+  __device__ void load(const bf16* __restrict__ K, const bf16* __restrict__ V, int hkv, int kvh,
+                       int base, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < KG; ++i) {
+      const int key = lg * KG + i;
+      if (key < nvalid) {
+        const int64_t off = ((int64_t)(base + key) * hkv + kvh) * D + lc * 8;
+        pk[i] = *reinterpret_cast<const u32x4*>(K + off);
+        pv[i] = *reinterpret_cast<const u32x4*>(V + off);
+      } else {
+        pk[i] = u32x4{0, 0, 0, 0};
+        pv[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
+  __device__ void store_k(bf16* sK) const {
+#pragma unroll
+    for (int i = 0; i < KG; ++i)
+      *reinterpret_cast<u32x4*>(sK + NatTile<D>::off(lg * KG + i, lc * 8)) = pk[i];
+  }
+
+  // V^T: element e of the 16-byte chunk becomes row lc*8+e, the KG keys become
+  // KG contiguous columns (kperm keeps aligned groups of 4 together).
+  __device__ void store_vt(bf16* sVt) const {
+    const int col = kperm(lg * KG);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = lc * 8 + e;
+      const int w = e >> 1;
+      if constexpr (KG == 4) {
+        *reinterpret_cast<u32x2*>(sVt + TrTile<kKTile>::off(d, col)) =
+            u32x2{pick_pair(pv[0][w], pv[1][w], e & 1), pick_pair(pv[2][w], pv[3][w], e & 1)};
+      } else {
+        *reinterpret_cast<uint32_t*>(sVt + TrTile<kKTile>::off(d, col)) = pick_pair(pv[0][w], pv[1][w], e & 1);
+      }
+    }
+  }
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
+  constexpr int KT = kKTile;
+  constexpr int NDB = D / 32;
+  constexpr int NKS = D / 16;
+  __shared__ __attribute__((aligned(16))) bf16 sK[KT * NatTile<D>::kStride];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[D * KT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 31, h = lane >> 5;
+  const int idx = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
+  const int4 itv = reinterpret_cast<const int4*>(a.items)[idx];
+  if (itv.x < 0) return;
+  const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
+  const QTile qt = load_qtile(a.qtiles, itv.x);
+  const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
+  const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
+  const bf16* __restrict__ V = static_cast<const bf16*>(a.v);
+
+  const int G = a.G;
+  const int row = wave * 32 + j;
+  int t = row / G;
+  const int gh = row - t * G;
+  const bool row_ok = row < qt.n_tok * G;
+  if (t >= qt.n_tok) t = qt.n_tok - 1;          // padding rows mirror the last token
+  const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * G + gh;
+
+  bf16x8 qf[NKS];
+  {
+    const bf16* qp = Q + qrow * D + h * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
+  }
+  const int L = row_limit(qt, t, a.B);
+  const int n1 = (qt.lim_max + KT - 1) / KT;
+
+  FwdTileLoader<D> ld;
+  ld.init(tid);
+  auto tile_geom = [&](int kt, int& base, int& nvalid) {
+    if (kt < n1) { base = qt.k_ctx + kt * KT; nvalid = min(KT, qt.lim_max - kt * KT); }
+    else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
+  };
+  {
+    int base, nv;
+    tile_geom(kt_begin, base, nv);
+    ld.load(K, V, a.hkv, kvh, base, nv);
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    __syncthreads();
+    ld.store_k(sK);
+    ld.store_vt(sVt);
+    __syncthreads();
+    const bool r1 = kt < n1;
+    const int kpos0 = r1 ? kt * KT : (kt - n1) * KT;
+    const int lim = r1 ? L : qt.n_own;
+    const bool need_mask = kpos0 + KT > (r1 ? qt.lim_min : qt.n_own);
+    if (kt + 1 < kt_end) {
+      int base, nv;
+      tile_geom(kt + 1, base, nv);
+      ld.load(K, V, a.hkv, kvh, base, nv);
+    }
+
+    // S^T = K Q^T : two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const bf16* kp = sK + NatTile<D>::off(kb * 32 + j, h * 8);
+#pragma unroll
+      for (int kk = 0; kk < NKS; ++kk)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qf[kk], s[kb]);
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kb][r] * a.scale_log2;
+        if (need_mask && (kpos0 + kb * 32 + c_row(r, h) >= lim)) x = -INFINITY;
+        s[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, swap_halves(mx));
+    const bool need = mx > m + kRescaleSlack;
+    if (__any(need)) {
+      const float mnew = need ? mx : m;
+      const float alpha = need ? fast_exp2(m - mnew) : 1.f;
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[kb][r] - mref);
+        s[kb][r] = p;
+        ls += p;
+      }
+    l += ls;
+
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      float tmp[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tmp[e] = s[kq >> 1][(kq & 1) * 8 + e];
+      pb[kq] = pack8(tmp);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 32 + j;
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+        acc[db] = mfma32(*reinterpret_cast<const bf16x8*>(sVt + TrTile<KT>::off(d, kq * 16 + h * 8)),
+                         pb[kq], acc[db]);
+    }
+  }
+
+  const float lt = l + swap_halves(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  if (a.part_o) {
+    float* po = a.part_o + ((int64_t)idx * kQRows + row) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[db][g4 * 4 + e] * inv;
+        *reinterpret_cast<f32x4*>(po + db * 32 + g4 * 8 + h * 4) = v;
+      }
+    if (h == 0) a.part_lse[(int64_t)idx * kQRows + row] = lse;
+  } else if (row_ok) {
+    bf16* op = static_cast<bf16*>(a.o) + qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 v;
+        v[0] = pack_bf16x2(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
+        v[1] = pack_bf16x2(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + db * 32 + g4 * 8 + h * 4) = v;
+      }
+    if (h == 0) a.lse[qrow] = lse;
+  }
+}
+
+// Merges the split partial results of one query tile: lse = log sum_i exp(lse_i),
+// O = sum_i exp(lse_i - lse) O_i.
+template <int D, bool BF16>
+__global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
+  const int4 it = reinterpret_cast<const int4*>(a.items)[blockIdx.x];
+  const QTile qt = load_qtile(a.qtiles, it.x);
+  const int kvh = it.y, first = it.z, count = it.w;
+  const int rows = qt.n_tok * a.G;
+  constexpr int C4 = D / 4;
+  for (int u = threadIdx.x; u < rows * C4; u += blockDim.x) {
+    const int row = u / C4, c = u - row * C4;
+    float mx = -INFINITY;
+    for (int i = 0; i < count; ++i) mx = fmaxf(mx, a.part_lse[(int64_t)(first + i) * kQRows + row]);
+    float wsum = 0.f;
+    f32x4 accv = f32x4{};
+    if (mx != -INFINITY) {
+      for (int i = 0; i < count; ++i) {
+        const float w = __expf(a.part_lse[(int64_t)(first + i) * kQRows + row] - mx);
+        wsum += w;
+        const f32x4 po = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)(first + i) * kQRows + row) * D + c * 4);
+        accv += w * po;
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int t = row / a.G, gh = row - t * a.G;
+    const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * a.G + gh;
+    if (BF16) {
+      u32x2 v;
+      v[0] = pack_bf16x2(accv[0] * inv, accv[1] * inv);
+      v[1] = pack_bf16x2(accv[2] * inv, accv[3] * inv);
+      *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.o) + qrow * D + c * 4) = v;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + qrow * D + c * 4) = accv * inv;
+    }
+    if (c == 0) a.lse[qrow] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128) {
+    if (bf16_out) hipLaunchKernelGGL((combine_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (bf16_out) hipLaunchKernelGGL((combine_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bdattn

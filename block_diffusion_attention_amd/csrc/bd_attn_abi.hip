@@ -1,0 +1,195 @@
+// C ABI of libbdattn.so: argument checks, plan handling and kernel launches.
+// Every entry point returns a status; no exception crosses the boundary.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/bd_attn.h"
+#include "kernels.h"
+#include "planner.h"
+
+using bdattn::Plan;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bd_attn_status fail(bd_attn_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bd_attn_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(BD_ATTN_EINVAL, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(BD_ATTN_EINVAL, std::string(name) + " is not 16-byte aligned");
+  return BD_ATTN_OK;
+}
+
+bd_attn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BD_ATTN_OK;
+  return fail(BD_ATTN_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class T>
+const T* section(const void* meta, int64_t off) {
+  return reinterpret_cast<const T*>(static_cast<const int32_t*>(meta) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+bd_attn_status bd_attn_plan(const bd_attn_desc* desc, bd_attn_plan_t* out) {
+  if (!out) return fail(BD_ATTN_EINVAL, "out is NULL");
+  try {
+    auto* h = new bd_attn_plan_s;
+    std::string err;
+    const bd_attn_status st = bdattn::build_plan(desc, &h->p, &err);
+    if (st != BD_ATTN_OK) {
+      delete h;
+      return fail(st, err);
+    }
+    *out = h;
+    return BD_ATTN_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(BD_ATTN_EINVAL, "out of host memory while planning");
+  } catch (...) {
+    return fail(BD_ATTN_EINVAL, "unexpected error while planning");
+  }
+}
+
+bd_attn_status bd_attn_plan_sizes(bd_attn_plan_t plan, int64_t* tq, int64_t* tk, size_t* meta_bytes,
+                                  size_t* ws_fwd_bytes, size_t* ws_bwd_bytes, int64_t* visible_pairs) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  const Plan& p = plan->p;
+  if (tq) *tq = p.tq;
+  if (tk) *tk = p.tk;
+  if (meta_bytes) *meta_bytes = p.blob.size() * sizeof(int32_t);
+  if (ws_fwd_bytes) *ws_fwd_bytes = p.ws_fwd;
+  if (ws_bwd_bytes) *ws_bwd_bytes = p.ws_bwd;
+  if (visible_pairs) *visible_pairs = p.pairs;
+  return BD_ATTN_OK;
+}
+
+bd_attn_status bd_attn_plan_serialize(bd_attn_plan_t plan, void* meta_host, size_t bytes) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  if (!meta_host) return fail(BD_ATTN_EINVAL, "meta_host is NULL");
+  const size_t need = plan->p.blob.size() * sizeof(int32_t);
+  if (bytes < need) return fail(BD_ATTN_EWORKSPACE, "meta_host buffer smaller than meta_bytes");
+  std::memcpy(meta_host, plan->p.blob.data(), need);
+  return BD_ATTN_OK;
+}
+
+bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_stream_t stream) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  if (bd_attn_status st = check_ptr(meta_dev, "meta_dev")) return st;
+  const size_t need = plan->p.blob.size() * sizeof(int32_t);
+  return hip_status(hipMemcpyAsync(meta_dev, plan->p.blob.data(), need, hipMemcpyHostToDevice,
+                                   reinterpret_cast<hipStream_t>(stream)),
+                    "hipMemcpyAsync(meta)");
+}
+
+bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                           const void* v, void* o, float* lse, void* ws, bd_attn_stream_t stream) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  const Plan& p = plan->p;
+  bd_attn_status st;
+  if ((st = check_ptr(meta_dev, "meta_dev")) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
+      (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
+    return st;
+  const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
+  const bool split = bf16 && p.split;
+  if (split) {
+    if (!ws) return fail(BD_ATTN_EWORKSPACE, "this plan needs a forward workspace (ws_fwd_bytes)");
+    if (!aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  bdattn::FwdArgs a{};
+  a.qtiles = section<int32_t>(meta_dev, p.off_qtiles);
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.B = p.desc.block_size;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  const int D = p.desc.head_dim;
+  hipError_t e;
+  if (!bf16) {
+    a.items = section<bdattn::FwdItem>(meta_dev, p.off_dq);
+    e = bdattn::launch_fwd_f32(a, D, (int)p.dq_items.size(), s);
+    return hip_status(e, "fwd_f32 launch");
+  }
+  a.items = section<bdattn::FwdItem>(meta_dev, p.off_fwd);
+  if (!split) {
+    e = bdattn::launch_fwd_bf16(a, D, (int)p.fwd_items.size(), s);
+    return hip_status(e, "fwd launch");
+  }
+  a.order = section<int32_t>(meta_dev, p.off_fwd_order);
+  a.part_o = static_cast<float*>(ws);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_lse);
+  e = bdattn::launch_fwd_bf16(a, D, (int)p.fwd_order.size(), s);
+  if ((st = hip_status(e, "fwd (split) launch"))) return st;
+  bdattn::CombArgs c{};
+  c.qtiles = a.qtiles;
+  c.items = section<bdattn::CombItem>(meta_dev, p.off_comb);
+  c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
+  c.hq = a.hq; c.G = a.G;
+  e = bdattn::launch_combine(c, D, true, (int)p.comb_items.size(), s);
+  return hip_status(e, "combine launch");
+}
+
+bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, void* ws, bd_attn_stream_t stream) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  const Plan& p = plan->p;
+  bd_attn_status st;
+  if ((st = check_ptr(meta_dev, "meta_dev")) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
+      (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")) ||
+      (st = check_ptr(dout, "dout")) || (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) ||
+      (st = check_ptr(dv, "dv")))
+    return st;
+  if (!ws) return fail(BD_ATTN_EWORKSPACE, "bd_attn_bwd needs a workspace of ws_bwd_bytes");
+  if (!aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
+  const int D = p.desc.head_dim;
+  bdattn::BwdArgs a{};
+  a.qtiles = section<int32_t>(meta_dev, p.off_qtiles);
+  a.dq_items = section<bdattn::FwdItem>(meta_dev, p.off_dq);
+  a.ktiles = section<int32_t>(meta_dev, p.off_ktiles);
+  a.canvq = section<bdattn::CanvasQ>(meta_dev, p.off_canvq);
+  a.bwd_items = section<bdattn::BwdItem>(meta_dev, p.off_bwd);
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.delta = static_cast<float*>(ws);
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.rows_q = p.tq * p.desc.num_q_heads;
+  a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.B = p.desc.block_size;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  hipError_t e = bdattn::launch_bwd_pre(a, D, bf16, s);
+  if ((st = hip_status(e, "bwd_pre launch"))) return st;
+  if (bf16) {
+    e = bdattn::launch_dkdv_bf16(a, D, (int)p.bwd_items.size(), s);
+    if ((st = hip_status(e, "dkdv launch"))) return st;
+    e = bdattn::launch_dq_bf16(a, D, (int)p.dq_items.size(), s);
+    return hip_status(e, "dq launch");
+  }
+  e = bdattn::launch_dkdv_f32(a, D, (int)p.bwd_items.size(), s);
+  if ((st = hip_status(e, "dkdv_f32 launch"))) return st;
+  e = bdattn::launch_dq_f32(a, D, (int)p.dq_items.size(), s);
+  return hip_status(e, "dq_f32 launch");
+}
+
+bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan) {
+  delete plan;
+  return BD_ATTN_OK;
+}
+
+const char* bd_attn_last_error(void) { return g_last_error.c_str(); }
+
+const char* bd_attn_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Work-list records shared by the host planner and the gfx950 kernels.
+//
+// Visibility is never stored as a mask: a query tile carries the ranges of keys
+// it can see and a key tile the ranges of queries that can see it, both derived
+// from the per-segment metadata (ORL paper, appendix D.2 paragraph on the
+// kernel: visible key ranges come from per-document metadata, invisible tiles
+// are skipped, the predicate is applied only inside boundary tiles; dK/dV use
+// valid query ranges per key tile).
+//
+// Row limit. Every query row r has a limit L(r) on the context positions of the
+// clean keys it sees (positions p < L(r)):
+//   clean query at context position t : L = (t / B + 1) * B  (block-causal)
+//   query of a canvas at block index b: L = b * B           (blocks before b)
+// and a canvas query additionally sees the B keys of its own canvas.
+#pragma once
+#include <stdint.h>
+
+namespace bdattn {
+
+// Query tile: up to kQRows rows, row r = token (r / G) x head (r % G) of one kv head.
+constexpr int kQRows = 128;
+// Forward / dQ key tile (keys per main-loop step).
+constexpr int kKTile = 64;
+// dK/dV: keys per workgroup (4 waves x 32) and query rows per inner step.
+constexpr int kKBlock = 128;
+constexpr int kQChunk = 32;
+
+// Serialized plan: a header of kBlobHeaderInts int32 (magic, format version,
+// then count and int32 offset of each section: query tiles, forward items,
+// forward launch order, combine items, dQ items, key tiles, canvas-query
+// entries, dK/dV items), followed by the sections, each 16-byte aligned.
+constexpr int kBlobHeaderInts = 32;
+constexpr int32_t kBlobMagic = 0x62646174;   // "bdat"
+
+struct QTile {         // 8 x int32
+  int32_t q_tok;       // first packed query token
+  int32_t n_tok;       // tokens in the tile (>= 1)
+  int32_t k_ctx;       // packed index of the segment's first clean key
+  int32_t pos0;        // context position of the first token, or -1 for a canvas tile
+  int32_t lim_max;     // clean keys [k_ctx, k_ctx + lim_max) may be visible to some row
+  int32_t lim_min;     // every row sees at least the clean keys below lim_min
+  int32_t k_own;       // packed index of the canvas' own keys (canvas tile)
+  int32_t n_own;       // own canvas keys (B for a canvas tile, 0 for a clean tile)
+};
+
+struct FwdItem {       // 4 x int32: one workgroup of the forward / dQ kernels
+  int32_t qtile;       // index into the query-tile list, or -1 for an empty slot
+  int32_t kvh;         // kv head
+  int32_t kt_begin;    // first key tile (tiles of range 1, then of range 2)
+  int32_t kt_end;      // one past the last key tile
+};
+
+struct CombItem {      // 4 x int32: merge of the split partial results of one query tile
+  int32_t qtile;
+  int32_t kvh;
+  int32_t first;       // index of the first split item (partial slot)
+  int32_t count;       // number of consecutive split items
+};
+
+struct KTile {         // 8 x int32
+  int32_t k_tok;       // first packed key token
+  int32_t n_keys;      // keys in the tile (1..kKBlock)
+  int32_t p0;          // context position of the first key, or -1 for canvas keys
+  int32_t cq_tok;      // first packed query token of the clean query range
+  int32_t cq_len;      // clean query tokens that may see the tile (0 if none)
+  int32_t cq_pos;      // context position of cq_tok
+  int32_t cv_begin;    // first entry of the canvas-query list
+  int32_t cv_count;    // canvas-query entries that may see the tile
+};
+
+struct CanvasQ {       // 4 x int32
+  int32_t q_tok;       // first packed query token of the canvas
+  int32_t n_tok;       // B
+  int32_t lim;         // b * B: clean context positions visible to the canvas
+  int32_t own;         // 1 for the entry of a canvas key tile (sees all of the tile)
+};
+
+struct BwdItem {       // 4 x int32: one workgroup of the dK/dV kernel
+  int32_t ktile;       // index into the key-tile list, or -1 for an empty slot
+  int32_t kvh;
+  int32_t pad0;
+  int32_t pad1;
+};
+
+static_assert(sizeof(QTile) == 32, "QTile layout");
+static_assert(sizeof(KTile) == 32, "KTile layout");
+
+}  // namespace bdattn

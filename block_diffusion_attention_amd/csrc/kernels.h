@@ -1,0 +1,68 @@
+// Kernel argument blocks and host-side launchers (one per kernel family).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bd_records.h"
+
+namespace bdattn {
+
+struct FwdArgs {
+  const int32_t* qtiles;
+  const FwdItem* items;
+  const int32_t* order;      // launch order over items (split mode) or NULL
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* part_o;             // split mode: partial O [slot][kQRows][D] fp32, else NULL
+  float* part_lse;           // split mode: partial LSE [slot][kQRows]
+  int hq, hkv, G, B;
+  float scale_log2;          // softmax scale * log2(e)
+  float scale;               // softmax scale
+};
+
+struct CombArgs {
+  const int32_t* qtiles;
+  const CombItem* items;
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;
+  int hq, G;
+};
+
+struct BwdArgs {
+  const int32_t* qtiles;     // dQ kernel
+  const FwdItem* dq_items;
+  const int32_t* ktiles;     // dK/dV kernel
+  const CanvasQ* canvq;
+  const BwdItem* bwd_items;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;              // [Tq, Hq] fp32 (workspace)
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t rows_q;            // Tq * Hq
+  int hq, hkv, G, B;
+  float scale_log2;
+  float scale;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int grid, hipStream_t s);
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
+
+hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_dkdv_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_dq_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
+
+}  // namespace bdattn

@@ -1,0 +1,384 @@
+// Host planner: validates the per-segment metadata and derives the work lists
+// (query tiles with their visible key ranges, key tiles with their visible query
+// ranges), ordered largest-cost-first and grouped per XCD.
+//
+// The visibility rule and the range derivation follow the ORL paper, section 3.2
+// "Staircase attention kernel" and the appendix D.2 paragraph on the kernel; the
+// largest-cost-first order follows section 3.2 "Packed and cost-balanced state
+// training" / appendix D.3, applied here to workgroups instead of data-parallel
+// groups. Pure C++17, no HIP calls.
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <string>
+
+namespace bdattn {
+
+namespace {
+
+constexpr int kNumXcd = 8;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Orders work items for launch: workgroup i is dispatched to XCD i % 8. Items
+// of one affinity class (same segment and kv head, i.e. the same K/V or Q/dO
+// rows) are kept on one XCD so they share its L2; classes go to XCDs
+// largest-total-first; inside an XCD items run largest-cost-first. Falls back to
+// one global largest-cost-first order when the class split is unbalanced.
+// Returns item indices, -1 for empty slots.
+std::vector<int32_t> launch_order(const std::vector<int64_t>& cost,
+                                  const std::vector<int64_t>& cls, bool xcd_groups) {
+  const int64_t n = (int64_t)cost.size();
+  std::vector<int32_t> idx(n);
+  std::iota(idx.begin(), idx.end(), 0);
+  auto by_cost = [&](int32_t a, int32_t b) {
+    if (cost[a] != cost[b]) return cost[a] > cost[b];
+    if (cls[a] != cls[b]) return cls[a] < cls[b];
+    return a < b;
+  };
+  std::sort(idx.begin(), idx.end(), by_cost);
+  if (!xcd_groups || n < 2 * kNumXcd) return idx;
+
+  // class totals
+  int64_t ncls = 0;
+  for (auto c : cls) ncls = std::max<int64_t>(ncls, c + 1);
+  if (ncls < kNumXcd) return idx;
+  std::vector<int64_t> tot(ncls, 0);
+  int64_t maxc = 0, sum = 0;
+  for (int64_t i = 0; i < n; ++i) { tot[cls[i]] += cost[i]; maxc = std::max(maxc, cost[i]); sum += cost[i]; }
+  std::vector<int64_t> corder(ncls);
+  std::iota(corder.begin(), corder.end(), 0);
+  std::sort(corder.begin(), corder.end(), [&](int64_t a, int64_t b) {
+    return tot[a] != tot[b] ? tot[a] > tot[b] : a < b; });
+  std::vector<int64_t> load(kNumXcd, 0);
+  std::vector<int> cx(ncls, 0);
+  for (int64_t c : corder) {
+    int best = 0;
+    for (int x = 1; x < kNumXcd; ++x) if (load[x] < load[best]) best = x;
+    cx[c] = best;
+    load[best] += tot[c];
+  }
+  int64_t mx = *std::max_element(load.begin(), load.end());
+  double mean = (double)sum / kNumXcd;
+  if ((double)mx > 1.03 * mean + (double)maxc) return idx;   // unbalanced: keep global order
+
+  std::vector<std::vector<int32_t>> per(kNumXcd);
+  for (int32_t i : idx) per[cx[cls[i]]].push_back(i);       // idx is already cost-sorted
+  size_t rows = 0;
+  for (auto& p : per) rows = std::max(rows, p.size());
+  std::vector<int32_t> out(rows * kNumXcd, -1);
+  for (int x = 0; x < kNumXcd; ++x)
+    for (size_t r = 0; r < per[x].size(); ++r) out[r * kNumXcd + x] = per[x][r];
+  // drop trailing empty slots
+  while (!out.empty() && out.back() < 0) out.pop_back();
+  return out;
+}
+
+template <class T>
+void append_records(std::vector<int32_t>& blob, const std::vector<T>& v, int64_t& off) {
+  // 16-byte aligned sections
+  while (blob.size() % 4) blob.push_back(0);
+  off = (int64_t)blob.size();
+  const int32_t* p = reinterpret_cast<const int32_t*>(v.data());
+  blob.insert(blob.end(), p, p + v.size() * (sizeof(T) / sizeof(int32_t)));
+}
+
+}  // namespace
+
+bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
+  if (!d) { *err = "desc is NULL"; return BD_ATTN_EINVAL; }
+  const int S = d->num_segments;
+  if (S < 1) { *err = "num_segments must be >= 1"; return BD_ATTN_EINVAL; }
+  if (!d->ctx_len || !d->canvas_offsets) { *err = "ctx_len and canvas_offsets must not be NULL"; return BD_ATTN_EINVAL; }
+  const int B = d->block_size;
+  if (B < 1) { *err = "block_size must be >= 1"; return BD_ATTN_EINVAL; }
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1) { *err = "head counts must be >= 1"; return BD_ATTN_EINVAL; }
+  if (d->num_q_heads % d->num_kv_heads) { *err = "num_q_heads must be a multiple of num_kv_heads"; return BD_ATTN_EINVAL; }
+  if (d->dtype != BD_ATTN_BF16 && d->dtype != BD_ATTN_FP32) { *err = "unknown dtype"; return BD_ATTN_EINVAL; }
+  if (d->head_dim < 1) { *err = "head_dim must be >= 1"; return BD_ATTN_EINVAL; }
+  if (d->head_dim != 64 && d->head_dim != 128) { *err = "head_dim must be 64 or 128"; return BD_ATTN_EUNSUPPORTED; }
+  if (!(std::isfinite(d->softmax_scale))) { *err = "softmax_scale must be finite"; return BD_ATTN_EINVAL; }
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G > kQChunk) { *err = "group size num_q_heads/num_kv_heads above 32 is not supported"; return BD_ATTN_EUNSUPPORTED; }
+  if (d->canvas_offsets[0] != 0) { *err = "canvas_offsets[0] must be 0"; return BD_ATTN_EINVAL; }
+  for (int s = 0; s < S; ++s)
+    if (d->canvas_offsets[s + 1] < d->canvas_offsets[s]) { *err = "canvas_offsets must be non-decreasing"; return BD_ATTN_EINVAL; }
+  const int64_t ncv = d->canvas_offsets[S];
+  if (ncv > 0 && !d->canvas_block_idx) { *err = "canvas_block_idx must not be NULL"; return BD_ATTN_EINVAL; }
+
+  Plan& p = *P;
+  p.desc = *d;
+  p.desc.ctx_len = nullptr; p.desc.ctx_q_begin = nullptr;
+  p.desc.canvas_offsets = nullptr; p.desc.canvas_block_idx = nullptr;
+  p.G = G;
+  p.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
+  p.ctx.assign(d->ctx_len, d->ctx_len + S);
+  p.q0.assign(S, 0);
+  if (d->ctx_q_begin) p.q0.assign(d->ctx_q_begin, d->ctx_q_begin + S);
+  p.coff.assign(d->canvas_offsets, d->canvas_offsets + S + 1);
+  p.cb.assign(d->canvas_block_idx, d->canvas_block_idx + ncv);
+
+  int64_t tq = 0, tk = 0, pairs = 0;
+  const int64_t kMaxTok = (int64_t)INT32_MAX / 2;
+  for (int s = 0; s < S; ++s) {
+    const int64_t C = p.ctx[s], q0 = p.q0[s];
+    if (C < 0 || C % B) { *err = "ctx_len[" + std::to_string(s) + "] must be >= 0 and a multiple of block_size"; return BD_ATTN_EINVAL; }
+    if (q0 < 0 || q0 > C) { *err = "ctx_q_begin[" + std::to_string(s) + "] must lie in [0, ctx_len]"; return BD_ATTN_EINVAL; }
+    const int64_t n = C / B;
+    const int64_t m = p.coff[s + 1] - p.coff[s];
+    for (int64_t c = p.coff[s]; c < p.coff[s + 1]; ++c)
+      if (p.cb[c] < 0 || p.cb[c] > n) { *err = "canvas_block_idx[" + std::to_string(c) + "] must lie in [0, ctx_len/block_size]"; return BD_ATTN_EINVAL; }
+    tq += (C - q0) + m * B;
+    tk += C + m * B;
+    if (tq > kMaxTok || tk > kMaxTok) { *err = "packed token count too large"; return BD_ATTN_EINVAL; }
+    // visible pairs: clean block j (queries from q0) sees (j+1)B keys; canvas b sees bB + B
+    for (int64_t j = q0 / B; j < n; ++j) {
+      const int64_t lo = std::max(q0, j * B), hi = (j + 1) * B;
+      pairs += (hi - lo) * (j + 1) * B;
+    }
+    for (int64_t c = p.coff[s]; c < p.coff[s + 1]; ++c) pairs += (int64_t)B * ((int64_t)p.cb[c] * B + B);
+  }
+  if (tq == 0) { *err = "the batch has no query tokens"; return BD_ATTN_EINVAL; }
+  if (tq * d->num_q_heads > (int64_t)INT32_MAX || tk * d->num_kv_heads > (int64_t)INT32_MAX) {
+    *err = "tensor rows (tokens x heads) must fit in int32"; return BD_ATTN_EINVAL; }
+  p.tq = tq; p.tk = tk; p.pairs = pairs;
+
+  const bool xcd = !(d->flags & BD_ATTN_FLAG_NO_XCD);
+  const int Hkv = d->num_kv_heads;
+  const int QT = std::max(1, kQRows / G);         // tokens per query tile
+  p.qt_tokens = QT;
+
+  // ---------------- query tiles (forward, dQ)
+  p.qtiles.clear();
+  std::vector<int> qtile_seg;
+  {
+    int64_t qo = 0, ko = 0;
+    for (int s = 0; s < S; ++s) {
+      const int64_t C = p.ctx[s], q0 = p.q0[s];
+      const int64_t m = p.coff[s + 1] - p.coff[s];
+      // clean queries, tiles of QT tokens that stay inside one block when B >= QT
+      for (int64_t t = q0; t < C;) {
+        int64_t len = std::min<int64_t>(QT, C - t);
+        if (B >= QT) len = std::min<int64_t>(len, (t / B + 1) * B - t);
+        QTile q{};
+        q.q_tok = (int32_t)(qo + (t - q0));
+        q.n_tok = (int32_t)len;
+        q.k_ctx = (int32_t)ko;
+        q.pos0 = (int32_t)t;
+        q.lim_min = (int32_t)((t / B + 1) * B);
+        q.lim_max = (int32_t)(((t + len - 1) / B + 1) * B);
+        q.k_own = (int32_t)ko; q.n_own = 0;
+        p.qtiles.push_back(q); qtile_seg.push_back(s);
+        t += len;
+      }
+      for (int64_t c = 0; c < m; ++c) {
+        const int64_t b = p.cb[p.coff[s] + c];
+        for (int64_t t = 0; t < B; t += QT) {
+          QTile q{};
+          q.q_tok = (int32_t)(qo + (C - q0) + c * B + t);
+          q.n_tok = (int32_t)std::min<int64_t>(QT, B - t);
+          q.k_ctx = (int32_t)ko;
+          q.pos0 = -1;
+          q.lim_min = q.lim_max = (int32_t)(b * B);
+          q.k_own = (int32_t)(ko + C + c * B);
+          q.n_own = B;
+          p.qtiles.push_back(q); qtile_seg.push_back(s);
+        }
+      }
+      qo += (C - q0) + m * B;
+      ko += C + m * B;
+    }
+  }
+  auto tiles_of = [&](const QTile& q) -> int64_t {
+    return ceil_div(q.lim_max, kKTile) + ceil_div(q.n_own, kKTile);
+  };
+
+  // ---------------- forward items: direct, or split along the key range
+  const int64_t nq = (int64_t)p.qtiles.size();
+  int64_t total_tiles = 0, max_tiles = 0;
+  for (auto& q : p.qtiles) { total_tiles += tiles_of(q); max_tiles = std::max(max_tiles, tiles_of(q)); }
+  const int64_t direct_items = nq * Hkv;
+  bool split = false;
+  int64_t tps = 0;   // key tiles per split
+  if (!(d->flags & BD_ATTN_FLAG_NO_SPLIT)) {
+    const int64_t target = 2 * 256;   // two workgroups per compute unit
+    if (d->flags & BD_ATTN_FLAG_FORCE_SPLIT) {
+      split = max_tiles > 1;
+      tps = std::max<int64_t>(1, (max_tiles + 1) / 2);
+    } else if (direct_items < target && max_tiles >= 4) {
+      tps = std::max<int64_t>(1, ceil_div(total_tiles * Hkv, target));
+      split = tps < max_tiles;
+    }
+  }
+  p.split = split;
+  p.fwd_items.clear(); p.comb_items.clear();
+  {
+    std::vector<FwdItem> raw;
+    std::vector<int64_t> cost, cls;
+    for (int64_t i = 0; i < nq; ++i) {
+      const int64_t nt = tiles_of(p.qtiles[i]);
+      for (int h = 0; h < Hkv; ++h) {
+        if (split && nt > tps) {
+          CombItem ci{(int32_t)i, h, (int32_t)raw.size(), 0};
+          for (int64_t b0 = 0; b0 < nt; b0 += tps) {
+            raw.push_back(FwdItem{(int32_t)i, h, (int32_t)b0, (int32_t)std::min(nt, b0 + tps)});
+            cost.push_back(std::min(nt, b0 + tps) - b0 + 1);
+            cls.push_back((int64_t)qtile_seg[i] * Hkv + h);
+            ci.count++;
+          }
+          p.comb_items.push_back(ci);
+        } else if (split) {
+          CombItem ci{(int32_t)i, h, (int32_t)raw.size(), 1};
+          raw.push_back(FwdItem{(int32_t)i, h, 0, (int32_t)nt});
+          cost.push_back(nt + 1);
+          cls.push_back((int64_t)qtile_seg[i] * Hkv + h);
+          p.comb_items.push_back(ci);
+        } else {
+          raw.push_back(FwdItem{(int32_t)i, h, 0, (int32_t)nt});
+          cost.push_back(nt + 1);
+          cls.push_back((int64_t)qtile_seg[i] * Hkv + h);
+        }
+      }
+    }
+    if (split) {
+      // Split items keep their partial-slot index: the launch order is a
+      // permutation stored beside them.
+      p.fwd_items = raw;
+      p.fwd_order = launch_order(cost, cls, xcd);
+    } else {
+      auto ord = launch_order(cost, cls, xcd);
+      for (int32_t o : ord) p.fwd_items.push_back(o < 0 ? FwdItem{-1, 0, 0, 0} : raw[o]);
+      p.fwd_order.clear();
+    }
+    // dQ items: every (query tile, kv head), whole key range, same order policy
+    p.dq_items.clear();
+    std::vector<FwdItem> dq_raw;
+    std::vector<int64_t> dcost, dcls;
+    for (int64_t i = 0; i < nq; ++i)
+      for (int h = 0; h < Hkv; ++h) {
+        dq_raw.push_back(FwdItem{(int32_t)i, h, 0, (int32_t)tiles_of(p.qtiles[i])});
+        dcost.push_back(tiles_of(p.qtiles[i]) + 1);
+        dcls.push_back((int64_t)qtile_seg[i] * Hkv + h);
+      }
+    auto ord = launch_order(dcost, dcls, xcd);
+    for (int32_t o : ord) p.dq_items.push_back(o < 0 ? FwdItem{-1, 0, 0, 0} : dq_raw[o]);
+  }
+
+  // ---------------- key tiles (dK / dV) and canvas-query lists
+  p.ktiles.clear(); p.canvq.clear(); p.bwd_items.clear();
+  std::vector<int> ktile_seg;
+  std::vector<int64_t> kcost;
+  {
+    int64_t qo = 0, ko = 0;
+    for (int s = 0; s < S; ++s) {
+      const int64_t C = p.ctx[s], q0 = p.q0[s];
+      const int64_t m = p.coff[s + 1] - p.coff[s];
+      // canvases of the segment sorted by block index, largest first: those
+      // visible to a clean key at position p0 (b*B > p0) form a prefix.
+      std::vector<int64_t> ord(m);
+      std::iota(ord.begin(), ord.end(), 0);
+      std::stable_sort(ord.begin(), ord.end(), [&](int64_t a, int64_t b) {
+        return p.cb[p.coff[s] + a] > p.cb[p.coff[s] + b]; });
+      const int32_t cv_first = (int32_t)p.canvq.size();
+      for (int64_t c : ord) {
+        CanvasQ e{};
+        e.q_tok = (int32_t)(qo + (C - q0) + c * B);
+        e.n_tok = B;
+        e.lim = (int32_t)(p.cb[p.coff[s] + c] * B);
+        e.own = 0;
+        p.canvq.push_back(e);
+      }
+      // clean key tiles
+      for (int64_t k0 = 0; k0 < C; k0 += kKBlock) {
+        KTile t{};
+        t.k_tok = (int32_t)(ko + k0);
+        t.n_keys = (int32_t)std::min<int64_t>(kKBlock, C - k0);
+        t.p0 = (int32_t)k0;
+        const int64_t cpos = std::max<int64_t>(q0, (k0 / B) * B);
+        t.cq_pos = (int32_t)cpos;
+        t.cq_len = (int32_t)std::max<int64_t>(0, C - cpos);
+        t.cq_tok = (int32_t)(qo + std::max<int64_t>(0, cpos - q0));
+        t.cv_begin = cv_first;
+        int32_t cnt = 0;
+        for (int64_t c = 0; c < m; ++c) if (p.canvq[cv_first + c].lim > k0) cnt++;
+        t.cv_count = cnt;
+        p.ktiles.push_back(t); ktile_seg.push_back(s);
+        kcost.push_back((int64_t)t.cq_len + (int64_t)cnt * B);
+      }
+      // canvas key tiles: each canvas' own keys, seen only by that canvas
+      for (int64_t c = 0; c < m; ++c) {
+        for (int64_t k0 = 0; k0 < B; k0 += kKBlock) {
+          CanvasQ e{};
+          e.q_tok = (int32_t)(qo + (C - q0) + c * B);
+          e.n_tok = B;
+          e.lim = 0;
+          e.own = 1;
+          KTile t{};
+          t.k_tok = (int32_t)(ko + C + c * B + k0);
+          t.n_keys = (int32_t)std::min<int64_t>(kKBlock, B - k0);
+          t.p0 = -1;
+          t.cq_tok = (int32_t)qo; t.cq_len = 0; t.cq_pos = 0;
+          t.cv_begin = (int32_t)p.canvq.size();
+          t.cv_count = 1;
+          p.canvq.push_back(e);
+          p.ktiles.push_back(t); ktile_seg.push_back(s);
+          kcost.push_back(B);
+        }
+      }
+      qo += (C - q0) + m * B;
+      ko += C + m * B;
+    }
+  }
+  {
+    std::vector<BwdItem> raw;
+    std::vector<int64_t> cost, cls;
+    for (size_t i = 0; i < p.ktiles.size(); ++i)
+      for (int h = 0; h < Hkv; ++h) {
+        raw.push_back(BwdItem{(int32_t)i, h, 0, 0});
+        cost.push_back(ceil_div(kcost[i], 8) + 1);
+        cls.push_back((int64_t)ktile_seg[i] * Hkv + h);
+      }
+    auto ord = launch_order(cost, cls, xcd);
+    for (int32_t o : ord) p.bwd_items.push_back(o < 0 ? BwdItem{-1, 0, 0, 0} : raw[o]);
+  }
+
+  // ---------------- serialize (int32 blob, 16-byte aligned sections)
+  // Header: magic, version, then (count, offset) of every section in order.
+  p.blob.assign(kBlobHeaderInts, 0);
+  append_records(p.blob, p.qtiles, p.off_qtiles);
+  append_records(p.blob, p.fwd_items, p.off_fwd);
+  append_records(p.blob, p.fwd_order, p.off_fwd_order);
+  append_records(p.blob, p.comb_items, p.off_comb);
+  append_records(p.blob, p.dq_items, p.off_dq);
+  append_records(p.blob, p.ktiles, p.off_ktiles);
+  append_records(p.blob, p.canvq, p.off_canvq);
+  append_records(p.blob, p.bwd_items, p.off_bwd);
+  while (p.blob.size() % 4) p.blob.push_back(0);
+  {
+    int32_t* hd = p.blob.data();
+    hd[0] = kBlobMagic;
+    hd[1] = 1;
+    const int64_t cnt[8] = {(int64_t)p.qtiles.size(), (int64_t)p.fwd_items.size(), (int64_t)p.fwd_order.size(),
+                            (int64_t)p.comb_items.size(), (int64_t)p.dq_items.size(), (int64_t)p.ktiles.size(),
+                            (int64_t)p.canvq.size(), (int64_t)p.bwd_items.size()};
+    const int64_t off[8] = {p.off_qtiles, p.off_fwd, p.off_fwd_order, p.off_comb, p.off_dq, p.off_ktiles,
+                            p.off_canvq, p.off_bwd};
+    for (int i = 0; i < 8; ++i) { hd[2 + 2 * i] = (int32_t)cnt[i]; hd[3 + 2 * i] = (int32_t)off[i]; }
+  }
+
+  const int64_t D = d->head_dim;
+  const int64_t Hq = d->num_q_heads;
+  p.ws_fwd = 0;
+  if (split) {
+    const int64_t nsplit = (int64_t)p.fwd_items.size();
+    p.off_ws_lse = nsplit * kQRows * D * 4;        // partial O (fp32), then partial LSE
+    p.ws_fwd = (size_t)(p.off_ws_lse + nsplit * kQRows * 4);
+  }
+  p.ws_bwd = (size_t)(ceil_div(tq * Hq * 4, 256) * 256);   // delta [Tq, Hq] fp32
+  return BD_ATTN_OK;
+}
+
+}  // namespace bdattn

@@ -1,0 +1,45 @@
+// Host-side plan: validated metadata plus the serialized work lists.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/bd_attn.h"
+#include "bd_records.h"
+
+namespace bdattn {
+
+struct Plan {
+  bd_attn_desc desc{};          // scalar fields only (pointers cleared)
+  int G = 1;                    // query heads per kv head
+  int qt_tokens = 1;            // tokens per query tile
+  float scale = 1.f;
+  std::vector<int32_t> ctx, q0, coff, cb;
+  int64_t tq = 0, tk = 0, pairs = 0;
+
+  std::vector<QTile> qtiles;
+  bool split = false;
+  std::vector<FwdItem> fwd_items;    // direct: launch order; split: partial-slot order
+  std::vector<int32_t> fwd_order;    // split only: launch order over fwd_items
+  std::vector<CombItem> comb_items;  // split only
+  std::vector<FwdItem> dq_items;     // launch order
+  std::vector<KTile> ktiles;
+  std::vector<CanvasQ> canvq;
+  std::vector<BwdItem> bwd_items;    // launch order
+
+  std::vector<int32_t> blob;         // device metadata image
+  int64_t off_qtiles = 0, off_fwd = 0, off_fwd_order = 0, off_comb = 0, off_dq = 0,
+          off_ktiles = 0, off_canvq = 0, off_bwd = 0;   // int32 offsets into blob
+  size_t ws_fwd = 0, ws_bwd = 0;
+  int64_t off_ws_lse = 0;            // byte offset of the partial LSE in the forward workspace
+};
+
+// Validates desc and fills *plan. On error returns a non-OK status and sets *err.
+bd_attn_status build_plan(const bd_attn_desc* desc, Plan* plan, std::string* err);
+
+}  // namespace bdattn
+
+struct bd_attn_plan_s {
+  bdattn::Plan p;
+};

@@ -1,0 +1,151 @@
+/*
+ * bd_attn.h — C ABI of libbdattn.so: staircase block-diffusion attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (ORL paper, arXiv 2610.20687, section 3.2 "Staircase attention
+ * kernel" and the appendix D.2 paragraph on the kernel): softmax attention over
+ * packed, mutually invisible documents, where each document (segment) holds a
+ * clean context followed by m captured canvases of one block each (section 3.1:
+ * the canvas is replayed after its clean context). Visibility:
+ *   - a canvas with block index b sees the clean context blocks 0..b-1 and its
+ *     own B tokens (bidirectionally); never its own clean copy (block b), later
+ *     blocks, other canvases or other segments;
+ *   - a clean query sees clean keys block-causally (key block <= query block,
+ *     bidirectional inside a block) and never a canvas key.
+ * The forward pass returns O = softmax(scale * Q K^T under that visibility) V and
+ * the natural-log LSE of the scaled scores; the backward pass returns dQ, dK,
+ * dV of L = <dO, O>. Visible key ranges are derived from per-segment metadata;
+ * no dense mask is ever built and fully invisible tiles are never visited
+ * (same section and appendix paragraph).
+ *
+ * Packed "THD" layouts, row-major, contiguous, element type = desc.dtype:
+ *   Q, O, dO, dQ : [Tq, Hq, D]      K, V, dK, dV : [Tk, Hkv, D]
+ *   LSE          : [Tq, Hq] float32 (always float32)
+ * Segment s occupies, in order of s:
+ *   keys    : ctx_len[s] clean tokens, then its canvases (B tokens each) in the
+ *             order they appear in canvas_block_idx;
+ *   queries : clean tokens at positions ctx_q_begin[s] .. ctx_len[s]-1, then the
+ *             same canvases in the same order.
+ *   Tq = sum_s (ctx_len[s] - ctx_q_begin[s] + m_s * B), Tk = sum_s (ctx_len[s] + m_s * B).
+ * ctx_q_begin[s] = 0 is replay (every context token is also a query);
+ * ctx_q_begin[s] = ctx_len[s] is the single-request denoising step (only the
+ * canvas queries; appendix F.1 "Kernels": attention of the canvas over a KV
+ * arena).
+ * Query head h reads kv head h / (Hq / Hkv).
+ *
+ * Ownership: the caller owns every device buffer (tensors, the metadata buffer
+ * and the workspace). The library never allocates device memory and never
+ * synchronises the host; every device operation is enqueued on the stream
+ * passed in. A plan owns host memory only and is immutable after creation:
+ * one plan may serve any number of calls on any streams.
+ *
+ * Errors: every function returns a bd_attn_status; nothing aborts or throws
+ * across the ABI. On a non-OK status, bd_attn_last_error() returns a message
+ * (thread-local, valid until the next call on the same thread) and no device
+ * work was enqueued by the failing call.
+ */
+#ifndef BD_ATTN_H_
+#define BD_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream type, declared opaquely so host-only users need no HIP headers. */
+typedef struct ihipStream_t* bd_attn_stream_t;
+
+typedef enum {
+  BD_ATTN_OK = 0,
+  BD_ATTN_EINVAL = 1,        /* invalid metadata, pointer, size or alignment */
+  BD_ATTN_EUNSUPPORTED = 2,  /* valid but not implemented (head_dim, group size) */
+  BD_ATTN_EWORKSPACE = 3,    /* workspace or metadata buffer too small */
+  BD_ATTN_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} bd_attn_status;
+
+typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
+
+/* flags */
+#define BD_ATTN_FLAG_NO_SPLIT   1u  /* never split a query tile's key range (forward) */
+#define BD_ATTN_FLAG_FORCE_SPLIT 2u /* always split long key ranges (forward; for tests) */
+#define BD_ATTN_FLAG_NO_XCD     4u  /* plain largest-cost-first order, no XCD grouping */
+
+typedef struct bd_attn_plan_s* bd_attn_plan_t;
+
+typedef struct {
+  int32_t num_segments;             /* S >= 1 */
+  const int32_t* ctx_len;           /* host [S]: C_s >= 0, multiple of block_size */
+  const int32_t* ctx_q_begin;       /* host [S] or NULL (= 0 for all): 0 <= q0_s <= C_s */
+  const int32_t* canvas_offsets;    /* host [S+1]: prefix sums, canvas_offsets[0] = 0 */
+  const int32_t* canvas_block_idx;  /* host [canvas_offsets[S]]: 0 <= b <= C_s / B, any order */
+  int32_t block_size;               /* B >= 1 */
+  int32_t num_q_heads;              /* Hq >= 1, multiple of num_kv_heads */
+  int32_t num_kv_heads;             /* Hkv >= 1 */
+  int32_t head_dim;                 /* 64 or 128 */
+  int32_t dtype;                    /* bd_attn_dtype */
+  float softmax_scale;              /* <= 0 selects 1/sqrt(head_dim) */
+  uint32_t flags;                   /* BD_ATTN_FLAG_* */
+} bd_attn_desc;
+
+/* Validates the metadata and builds a plan (host only; copies everything it
+ * needs). Work lists: query tiles with their visible key ranges (forward and
+ * dQ), key tiles with their visible query ranges (dK/dV), each ordered
+ * largest-cost-first (ORL section 3.2 "Packed and cost-balanced state training"
+ * and appendix D.3 apply that order to data-parallel groups; here it orders
+ * workgroups across compute units). Errors: EINVAL on bad metadata, EUNSUPPORTED
+ * on an unsupported head_dim / group size, both with *out untouched. */
+bd_attn_status bd_attn_plan(const bd_attn_desc* desc, bd_attn_plan_t* out);
+
+/* Sizes implied by a plan: packed token counts, bytes of the device metadata
+ * buffer, bytes of forward / backward workspace (0 when none is needed) and
+ * the number of visible (query token, key token) pairs per query head. Any
+ * output pointer may be NULL. */
+bd_attn_status bd_attn_plan_sizes(bd_attn_plan_t plan, int64_t* tq, int64_t* tk,
+                                  size_t* meta_bytes, size_t* ws_fwd_bytes,
+                                  size_t* ws_bwd_bytes, int64_t* visible_pairs);
+
+/* Copies the plan's host work lists into meta_host (meta_bytes bytes, host
+ * memory owned by the caller), e.g. to stage them into pinned memory. */
+bd_attn_status bd_attn_plan_serialize(bd_attn_plan_t plan, void* meta_host, size_t bytes);
+
+/* Enqueues an asynchronous copy of the work lists into meta_dev (device memory
+ * of at least meta_bytes bytes, 16-byte aligned) on stream. The source is the
+ * plan's own host memory, so the plan must outlive the copy. Call once before
+ * the first bd_attn_fwd / bd_attn_bwd with this meta_dev. */
+bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_stream_t stream);
+
+/* Forward. q [Tq,Hq,D], k/v [Tk,Hkv,D] in desc.dtype; writes o [Tq,Hq,D] and
+ * lse [Tq,Hq] (float32). ws: ws_fwd_bytes of device memory (may be NULL when
+ * that size is 0). All pointers device pointers, 16-byte aligned.
+ * Errors: EINVAL (NULL or misaligned pointer), EWORKSPACE (ws NULL while
+ * needed), EHIP (launch failure). */
+bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev,
+                           const void* q, const void* k, const void* v,
+                           void* o, float* lse, void* ws, bd_attn_stream_t stream);
+
+/* Backward of L = <dO, O> with o / lse from bd_attn_fwd on the same inputs.
+ * Writes (does not accumulate) dq [Tq,Hq,D], dk and dv [Tk,Hkv,D]; dK and dV
+ * are summed over the query heads of each kv head. Deterministic: no atomics,
+ * bitwise identical across runs. ws: ws_bwd_bytes of device memory (holds the
+ * float32 row terms delta = rowsum(dO * O), [Tq, Hq]). Errors as bd_attn_fwd. */
+bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev,
+                           const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv, void* ws, bd_attn_stream_t stream);
+
+/* Frees a plan (NULL is accepted). */
+bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* bd_attn_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* bd_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BD_ATTN_H_ */

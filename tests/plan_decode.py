@@ -1,0 +1,57 @@
+"""Decodes a serialized plan (host copy) into Python records, and rebuilds the
+visibility those records encode, so tests can compare it with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+MAGIC = 0x62646174
+SECTIONS = ["qtiles", "fwd", "fwd_order", "comb", "dq", "ktiles", "canvq", "bwd"]
+WIDTH = {"qtiles": 8, "fwd": 4, "fwd_order": 1, "comb": 4, "dq": 4, "ktiles": 8, "canvq": 4, "bwd": 4}
+
+
+def decode(blob):
+    b = np.asarray(blob, dtype=np.int64)
+    assert b[0] == MAGIC and b[1] == 1
+    out = {}
+    for i, name in enumerate(SECTIONS):
+        cnt, off = int(b[2 + 2 * i]), int(b[3 + 2 * i])
+        assert off % 4 == 0
+        w = WIDTH[name]
+        out[name] = b[off:off + cnt * w].reshape(cnt, w) if w > 1 else b[off:off + cnt]
+    return out
+
+
+def qtile_visibility(rec, meta, G):
+    """Boolean [Tq, Tk] visibility encoded by the query tiles (each token once per tile)."""
+    B = meta.block_size
+    vis = np.zeros((meta.tq, meta.tk), dtype=bool)
+    cover = np.zeros(meta.tq, dtype=np.int64)
+    for q_tok, n_tok, k_ctx, pos0, lim_max, lim_min, k_own, n_own in rec["qtiles"]:
+        for t in range(n_tok):
+            L = ((pos0 + t) // B + 1) * B if pos0 >= 0 else lim_min
+            assert L <= lim_max and L >= lim_min
+            vis[q_tok + t, k_ctx:k_ctx + L] = True
+            vis[q_tok + t, k_own:k_own + n_own] = True
+            cover[q_tok + t] += 1
+    return vis, cover
+
+
+def ktile_visibility(rec, meta, G):
+    """Boolean [Tq, Tk] visibility encoded by the key tiles and canvas-query entries."""
+    B = meta.block_size
+    vis = np.zeros((meta.tq, meta.tk), dtype=bool)
+    cover = np.zeros(meta.tk, dtype=np.int64)
+    cv = rec["canvq"]
+    for k_tok, n_keys, p0, cq_tok, cq_len, cq_pos, cv_begin, cv_count in rec["ktiles"]:
+        cover[k_tok:k_tok + n_keys] += 1
+        for kk in range(n_keys):
+            key = k_tok + kk
+            for t in range(cq_len):
+                L = ((cq_pos + t) // B + 1) * B
+                if p0 >= 0 and p0 + kk < L:
+                    vis[cq_tok + t, key] = True
+            for e in range(cv_begin, cv_begin + cv_count):
+                q_tok, n_tok, lim, own = cv[e]
+                if own or (p0 >= 0 and p0 + kk < lim):
+                    vis[q_tok:q_tok + n_tok, key] = True
+    return vis, cover

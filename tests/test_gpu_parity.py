@@ -1,0 +1,234 @@
+"""GPU parity: libbdattn (HIP, gfx950) against the fp64 CPU oracle, through the C ABI.
+
+bf16: max-abs <= 2e-2, mean-abs <= 2e-3 and relative Frobenius <= 1e-2 on O, dQ,
+dK, dV (the relative bound keeps the check meaningful with near-uniform softmax);
+fp32: max-abs <= 1e-5. LSE is compared as an extra check.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from block_diffusion_attention_amd import workloads as W
+from helpers import assert_close, error_stats
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+if not _gpu_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import torch  # noqa: E402
+
+from gpu_common import run_gpu, run_oracle  # noqa: E402
+from block_diffusion_attention_amd import binding as b  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _compare(wl, gpu, ref, names=("o", "dq", "dk", "dv"), rows=None, krows=None):
+    dt = wl.meta.dtype
+    stats = {}
+    for n in names:
+        if n not in gpu or n not in ref:
+            continue
+        g, r = gpu[n], ref[n]
+        if rows is not None and n in ("o", "dq"):
+            g, r = g[rows], r[rows]
+        if krows is not None and n in ("dk", "dv"):
+            g, r = g[krows], r[krows]
+        stats[n] = assert_close(f"{wl.name}:{n}", g, r, dt)
+    g, r = gpu["lse"], ref["lse"]
+    if rows is not None:
+        g, r = g[rows], r[rows]
+    tol = 1e-5 if dt == "fp32" else 2e-3
+    assert np.abs(g - r).max() <= tol, f"{wl.name}: lse max err {np.abs(g - r).max()}"
+    return stats
+
+
+def test_native_library_is_loaded_once():
+    maps = open(f"/proc/{os.getpid()}/maps").read()
+    assert "libbdattn.so" in maps
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, f"more than one HIP runtime mapped: {hip}"
+
+
+# ---------------------------------------------------------------- named workloads
+
+def test_tiny_fp32_replay():
+    wl = W.make_config(1)
+    _say(f"case {wl.name} seed 1")
+    gpu, _ = run_gpu(wl)
+    ref = run_oracle(wl)
+    _compare(wl, gpu, ref)
+
+
+def test_tiny_fp32_canvas_only():
+    rng = np.random.default_rng(101)
+    meta = W.Meta([64], [64], [[4]], 16, 2, 1, 64, "fp32")
+    wl = W.random_workload(rng, meta, sigma=1.0)
+    _say(f"case tiny-fp32-canvas-only")
+    gpu, _ = run_gpu(wl)
+    _compare(wl, gpu, run_oracle(wl))
+
+
+@pytest.mark.parametrize("seed", [2, 102, 202])
+def test_denoise_step_split(seed):
+    wl = W.make_config(2, seed=seed, with_do=False)
+    _say(f"case {wl.name} seed {seed}")
+    gpu, plan = run_gpu(wl, backward=False)
+    assert plan.ws_fwd_bytes > 0, "the single-request shape takes the split path"
+    _compare(wl, gpu, run_oracle(wl, backward=False))
+
+
+def test_denoise_step_no_split_matches_split():
+    wl = W.make_config(2, with_do=False)
+    g1, _ = run_gpu(wl, backward=False)
+    g2, p2 = run_gpu(wl, flags=b.FLAG_NO_SPLIT, backward=False)
+    assert p2.ws_fwd_bytes == 0
+    st = error_stats(g1["o"], g2["o"])
+    assert st["max_abs"] <= 4e-3, st
+
+
+def test_staircase_full_kv_group_samples():
+    wl = W.make_config(4)
+    _say(f"case {wl.name} seed 4")
+    gpu, _ = run_gpu(wl)
+    for g in (0, 5):
+        sub = W.kv_group_slice(wl, g)
+        ref = run_oracle(sub)
+        G = wl.meta.num_q_heads // wl.meta.num_kv_heads
+        gs = {n: (gpu[n][:, g * G:(g + 1) * G] if n in ("o", "dq", "lse") else gpu[n][:, g:g + 1])
+              for n in gpu}
+        _compare(sub, gs, ref)
+
+
+def test_packed_replay_segment_samples():
+    wl = W.make_config(3)
+    _say(f"case {wl.name} seed 3")
+    gpu, _ = run_gpu(wl)
+    qo, ko = wl.meta.q_offsets(), wl.meta.k_offsets()
+    lens = wl.meta.ctx_len
+    for s in (int(np.argmin(lens)), int(np.argmax(lens))):
+        sub = W.kv_group_slice(W.segment_slice(wl, s), 3)
+        ref = run_oracle(sub)
+        gs = {}
+        for n, x in gpu.items():
+            if n in ("o", "dq", "lse"):
+                gs[n] = x[qo[s]:qo[s + 1], 12:16]
+            else:
+                gs[n] = x[ko[s]:ko[s + 1], 3:4]
+        _compare(sub, gs, ref)
+
+
+def test_large_pack_segment_sample():
+    wl = W.make_config(5)
+    _say(f"case {wl.name} seed 5")
+    gpu, _ = run_gpu(wl)
+    qo, ko = wl.meta.q_offsets(), wl.meta.k_offsets()
+    s, g = 2, 6
+    sub = W.kv_group_slice(W.segment_slice(wl, s), g)
+    ref = run_oracle(sub)
+    gs = {}
+    for n, x in gpu.items():
+        if n in ("o", "dq", "lse"):
+            gs[n] = x[qo[s]:qo[s + 1], 4 * g:4 * g + 4]
+        else:
+            gs[n] = x[ko[s]:ko[s + 1], g:g + 1]
+    _compare(sub, gs, ref)
+
+
+# ---------------------------------------------------------------- random packs, edge cases
+
+CASES = [
+    # (block, hq, hkv, D, dtype, sigma)
+    (32, 8, 2, 128, "bf16", 1 / np.sqrt(128)),
+    (32, 4, 4, 64, "bf16", 1 / np.sqrt(64)),
+    (16, 4, 2, 128, "bf16", 1.0),        # peaky softmax
+    (1, 4, 1, 64, "bf16", 0.3),
+    (2, 2, 1, 128, "bf16", 0.5),
+    (64, 4, 1, 128, "bf16", 0.3),
+    (256, 8, 2, 128, "bf16", 0.2),
+    (3, 6, 2, 64, "bf16", 0.5),          # group size 3
+    (8, 4, 2, 64, "fp32", 1.0),
+    (32, 4, 1, 128, "fp32", 0.5),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_random_packs(case, seed):
+    B, hq, hkv, D, dt, sigma = CASES[case]
+    rng = np.random.default_rng(7000 + 31 * case + seed)
+    max_blocks = max(2, min(12, 600 // B))
+    meta = W.random_meta(rng, max_segments=3, max_blocks=max_blocks, block_sizes=(B,), max_canvases=4,
+                         hq=hq, hkv=hkv, d=D, dtype=dt)
+    wl = W.random_workload(rng, meta, sigma=sigma)
+    _say(f"case random B={B} hq={hq} hkv={hkv} D={D} {dt} seed={seed} tq={meta.tq} tk={meta.tk}")
+    gpu, _ = run_gpu(wl)
+    _compare(wl, gpu, run_oracle(wl))
+
+
+def test_forced_split_matches_oracle():
+    rng = np.random.default_rng(42)
+    meta = W.Meta([1024, 512], [0, 512], [[5, 32, 0], [16]], 32, 8, 2, 128, "bf16")
+    wl = W.random_workload(rng, meta, sigma=0.3)
+    gpu, plan = run_gpu(wl, flags=b.FLAG_FORCE_SPLIT)
+    assert plan.ws_fwd_bytes > 0
+    _compare(wl, gpu, run_oracle(wl))
+
+
+def test_key_shift_stress():
+    # scores shifted by a large common offset exercise the running-maximum rescaling
+    rng = np.random.default_rng(43)
+    meta = W.Meta([512], [0], [[3, 16, 9]], 32, 4, 1, 128, "bf16")
+    wl = W.random_workload(rng, meta, sigma=1.0)
+    c = W.round_bf16(np.full((1, 1, 128), 2.0, np.float32))
+    wl.k = W.round_bf16(wl.k + c)
+    gpu, _ = run_gpu(wl)
+    _compare(wl, gpu, run_oracle(wl))
+
+
+def test_empty_context_and_no_canvas_segments():
+    rng = np.random.default_rng(44)
+    meta = W.Meta([0, 96, 64], [0, 0, 64], [[0, 0], [], [2]], 32, 4, 2, 128, "bf16")
+    wl = W.random_workload(rng, meta, sigma=0.4)
+    gpu, _ = run_gpu(wl)
+    _compare(wl, gpu, run_oracle(wl))
+
+
+def test_backward_is_deterministic():
+    wl = W.make_config(4)
+    g1, _ = run_gpu(wl)
+    g2, _ = run_gpu(wl)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(g1[n], g2[n]), n
+
+
+def test_autograd_function():
+    rng = np.random.default_rng(45)
+    meta = W.Meta([128], [0], [[1, 4]], 32, 4, 1, 64, "bf16")
+    wl = W.random_workload(rng, meta, sigma=0.5)
+    plan = b.Plan(meta).upload("cuda")
+    q = torch.from_numpy(wl.q).cuda().bfloat16().requires_grad_()
+    k = torch.from_numpy(wl.k).cuda().bfloat16().requires_grad_()
+    v = torch.from_numpy(wl.v).cuda().bfloat16().requires_grad_()
+    o = b.attention(q, k, v, plan)
+    o.backward(torch.from_numpy(wl.do).cuda().bfloat16())
+    ref = run_oracle(wl)
+    assert_close("autograd:o", o.detach().float().cpu().numpy(), ref["o"], "bf16")
+    assert_close("autograd:dq", q.grad.float().cpu().numpy(), ref["dq"], "bf16")
+    assert_close("autograd:dk", k.grad.float().cpu().numpy(), ref["dk"], "bf16")
+    assert_close("autograd:dv", v.grad.float().cpu().numpy(), ref["dv"], "bf16")

@@ -1,0 +1,195 @@
+"""Host planner and C ABI, on the CPU (no kernel is launched here).
+
+* the library loads and exports every function include/bd_attn.h declares;
+* metadata validation returns the documented status codes with a message;
+* the work lists encode exactly the oracle's visibility (every query token in
+  one query tile, every key token in one key tile, ranges == dense mask);
+* plans are deterministic and their size grows with tiles, not with N^2.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import bd_oracle as orc
+from block_diffusion_attention_amd.workloads import Meta, config_meta, random_meta
+from plan_decode import decode, ktile_visibility, qtile_visibility
+
+b = pytest.importorskip("block_diffusion_attention_amd.binding")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_function():
+    hdr = open(os.path.join(ROOT, "include", "bd_attn.h")).read()
+    names = set(re.findall(r"^\s*(?:bd_attn_status|const char\*)\s+(bd_attn_\w+)\s*\(", hdr, re.M))
+    assert {"bd_attn_plan", "bd_attn_fwd", "bd_attn_bwd"} <= names
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert set(b.EXPORTED) == names
+
+
+def _status(meta, **over):
+    d = dict(ctx=meta.ctx_len, q0=meta.ctx_q_begin, off=meta.canvas_offsets, cb=meta.flat_canvas_block_idx,
+             B=meta.block_size, hq=meta.num_q_heads, hkv=meta.num_kv_heads, D=meta.head_dim,
+             dtype=0 if meta.dtype == "bf16" else 1, scale=0.0, S=len(meta.ctx_len))
+    d.update(over)
+    keep = [b._arr(d["ctx"]), b._arr(d["q0"]), b._arr(d["off"]), b._arr(d["cb"])]
+    desc = b.Desc()
+    desc.num_segments = d["S"]
+    desc.ctx_len, desc.ctx_q_begin, desc.canvas_offsets, desc.canvas_block_idx = (
+        ctypes.cast(x, b._i32p) for x in keep)
+    desc.block_size, desc.num_q_heads, desc.num_kv_heads, desc.head_dim = d["B"], d["hq"], d["hkv"], d["D"]
+    desc.dtype, desc.softmax_scale, desc.flags = d["dtype"], d["scale"], 0
+    h = ctypes.c_void_p()
+    st = b._lib.bd_attn_plan(ctypes.byref(desc), ctypes.byref(h))
+    msg = b._lib.bd_attn_last_error().decode()
+    if st == 0:
+        b._lib.bd_attn_plan_destroy(h)
+    return st, msg
+
+
+GOOD = Meta([64, 32], [0, 32], [[1, 2], [1]], 16, 4, 2, 128, "bf16")
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=0), b.EINVAL),
+    (dict(B=0), b.EINVAL),
+    (dict(ctx=[65, 32]), b.EINVAL),          # not a multiple of B
+    (dict(ctx=[-16, 32]), b.EINVAL),
+    (dict(q0=[70, 32]), b.EINVAL),           # beyond ctx_len
+    (dict(q0=[-1, 32]), b.EINVAL),
+    (dict(cb=[1, 5, 1]), b.EINVAL),          # block index beyond ctx_len/B
+    (dict(cb=[1, -1, 1]), b.EINVAL),
+    (dict(off=[1, 2, 3]), b.EINVAL),         # offsets must start at 0
+    (dict(off=[0, 2, 1]), b.EINVAL),         # non-decreasing
+    (dict(hq=6, hkv=4), b.EINVAL),           # Hq % Hkv
+    (dict(hkv=0), b.EINVAL),
+    (dict(D=96), b.EUNSUPPORTED),
+    (dict(hq=64, hkv=1), b.EUNSUPPORTED),    # group size above 32
+    (dict(dtype=7), b.EINVAL),
+    (dict(scale=float("inf")), b.EINVAL),
+    (dict(ctx=[0, 0], q0=[0, 0], off=[0, 0, 0], cb=[]), b.EINVAL),   # no query at all
+])
+def test_validation_errors(over, code):
+    st, msg = _status(GOOD, **over)
+    assert st == code and msg
+    st_ok, _ = _status(GOOD)
+    assert st_ok == b.OK
+
+
+def test_null_and_alignment_checks():
+    p = b.Plan(GOOD)
+    vp = ctypes.c_void_p
+    st = b._lib.bd_attn_fwd(p.handle, vp(0), vp(16), vp(16), vp(16), vp(16), vp(16), vp(0), vp(0))
+    assert st == b.EINVAL and "meta_dev" in b._lib.bd_attn_last_error().decode()
+    st = b._lib.bd_attn_fwd(p.handle, vp(16), vp(18), vp(16), vp(16), vp(16), vp(16), vp(0), vp(0))
+    assert st == b.EINVAL and "aligned" in b._lib.bd_attn_last_error().decode()
+    st = b._lib.bd_attn_bwd(p.handle, *([vp(16)] * 10), vp(0), vp(0))
+    assert st == b.EWORKSPACE
+    assert b._lib.bd_attn_fwd(None, *([vp(16)] * 8)) == b.EINVAL
+    assert b._lib.bd_attn_plan_destroy(None) == b.OK
+
+
+def _check_plan(meta, flags=0):
+    p = b.Plan(meta, flags)
+    rec = decode(p.host_blob())
+    G = meta.num_q_heads // meta.num_kv_heads
+    mask = orc.dense_mask(meta)
+    assert p.visible_pairs == int(mask.sum()) == orc.visible_pairs(meta)
+    assert (p.tq, p.tk) == mask.shape
+    vis, cover = qtile_visibility(rec, meta, G)
+    assert (cover == 1).all(), "every query token in exactly one query tile"
+    assert (vis == mask).all()
+    kvis, kcover = ktile_visibility(rec, meta, G)
+    assert (kcover == 1).all(), "every key token in exactly one key tile"
+    assert (kvis == mask).all()
+    hkv = meta.num_kv_heads
+    nq, nk = len(rec["qtiles"]), len(rec["ktiles"])
+    # launch lists: every (tile, kv head) exactly once, empty slots marked -1
+    dq = [tuple(x[:2]) for x in rec["dq"] if x[0] >= 0]
+    assert sorted(dq) == sorted(itertools.product(range(nq), range(hkv)))
+    bw = [tuple(x[:2]) for x in rec["bwd"] if x[0] >= 0]
+    assert sorted(bw) == sorted(itertools.product(range(nk), range(hkv)))
+    if len(rec["comb"]) == 0:
+        fw = [tuple(x[:2]) for x in rec["fwd"] if x[0] >= 0]
+        assert sorted(fw) == sorted(dq)
+    else:
+        # split: the splits of a (tile, head) cover its key tiles once, in order
+        order = [o for o in rec["fwd_order"] if o >= 0]
+        assert sorted(order) == list(range(len(rec["fwd"])))
+        for qt, h, first, count in rec["comb"]:
+            spans = rec["fwd"][first:first + count]
+            assert (spans[:, 0] == qt).all() and (spans[:, 1] == h).all()
+            assert spans[0, 2] == 0 and (spans[1:, 2] == spans[:-1, 3]).all()
+            t = rec["qtiles"][qt]
+            ntiles = -(-t[4] // 64) + -(-t[7] // 64)
+            assert spans[-1, 3] == ntiles
+    return p, rec
+
+
+def test_plan_encodes_oracle_visibility_exhaustive():
+    n = 0
+    for B in (1, 2, 3):
+        for nb in range(0, 4):
+            C = nb * B
+            for q0 in sorted({0, C, min(C, B)}):
+                for cv in [[]] + [[x] for x in range(nb + 1)] + [list(p) for p in itertools.permutations(range(nb + 1), 2)]:
+                    if (C - q0) + len(cv) * B == 0:
+                        continue
+                    _check_plan(Meta([C], [q0], [cv], B, 2, 1, 64, "bf16"))
+                    n += 1
+    assert n > 100
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_encodes_oracle_visibility_random(seed):
+    rng = np.random.default_rng(500 + seed)
+    meta = random_meta(rng, hq=4, hkv=2, d=64, max_segments=4, max_blocks=8,
+                       block_sizes=(1, 2, 4, 8, 16, 32, 48), max_canvases=4, dtype="bf16")
+    _check_plan(meta)
+    _check_plan(meta, b.FLAG_FORCE_SPLIT)
+    _check_plan(meta, b.FLAG_NO_XCD)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 32])
+def test_plan_group_sizes(G):
+    meta = Meta([96, 64], [0, 64], [[2, 0, 3], [4]], 16, 2 * G, 2, 64, "bf16")
+    _check_plan(meta)
+
+
+def test_plan_large_blocks():
+    # blocks larger than a query tile / key tile (B=256 as in the 256-token block models)
+    meta = Meta([512], [0], [[1, 2, 0]], 256, 8, 2, 128, "bf16")
+    _check_plan(meta)
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_named_workload_plans(k):
+    meta = config_meta(k, np.random.default_rng(k))
+    p = b.Plan(meta)
+    assert p.visible_pairs == orc.visible_pairs(meta)
+    rec = decode(p.host_blob())
+    if k == 2:
+        assert len(rec["comb"]) == 8, "the denoising-step shape is split along its key range"
+        assert len([o for o in rec["fwd_order"] if o >= 0]) >= 256
+
+
+def test_plan_is_deterministic():
+    meta = config_meta(5, np.random.default_rng(5))
+    a = b.Plan(meta).host_blob()
+    c = b.Plan(meta).host_blob()
+    assert a == c
+
+
+def test_metadata_grows_with_tiles_not_n_squared():
+    sizes = []
+    for n in (64, 128, 256, 512):
+        meta = Meta([32 * n], [0], [[n // 2, n]], 32, 32, 8, 128, "bf16")
+        sizes.append(b.Plan(meta).meta_bytes)
+    # doubling the context about doubles the work lists (linear), never quadruples them
+    for s0, s1 in zip(sizes, sizes[1:]):
+        assert s1 < 2.3 * s0
