@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the staircase block-diffusion attention on one MI355X.
+
+A step is one forward and one backward pass (every kernel of the hot path) over
+one packed batch of synthetic input already resident in HBM, with the plan
+built once beforehand (as a model reuses one plan in every layer). The default
+workload is the packed-replay pack: 16 segments, each a clean context of
+256..4096 tokens (whole blocks of 32) followed by one 32-token canvas at the
+next block index; 32 query / 8 kv heads, head_dim 128, bf16 inputs drawn from
+N(0, 1/128) and dO from N(0, 1), seed 3.
+
+Prints one JSON line: useful (visible-pair) TFLOP/s of the step, the roofline
+of the dominant kernel (its algorithmic FLOPs or bytes per launch over its
+average launch duration, timed with HIP events on the stream that runs it) and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+METRIC = "useful TFLOP/s + % of bf16 MFMA peak, staircase block-diffusion attn fwd/bwd"
+WORKLOAD_NAMES = {
+    1: "tiny fp32: 64-token context (4 blocks of 16) + 1 canvas at block 4, 2q/1kv, D=64",
+    2: "single-request denoising step: 2048-token context in KV + one 32-token canvas, 32q/8kv, D=128, bf16",
+    3: "packed replay: 16 segments, contexts U[256,4096] in blocks of 32, one 32-token canvas each at the "
+       "next block index, 32q/8kv, D=128, bf16, fwd+bwd",
+    4: "staircase: 4096-token context + 24 canvases at distinct block indices in [1,128], 32q/8kv, D=128, "
+       "bf16, fwd+bwd",
+    5: "large pack: 4 x (8192-token context + 16 canvases), 32q/8kv, D=128, bf16, fwd+bwd",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--flags", type=int, default=0, help="plan flags (BD_ATTN_FLAG_*)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    ap.add_argument("--fwd-only", action="store_true")
+    return ap.parse_args()
+
+
+def src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "block_diffusion_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "fwd": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "dkdv": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "dq": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "bwd_pre": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "combine": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+}
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json),
+    only if the kernel source has not changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[f"{kernel}@{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("src_sha256") != src_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle (fp64 numpy) on a bounded sample of the workload: whole
+    (segment, kv head) slices, forward + backward, until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from block_diffusion_attention_amd import workloads as W
+    from oracle import bd_oracle as orc
+
+    m = wl.meta
+    G = m.num_q_heads // m.num_kv_heads
+    order = [(s, g) for s in range(m.num_segments) for g in range(m.num_kv_heads)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    done, flops, t_total = [], 0.0, 0.0
+    backward = wl.do is not None and wl.passes != "fwd"
+    for s, g in order:
+        sub = W.kv_group_slice(W.segment_slice(wl, s), g)
+        t0 = time.perf_counter()
+        orc.attention_fwd(sub.q, sub.k, sub.v, sub.meta)
+        if backward:
+            orc.attention_bwd(sub.q, sub.k, sub.v, sub.do, sub.meta)
+        t_total += time.perf_counter() - t0
+        pairs = orc.visible_pairs(sub.meta)
+        flops += (14.0 if backward else 4.0) * m.head_dim * G * pairs
+        done.append((s, g))
+        if t_total >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("internal_api") in
+                   ("openblas", "mkl", "blis")] or [1])
+    frac = len(done) / len(order)
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {len(order)} (segment, kv head) slices ({frac:.1%} of the work), "
+                  f"{'fwd+bwd' if backward else 'fwd'}, fp64 numpy, {t_total:.1f} s",
+        "seconds": t_total,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_attention_amd import binding as b
+    from block_diffusion_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    k = args.workload
+    wl = W.make_config(k, seed=args.seed)
+    m = wl.meta
+    backward = wl.do is not None and not args.fwd_only and k != 2
+    t_plan0 = time.perf_counter()
+    plan = b.Plan(m, args.flags)
+    t_plan = time.perf_counter() - t_plan0
+    plan.upload(dev)
+    dt = plan.dtype
+    to = lambda x: torch.from_numpy(x).to(dev).to(dt).contiguous()
+    q, kk, v = to(wl.q), to(wl.k), to(wl.v)
+    do = to(wl.do) if backward else None
+    o = torch.empty_like(q)
+    lse = torch.empty((plan.tq, m.num_q_heads), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(kk), torch.empty_like(v)) if backward else (None,) * 3
+
+    nf = plan.kernels(False)
+    fwd_names = ["fwd"] if nf == 1 else ["fwd", "combine"]
+    bwd_names = ["bwd_pre", "dkdv", "dq"]
+
+    def step(evf=None, evb=None):
+        b.fwd(plan, q, kk, v, o, lse, events=evf)
+        if backward:
+            b.bwd(plan, q, kk, v, o, lse, do, dq, dk, dv, events=evb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(nf + 1)] for _ in range(K)]
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)] if backward else [None] * K
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in [x for row in evf for x in row] + [x for row in evb if row for x in row]:
+        e.record()          # creates the HIP events before the timed region
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(evf[i], evb[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K
+
+    per_kernel = {}
+    for i in range(K):
+        for j, n in enumerate(fwd_names):
+            per_kernel.setdefault(n, []).append(evf[i][j].elapsed_time(evf[i][j + 1]))
+        if backward:
+            for j, n in enumerate(bwd_names):
+                per_kernel.setdefault(n, []).append(evb[i][j].elapsed_time(evb[i][j + 1]))
+    avg_ms = {n: float(np.mean(v_)) for n, v_ in per_kernel.items()}
+
+    D, Hq = m.head_dim, m.num_q_heads
+    pairs = plan.visible_pairs
+    useful = (4.0 + (10.0 if backward else 0.0)) * D * Hq * pairs
+    value = useful / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if m.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    # algorithmic work per launch of each kernel
+    esz = 2 if m.dtype == "bf16" else 4
+    q_bytes = plan.tq * Hq * D * esz
+    kv_bytes = plan.tk * m.num_kv_heads * D * esz
+    algo = {
+        "fwd": ("mfma", 4.0 * D * Hq * pairs),
+        "dkdv": ("mfma", 8.0 * D * Hq * pairs),
+        "dq": ("mfma", 6.0 * D * Hq * pairs),
+        "bwd_pre": ("hbm", 2.0 * q_bytes + plan.tq * Hq * 4),
+        "combine": ("hbm", q_bytes + plan.tq * Hq * 4),
+    }
+    if k == 2:   # the denoising step is bandwidth-bound: its forward is priced in bytes
+        algo["fwd"] = ("hbm", float(q_bytes + 2 * kv_bytes))
+    dom = max(avg_ms, key=lambda n: avg_ms[n])
+    bound, work = algo[dom]
+    dur_s = avg_ms[dom] * 1e-3
+    if bound == "mfma":
+        achieved = work / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        achieved = work / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["work_per_launch"] = work
+    roof["avg_launch_ms"] = round(avg_ms[dom], 4)
+    roof["traffic"] = traffic_from_profiles(dom, k)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu.pop("seconds", None)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[k],
+            "seed": k if args.seed is None else args.seed,
+            "tq": plan.tq, "tk": plan.tk, "visible_pairs_per_head": pairs,
+            "passes": "fwd+bwd" if backward else "fwd",
+            "useful_flop_per_step": useful,
+            "parallelism": "single GPU",
+        },
+        "kernels_ms": {n: round(t, 4) for n, t in avg_ms.items()},
+        "plan_ms": round(t_plan * 1e3, 3),
+        "wall_s": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,15 +54,20 @@ _lib.bd_attn_plan_serialize.argtypes = [_vp, _vp, _sz]
 _lib.bd_attn_plan_upload.argtypes = [_vp, _vp, _vp]
 _lib.bd_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.bd_attn_bwd.argtypes = [_vp] * 13
+_lib.bd_attn_fwd_timed.argtypes = [_vp] * 10 + [ctypes.c_int]
+_lib.bd_attn_bwd_timed.argtypes = [_vp] * 14 + [ctypes.c_int]
+_lib.bd_attn_plan_kernels.argtypes = [_vp, ctypes.c_int32]
+_lib.bd_attn_plan_kernels.restype = ctypes.c_int32
 _lib.bd_attn_plan_destroy.argtypes = [_vp]
 _lib.bd_attn_last_error.restype = ctypes.c_char_p
 _lib.bd_attn_version.restype = ctypes.c_char_p
 for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
-           "bd_attn_fwd", "bd_attn_bwd", "bd_attn_plan_destroy"):
+           "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_destroy"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
-            "bd_attn_fwd", "bd_attn_bwd", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version")
+            "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
+            "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version")
 
 
 class BdAttnError(RuntimeError):
@@ -121,6 +126,9 @@ class Plan:
         self.ws_fwd: Optional[torch.Tensor] = None
         self.ws_bwd: Optional[torch.Tensor] = None
 
+    def kernels(self, backward: bool) -> int:
+        return int(_lib.bd_attn_plan_kernels(self.handle, 1 if backward else 0))
+
     def host_blob(self):
         buf = (ctypes.c_int32 * (self.meta_bytes // 4))()
         _check(_lib.bd_attn_plan_serialize(self.handle, ctypes.cast(buf, _vp), self.meta_bytes))
@@ -158,7 +166,18 @@ def _expect(t, shape, dtype, name):
                          f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} cuda={t.is_cuda}")
 
 
-def fwd(plan: Plan, q, k, v, o=None, lse=None) -> Tuple[torch.Tensor, torch.Tensor]:
+def _events_arg(events):
+    if events is None:
+        return None, 0
+    for e in events:
+        if not e.cuda_event:          # torch creates the HIP event on first record
+            e.record()
+    arr = (_vp * len(events))(*[e.cuda_event for e in events])
+    return arr, len(events)
+
+
+def fwd(plan: Plan, q, k, v, o=None, lse=None, events=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward; ``events`` (optional list of torch.cuda.Event) time each kernel."""
     m = plan.meta
     _expect(q, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "q")
     _expect(k, (plan.tk, m.num_kv_heads, m.head_dim), plan.dtype, "k")
@@ -169,12 +188,18 @@ def fwd(plan: Plan, q, k, v, o=None, lse=None) -> Tuple[torch.Tensor, torch.Tens
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((plan.tq, m.num_q_heads), dtype=torch.float32, device=q.device)
-    _check(_lib.bd_attn_fwd(plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                            _ptr(plan.ws_fwd), _stream(q.device)))
+    args = (plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+            _ptr(plan.ws_fwd), _stream(q.device))
+    if events is None:
+        _check(_lib.bd_attn_fwd(*args))
+    else:
+        arr, n = _events_arg(events)
+        _check(_lib.bd_attn_fwd_timed(*args, ctypes.cast(arr, _vp), n))
     return o, lse
 
 
-def bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
+def bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, events=None):
+    """Backward; ``events`` (optional list of 4 torch.cuda.Event) time each kernel."""
     m = plan.meta
     _expect(do, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "do")
     _expect(o, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "o")
@@ -184,8 +209,13 @@ def bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _check(_lib.bd_attn_bwd(plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(plan.ws_bwd), _stream(q.device)))
+    args = (plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(plan.ws_bwd), _stream(q.device))
+    if events is None:
+        _check(_lib.bd_attn_bwd(*args))
+    else:
+        arr, n = _events_arg(events)
+        _check(_lib.bd_attn_bwd_timed(*args, ctypes.cast(arr, _vp), n))
     return dq, dk, dv
 
 

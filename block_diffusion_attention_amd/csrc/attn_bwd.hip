@@ -4,8 +4,8 @@
 // on the kernel: the backward pass uses the same visibility, dQ follows the
 // query traversal and dK/dV derive the valid query ranges of each key tile):
 //   bwd_pre : delta = rowsum(dO * O) per (token, query head), fp32;
-//   dkdv    : one workgroup per (key tile of up to 128 keys, kv head), looping
-//             over the query chunks that can see the tile; each wave owns 32 keys;
+//   dkdv    : one workgroup per (key tile of up to 64 keys, kv head), looping
+//             over the 64-row query chunks that can see the tile;
 //   dq      : one workgroup per (query tile, kv head), looping over the same key
 //             tiles as the forward pass.
 // Gradients of L = <dO, O>: dp = dO V^T, ds = p (dp - delta), dQ = scale ds K,
@@ -76,21 +76,29 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const KTile& kt, const CanvasQ* 
 }
 
 // ---------------------------------------------------------------- dK / dV
+// Workgroup: one key tile of up to 64 keys and one kv head. Wave w owns keys
+// 32*(w&1) .. +31 and, of every 64-row query chunk, rows 32*(w>>1) .. +31; the
+// two waves that share keys add their partial dK/dV through LDS at the end.
+// Query chunks (rows = tokens x grouped heads, with their LSE and delta) go
+// from global memory straight into LDS, two chunks in flight. The transposed
+// operands dO^T and Q^T of dV^T = dO^T P and dK^T = Q^T dS are read with the
+// LDS transpose read from the natural tiles.
 template <int D>
-__global__ void __launch_bounds__(256, 2) dkdv_bf16_kernel(BwdArgs a) {
-  constexpr int NKS = D / 16, NDB = D / 32, CH = D / 8;
-  constexpr int RG = D / 64;                   // rows per loader thread (32 rows x CH chunks / 256)
-  constexpr int QC = kQChunk;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[QC * NatTile<D>::kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[QC * NatTile<D>::kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sQt[D * QC];
-  __shared__ __attribute__((aligned(16))) bf16 sdOt[D * QC];
-  __shared__ __attribute__((aligned(16))) float sL[QC];
-  __shared__ __attribute__((aligned(16))) float sDl[QC];
-  __shared__ __attribute__((aligned(16))) int sLim[QC];
+__global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int QC = 64;                       // query rows per chunk
+  constexpr int TE = QC * D;
+  __shared__ __attribute__((aligned(1024))) bf16 sQ0[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sG0[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sQ1[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sG1[TE];
+  __shared__ __attribute__((aligned(256))) float sL0[QC], sD0[QC], sL1[QC], sD1[QC];
+  __shared__ __attribute__((aligned(256))) int sM0[QC], sM1[QC];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
+  const CmLane lo(lane);
+  const int kg = wave & 1, qh = wave >> 1;
   const int4 itv = reinterpret_cast<const int4*>(a.bwd_items)[blockIdx.x];
   if (itv.x < 0) return;
   const int kvh = itv.y;
@@ -101,121 +109,103 @@ __global__ void __launch_bounds__(256, 2) dkdv_bf16_kernel(BwdArgs a) {
   const bf16* __restrict__ dO = static_cast<const bf16*>(a.dout);
   const int G = a.G, B = a.B;
 
-  // this lane's key (column j of the wave's 32 keys)
-  const int kidx = wave * 32 + j;
+  const int kidx = kg * 32 + j;
   const bool key_ok = kidx < kt.n_keys;
-  const bool wave_live = wave * 32 < kt.n_keys;
+  const bool wave_live = kg * 32 < kt.n_keys;
   const int64_t krow = (int64_t)(kt.k_tok + min(kidx, kt.n_keys - 1)) * a.hkv + kvh;
-  bf16x8 kf[NKS], vf[NKS];
-#pragma unroll
-  for (int kk = 0; kk < NKS; ++kk) {
-    kf[kk] = *reinterpret_cast<const bf16x8*>(K + krow * D + kk * 16 + h * 8);
-    vf[kk] = *reinterpret_cast<const bf16x8*>(V + krow * D + kk * 16 + h * 8);
-  }
-  const int kpos = kt.p0 >= 0 ? kt.p0 + kidx : 0;
-  const int wpos_lo = kt.p0 + wave * 32;                // lowest key position of the wave
-  const int wpos_hi = kt.p0 + min(wave * 32 + 31, kt.n_keys - 1);
-
-  f32x16 dkt[NDB], dvt[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
+  const bool canvas_keys = kt.p0 < 0;
+  const int kpos = canvas_keys ? 0 : kt.p0 + kidx;
+  const int wpos_lo = kt.p0 + kg * 32;
+  const int wpos_hi = kt.p0 + min(kg * 32 + 31, kt.n_keys - 1);
 
   const int qct = QC / G;                               // tokens per chunk
   const int nc0 = (kt.cq_len + qct - 1) / qct;
   const int cpc = (B + qct - 1) / qct;
   const int nchunks = nc0 + kt.cv_count * cpc;
 
-  // loader: rows lg*RG.. of the chunk, 16-byte chunk lc
-  const int lc = tid % CH, lg = tid / CH;
-  u32x4 pq[RG], pd[RG];
-  float p_l = 0.f, p_dl = 0.f;
-  int p_lim = 0;
-  auto load_chunk = [&](int c) {
+  // async fetch of chunk c: Q and dO rows, LSE and delta per row, row limits
+  auto issue = [&](int c, bf16* dQ_, bf16* dG_, float* dL_, float* dD_, int* dM_) {
     const ChunkGeom g = chunk_geom(kt, a.canvq, c, nc0, cpc, qct);
-#pragma unroll
-    for (int i = 0; i < RG; ++i) {
-      const int r = lg * RG + i;
+    const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
+    auto rowp = [&](const bf16* base) {
+      return [=](int r) {
+        const int t = r / G, gh = r - (r / G) * G;
+        return base + ((int64_t)(g.tok0 + t) * a.hq + kvh * G + gh) * D;
+      };
+    };
+    tile_fetch<D>(dQ_, rowp(Q), nrows, wave, lane);
+    tile_fetch<D>(dG_, rowp(dO), nrows, wave, lane);
+    if (wave < 2) {                                     // 64 rows x 4 bytes each
+      const int r = min(lane, nrows - 1);
       const int t = r / G, gh = r - (r / G) * G;
-      if (t < g.ntok && r < qct * G) {
-        const int64_t off = ((int64_t)(g.tok0 + t) * a.hq + kvh * G + gh) * D + lc * 8;
-        pq[i] = *reinterpret_cast<const u32x4*>(Q + off);
-        pd[i] = *reinterpret_cast<const u32x4*>(dO + off);
-      } else {
-        pq[i] = u32x4{0, 0, 0, 0};
-        pd[i] = u32x4{0, 0, 0, 0};
-      }
+      const int64_t qr = (int64_t)(g.tok0 + t) * a.hq + kvh * G + gh;
+      const float* src = wave == 0 ? a.lse + qr : a.delta + qr;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(wave == 0 ? dL_ : dD_), 4, 0, 0);
+    } else if (wave == 2) {
+      const int r = lane, t = r / G;
+      int lim = -1;                                     // padding rows see nothing
+      if (r < nrows) lim = g.pos0 >= 0 ? ((g.pos0 + t) / B + 1) * B : g.lim;
+      dM_[r] = lim;
     }
-    if (tid < QC) {
-      const int r = tid, t = r / G, gh = r - (r / G) * G;
-      if (t < g.ntok && r < qct * G) {
-        const int64_t qr = (int64_t)(g.tok0 + t) * a.hq + kvh * G + gh;
-        p_l = a.lse[qr] * kLog2e;
-        p_dl = a.delta[qr];
-        p_lim = g.pos0 >= 0 ? ((g.pos0 + t) / B + 1) * B : g.lim;
-      } else {
-        p_l = INFINITY; p_dl = 0.f; p_lim = 0;
-      }
-    }
-  };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int i = 0; i < RG; ++i) {
-      *reinterpret_cast<u32x4*>(sQ + NatTile<D>::off(lg * RG + i, lc * 8)) = pq[i];
-      *reinterpret_cast<u32x4*>(sdO + NatTile<D>::off(lg * RG + i, lc * 8)) = pd[i];
-    }
-    const int col = kperm(lg * RG);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = lc * 8 + e, w = e >> 1;
-      if constexpr (RG == 2) {
-        *reinterpret_cast<uint32_t*>(sQt + TrTile<QC>::off(d, col)) = pick_pair(pq[0][w], pq[1][w], e & 1);
-        *reinterpret_cast<uint32_t*>(sdOt + TrTile<QC>::off(d, col)) = pick_pair(pd[0][w], pd[1][w], e & 1);
-      } else {
-        sQt[TrTile<QC>::off(d, col)] = __builtin_bit_cast(bf16, (uint16_t)((e & 1) ? (pq[0][w] >> 16) : (pq[0][w] & 0xffffu)));
-        sdOt[TrTile<QC>::off(d, col)] = __builtin_bit_cast(bf16, (uint16_t)((e & 1) ? (pd[0][w] >> 16) : (pd[0][w] & 0xffffu)));
-      }
-    }
-    if (tid < QC) { sL[tid] = p_l; sDl[tid] = p_dl; sLim[tid] = p_lim; }
   };
 
-  if (nchunks > 0) load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();
-    store_chunk();
-    __syncthreads();
+  bf16x8 kf[NKS], vf[NKS];
+#pragma unroll
+  for (int kk = 0; kk < NKS; ++kk) {
+    kf[kk] = *reinterpret_cast<const bf16x8*>(K + krow * D + kk * 16 + h * 8);
+    vf[kk] = *reinterpret_cast<const bf16x8*>(V + krow * D + kk * 16 + h * 8);
+  }
+  f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
+
+  if (nchunks > 0) issue(0, sQ0, sG0, sL0, sD0, sM0);
+
+  auto step = [&](int c, const bf16* cQ, const bf16* cG, const float* cL, const float* cD, const int* cM,
+                  bf16* nQ, bf16* nG, float* nL, float* nD, int* nM) __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();                                    // chunk c landed; the other stage is free
+    if (c + 1 < nchunks) issue(c + 1, nQ, nG, nL, nD, nM);
     const ChunkGeom g = chunk_geom(kt, a.canvq, c, nc0, cpc, qct);
-    if (c + 1 < nchunks) load_chunk(c + 1);
-
-    // visibility of this chunk for the wave's keys
+    // visibility of this wave's 32 rows for its 32 keys
+    const int r_lo = qh * 32, r_hi = min(qh * 32 + 31, g.ntok * G - 1);
+    if (r_hi < r_lo || !wave_live) return;              // no valid row in this half, or no key
     int lim_lo, lim_hi;
-    if (g.pos0 >= 0) { lim_lo = (g.pos0 / B + 1) * B; lim_hi = ((g.pos0 + g.ntok - 1) / B + 1) * B; }
-    else { lim_lo = lim_hi = g.lim; }
-    const bool canvas_keys = kt.p0 < 0;
-    const bool skip = !wave_live || (!canvas_keys && wpos_lo >= lim_hi);
-    const bool need_mask = !canvas_keys && wpos_hi >= lim_lo;
-    if (skip) continue;
+    if (g.pos0 >= 0) {
+      lim_lo = ((g.pos0 + r_lo / G) / B + 1) * B;
+      lim_hi = ((g.pos0 + r_hi / G) / B + 1) * B;
+    } else {
+      lim_lo = lim_hi = g.lim;
+    }
+    const bool half_pad = r_hi < qh * 32 + 31;
+    if (!canvas_keys && wpos_lo >= lim_hi) return;      // all of the wave's keys are invisible
+    const bool need_mask = half_pad || (!canvas_keys && wpos_hi >= lim_lo);
 
     f32x16 s = f32x16{}, dp = f32x16{};
-    const bf16* qp = sQ + NatTile<D>::off(j, h * 8);
-    const bf16* gp = sdO + NatTile<D>::off(j, h * 8);
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) {
-      s = mfma32(*reinterpret_cast<const bf16x8*>(qp + kk * 16), kf[kk], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(gp + kk * 16), vf[kk], dp);
+      s = mfma32(cm_row8(cQ, lo, r_lo, kk), kf[kk], s);
+      dp = mfma32(cm_row8(cG, lo, r_lo, kk), vf[kk], dp);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int4 mv = *reinterpret_cast<const int4*>(cM + r_lo + 8 * g4 + 4 * h);
+        const int lims[4] = {mv.x, mv.y, mv.z, mv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (kpos >= lims[e]) s[g4 * 4 + e] = -INFINITY;
+      }
     }
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const int r0 = 8 * g4 + 4 * h;
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(sL + r0);
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(sDl + r0);
-      const int4 mv = *reinterpret_cast<const int4*>(sLim + r0);
-      const int lims[4] = {mv.x, mv.y, mv.z, mv.w};
+      const int r0 = r_lo + 8 * g4 + 4 * h;
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(cL + r0);
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(cD + r0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = g4 * 4 + e;
-        float x = s[r] * a.scale_log2 - lv[e];
-        if (need_mask && kpos >= lims[e]) x = -INFINITY;
-        const float p = fast_exp2(x);
+        const float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -lv[e] * kLog2e));
         s[r] = p;
         dp[r] = p * (dp[r] - dv[e]);
       }
@@ -230,46 +220,72 @@ __global__ void __launch_bounds__(256, 2) dkdv_bf16_kernel(BwdArgs a) {
       sb[ks] = pack8(t1);
     }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + j;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        dvt[db] = mfma32(*reinterpret_cast<const bf16x8*>(sdOt + TrTile<QC>::off(d, ks * 16 + h * 8)), pb[ks], dvt[db]);
-        dkt[db] = mfma32(*reinterpret_cast<const bf16x8*>(sQt + TrTile<QC>::off(d, ks * 16 + h * 8)), sb[ks], dkt[db]);
+      for (int db = 0; db < NDB; ++db) {
+        dvt[db] = mfma32(cm_tr8(cG, lo, r_lo + ks * 16, db * 32), pb[ks], dvt[db]);
+        dkt[db] = mfma32(cm_tr8(cQ, lo, r_lo + ks * 16, db * 32), sb[ks], dkt[db]);
       }
-    }
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, sQ0, sG0, sL0, sD0, sM0, sQ1, sG1, sL1, sD1, sM1);
+    if (c + 1 < nchunks) step(c + 1, sQ1, sG1, sL1, sD1, sM1, sQ0, sG0, sL0, sD0, sM0);
   }
 
-  if (key_ok) {
+  // add the partial sums of the two query halves: waves 2, 3 hand theirs to 0, 1
+  wait_vmem();
+  __syncthreads();
+  float* redk = reinterpret_cast<float*>(kg == 0 ? sQ0 : sQ1);   // NDB*16*64 floats = one tile
+  float* redv = reinterpret_cast<float*>(kg == 0 ? sG0 : sG1);
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        redk[(db * 16 + r) * 64 + lane] = dkt[db][r];
+        redv[(db * 16 + r) * 64 + lane] = dvt[db][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 0 && key_ok) {
     bf16* dkp = static_cast<bf16*>(a.dk) + krow * D;
     bf16* dvp = static_cast<bf16*>(a.dv) + krow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
+        float kx[4], vx[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = g4 * 4 + e;
+          kx[e] = (dkt[db][r] + redk[(db * 16 + r) * 64 + lane]) * a.scale;
+          vx[e] = dvt[db][r] + redv[(db * 16 + r) * 64 + lane];
+        }
         const int d0 = db * 32 + g4 * 8 + h * 4;
-        u32x2 vk, vv;
-        vk[0] = pack_bf16x2(dkt[db][g4 * 4 + 0] * a.scale, dkt[db][g4 * 4 + 1] * a.scale);
-        vk[1] = pack_bf16x2(dkt[db][g4 * 4 + 2] * a.scale, dkt[db][g4 * 4 + 3] * a.scale);
-        vv[0] = pack_bf16x2(dvt[db][g4 * 4 + 0], dvt[db][g4 * 4 + 1]);
-        vv[1] = pack_bf16x2(dvt[db][g4 * 4 + 2], dvt[db][g4 * 4 + 3]);
-        *reinterpret_cast<u32x2*>(dkp + d0) = vk;
-        *reinterpret_cast<u32x2*>(dvp + d0) = vv;
+        *reinterpret_cast<u32x2*>(dkp + d0) = u32x2{pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3])};
+        *reinterpret_cast<u32x2*>(dvp + d0) = u32x2{pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3])};
       }
   }
 }
 
 // ---------------------------------------------------------------- dQ
+// Workgroup: one query tile (up to 128 rows) and one kv head, over the same key
+// tiles as the forward pass. Per wave 32 rows; scores transposed as in the
+// forward pass. K and V tiles go straight into LDS (two stages); K^T for
+// dQ^T = K^T dS^T is read with the LDS transpose read.
 template <int D>
 __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   constexpr int KT = kKTile;
-  constexpr int NDB = D / 32, NKS = D / 16, CH = D / 8, KG = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sK[KT * NatTile<D>::kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sV[KT * NatTile<D>::kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sKt[D * KT];
+  constexpr int NDB = D / 32, NKS = D / 16;
+  constexpr int TE = KT * D;
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[TE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
+  const CmLane lo(lane);
   const int4 itv = reinterpret_cast<const int4*>(a.dq_items)[blockIdx.x];
   if (itv.x < 0) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
@@ -286,6 +302,21 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   const bool row_ok = row < qt.n_tok * G;
   if (t >= qt.n_tok) t = qt.n_tok - 1;
   const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * G + gh;
+  const int L = row_limit(qt, t, a.B);
+  const int n1 = (qt.lim_max + KT - 1) / KT;
+  const int64_t kv_stride = (int64_t)a.hkv * D;
+
+  auto issue = [&](int kt, bf16* dK, bf16* dV) {
+    int base, nvalid;
+    if (kt < n1) { base = qt.k_ctx + kt * KT; nvalid = min(KT, qt.lim_max - kt * KT); }
+    else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
+    const bf16* kb = K + (int64_t)base * kv_stride + kvh * D;
+    const bf16* vb = V + (int64_t)base * kv_stride + kvh * D;
+    tile_fetch<D>(dK, [&](int r) { return kb + r * kv_stride; }, nvalid, wave, lane);
+    tile_fetch<D>(dV, [&](int r) { return vb + r * kv_stride; }, nvalid, wave, lane);
+  };
+  if (kt_begin < kt_end) issue(kt_begin, sK0, sV0);
+
   bf16x8 qf[NKS], df[NKS];
 #pragma unroll
   for (int kk = 0; kk < NKS; ++kk) {
@@ -294,81 +325,42 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   }
   const float lse2 = a.lse[qrow] * kLog2e;
   const float dl = a.delta[qrow];
-  const int L = row_limit(qt, t, a.B);
-  const int n1 = (qt.lim_max + KT - 1) / KT;
-
-  const int lc = tid % CH, lg = tid / CH;
-  u32x4 pk[KG], pv[KG];
-  auto load_tile = [&](int kt) {
-    int base, nvalid;
-    if (kt < n1) { base = qt.k_ctx + kt * KT; nvalid = min(KT, qt.lim_max - kt * KT); }
-    else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
-#pragma unroll
-    for (int i = 0; i < KG; ++i) {
-      const int key = lg * KG + i;
-      if (key < nvalid) {
-        const int64_t off = ((int64_t)(base + key) * a.hkv + kvh) * D + lc * 8;
-        pk[i] = *reinterpret_cast<const u32x4*>(K + off);
-        pv[i] = *reinterpret_cast<const u32x4*>(V + off);
-      } else {
-        pk[i] = u32x4{0, 0, 0, 0};
-        pv[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KG; ++i) {
-      *reinterpret_cast<u32x4*>(sK + NatTile<D>::off(lg * KG + i, lc * 8)) = pk[i];
-      *reinterpret_cast<u32x4*>(sV + NatTile<D>::off(lg * KG + i, lc * 8)) = pv[i];
-    }
-    const int col = kperm(lg * KG);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = lc * 8 + e, w = e >> 1;
-      if constexpr (KG == 4) {
-        *reinterpret_cast<u32x2*>(sKt + TrTile<KT>::off(d, col)) =
-            u32x2{pick_pair(pk[0][w], pk[1][w], e & 1), pick_pair(pk[2][w], pk[3][w], e & 1)};
-      } else {
-        *reinterpret_cast<uint32_t*>(sKt + TrTile<KT>::off(d, col)) = pick_pair(pk[0][w], pk[1][w], e & 1);
-      }
-    }
-  };
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  if (kt_begin < kt_end) load_tile(kt_begin);
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
+
+  auto step = [&](int kt, const bf16* sK, const bf16* sV, bf16* nK, bf16* nV) __attribute__((always_inline)) {
+    wait_vmem();
     __syncthreads();
-    store_tile();
-    __syncthreads();
+    if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
     const bool r1 = kt < n1;
     const int kpos0 = r1 ? kt * KT : (kt - n1) * KT;
     const int lim = r1 ? L : qt.n_own;
     const bool need_mask = kpos0 + KT > (r1 ? qt.lim_min : qt.n_own);
-    if (kt + 1 < kt_end) load_tile(kt + 1);
 
     f32x16 s[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-      const bf16* kp = sK + NatTile<D>::off(kb * 32 + j, h * 8);
-      const bf16* vp = sV + NatTile<D>::off(kb * 32 + j, h * 8);
+    for (int kb = 0; kb < 2; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
 #pragma unroll
-      for (int kk = 0; kk < NKS; ++kk) {
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qf[kk], s[kb]);
-        dp[kb] = mfma32(*reinterpret_cast<const bf16x8*>(vp + kk * 16), df[kk], dp[kb]);
+    for (int kk = 0; kk < NKS; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma32(cm_row8(sK, lo, kb * 32, kk), qf[kk], s[kb]);
+        dp[kb] = mfma32(cm_row8(sV, lo, kb * 32, kk), df[kk], dp[kb]);
       }
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kpos0 + kb * 32 + c_row(r, h) >= lim) s[kb][r] = -INFINITY;
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * a.scale_log2 - lse2;
-        if (need_mask && (kpos0 + kb * 32 + c_row(r, h) >= lim)) x = -INFINITY;
-        const float p = fast_exp2(x);
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], a.scale_log2, -lse2));
         dp[kb][r] = p * (dp[kb][r] - dl);
       }
     bf16x8 sb[4];
@@ -380,13 +372,16 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
       sb[kq] = pack8(tmp);
     }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + j;
+    for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-        acc[db] = mfma32(*reinterpret_cast<const bf16x8*>(sKt + TrTile<KT>::off(d, kq * 16 + h * 8)), sb[kq], acc[db]);
-    }
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = mfma32(cm_tr8(sK, lo, kq * 16, db * 32), sb[kq], acc[db]);
+  };
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    step(kt, sK0, sV0, sK1, sV1);
+    if (kt + 1 < kt_end) step(kt + 1, sK1, sV1, sK0, sV0);
   }
+
   if (row_ok) {
     bf16* op = static_cast<bf16*>(a.dq) + qrow * D;
 #pragma unroll

@@ -11,9 +11,9 @@
 // Per wave, 32 query rows. Scores are computed transposed, S^T = K Q^T, with
 // the 32x32x16 MFMA so that each lane owns one query row: row maxima and sums
 // need one cross-half exchange instead of a 32-lane reduction, and the
-// probabilities feed the P V product straight from registers. V is staged in
-// LDS transposed (a 4x8 register transpose per loader thread) so that its MFMA
-// operand is one 16-byte LDS read.
+// probabilities feed the P V product straight from registers. K and V tiles go
+// from global memory straight into LDS (global_load_lds, two pipeline stages,
+// no register staging); the V^T operand is read with the LDS transpose read.
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -22,64 +22,21 @@ namespace bdattn {
 namespace {
 
 template <int D>
-struct FwdTileLoader {
-  static constexpr int CH = D / 8;        // 16-byte chunks per row
-  static constexpr int KG = D / 32;       // keys per loader thread (64 keys x CH chunks / 256 threads)
-  int lc, lg;
-  u32x4 pk[KG], pv[KG];
-
-  __device__ void init(int tid) { lc = tid % CH; lg = tid / CH; }
-
-  __device__ void load(const bf16* __restrict__ K, const bf16* __restrict__ V, int hkv, int kvh,
-                       int base, int nvalid) {
-#pragma unroll
-    for (int i = 0; i < KG; ++i) {
-      const int key = lg * KG + i;
-      if (key < nvalid) {
-        const int64_t off = ((int64_t)(base + key) * hkv + kvh) * D + lc * 8;
-        pk[i] = *reinterpret_cast<const u32x4*>(K + off);
-        pv[i] = *reinterpret_cast<const u32x4*>(V + off);
-      } else {
-        pk[i] = u32x4{0, 0, 0, 0};
-        pv[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-
-  __device__ void store_k(bf16* sK) const {
-#pragma unroll
-    for (int i = 0; i < KG; ++i)
-      *reinterpret_cast<u32x4*>(sK + NatTile<D>::off(lg * KG + i, lc * 8)) = pk[i];
-  }
-
-  // V^T: element e of the 16-byte chunk becomes row lc*8+e, the KG keys become
-  // KG contiguous columns (kperm keeps aligned groups of 4 together).
-  __device__ void store_vt(bf16* sVt) const {
-    const int col = kperm(lg * KG);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = lc * 8 + e;
-      const int w = e >> 1;
-      if constexpr (KG == 4) {
-        *reinterpret_cast<u32x2*>(sVt + TrTile<kKTile>::off(d, col)) =
-            u32x2{pick_pair(pv[0][w], pv[1][w], e & 1), pick_pair(pv[2][w], pv[3][w], e & 1)};
-      } else {
-        *reinterpret_cast<uint32_t*>(sVt + TrTile<kKTile>::off(d, col)) = pick_pair(pv[0][w], pv[1][w], e & 1);
-      }
-    }
-  }
-};
-
-template <int D>
 __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   constexpr int KT = kKTile;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  __shared__ __attribute__((aligned(16))) bf16 sK[KT * NatTile<D>::kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sVt[D * KT];
+  constexpr int TE = KT * D;                       // elements of one K or V tile
+  // two pipeline stages of (K tile, V tile), filled asynchronously; separate
+  // arrays so the compiler can tell a stage being read from the one being filled
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[TE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
+  const CmLane lo(lane);
   const int idx = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
   const int4 itv = reinterpret_cast<const int4*>(a.items)[idx];
   if (itv.x < 0) return;
@@ -97,25 +54,26 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   if (t >= qt.n_tok) t = qt.n_tok - 1;          // padding rows mirror the last token
   const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * G + gh;
 
+  const int L = row_limit(qt, t, a.B);
+  const int n1 = (qt.lim_max + KT - 1) / KT;
+  const int64_t kv_stride = (int64_t)a.hkv * D;
+
+  auto issue = [&](int kt, bf16* dK, bf16* dV) {
+    int base, nvalid;
+    if (kt < n1) { base = qt.k_ctx + kt * KT; nvalid = min(KT, qt.lim_max - kt * KT); }
+    else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
+    const bf16* kb = K + (int64_t)base * kv_stride + kvh * D;
+    const bf16* vb = V + (int64_t)base * kv_stride + kvh * D;
+    tile_fetch<D>(dK, [&](int r) { return kb + r * kv_stride; }, nvalid, wave, lane);
+    tile_fetch<D>(dV, [&](int r) { return vb + r * kv_stride; }, nvalid, wave, lane);
+  };
+  issue(kt_begin, sK0, sV0);
+
   bf16x8 qf[NKS];
   {
     const bf16* qp = Q + qrow * D + h * 8;
 #pragma unroll
     for (int kk = 0; kk < NKS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
-  }
-  const int L = row_limit(qt, t, a.B);
-  const int n1 = (qt.lim_max + KT - 1) / KT;
-
-  FwdTileLoader<D> ld;
-  ld.init(tid);
-  auto tile_geom = [&](int kt, int& base, int& nvalid) {
-    if (kt < n1) { base = qt.k_ctx + kt * KT; nvalid = min(KT, qt.lim_max - kt * KT); }
-    else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
-  };
-  {
-    int base, nv;
-    tile_geom(kt_begin, base, nv);
-    ld.load(K, V, a.hkv, kvh, base, nv);
   }
 
   float m = -INFINITY, l = 0.f;
@@ -123,43 +81,39 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    __syncthreads();
-    ld.store_k(sK);
-    ld.store_vt(sVt);
-    __syncthreads();
+  auto step = [&](int kt, const bf16* sK, const bf16* sV, bf16* nK, bf16* nV) __attribute__((always_inline)) {
+    wait_vmem();
+    __syncthreads();                  // tile kt is in LDS; the other stage is free again
+    if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
     const bool r1 = kt < n1;
     const int kpos0 = r1 ? kt * KT : (kt - n1) * KT;
     const int lim = r1 ? L : qt.n_own;
     const bool need_mask = kpos0 + KT > (r1 ? qt.lim_min : qt.n_own);
-    if (kt + 1 < kt_end) {
-      int base, nv;
-      tile_geom(kt + 1, base, nv);
-      ld.load(K, V, a.hkv, kvh, base, nv);
-    }
 
-    // S^T = K Q^T : two 32-key blocks
+    // S^T = K Q^T : two 32-key blocks, each lane one query row
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const bf16* kp = sK + NatTile<D>::off(kb * 32 + j, h * 8);
 #pragma unroll
       for (int kk = 0; kk < NKS; ++kk)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kp + kk * 16), qf[kk], s[kb]);
+        s[kb] = mfma32(cm_row8(sK, lo, kb * 32, kk), qf[kk], s[kb]);
     }
 
+    // masking only on tiles that cross a row limit or the end of a range
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kpos0 + kb * 32 + c_row(r, h) >= lim) s[kb][r] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * a.scale_log2;
-        if (need_mask && (kpos0 + kb * 32 + c_row(r, h) >= lim)) x = -INFINITY;
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, swap_halves(mx));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, swap_halves(mx)) * a.scale_log2;     // running max in the log2 domain
     const bool need = mx > m + kRescaleSlack;
     if (__any(need)) {
       const float mnew = need ? mx : m;
@@ -177,7 +131,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[kb][r] - mref);
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], a.scale_log2, -mref));
         s[kb][r] = p;
         ls += p;
       }
@@ -191,14 +145,16 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
       for (int e = 0; e < 8; ++e) tmp[e] = s[kq >> 1][(kq & 1) * 8 + e];
       pb[kq] = pack8(tmp);
     }
+    // O^T += V^T P^T, V^T read transposed out of the natural V tile
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + j;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq)
-        acc[db] = mfma32(*reinterpret_cast<const bf16x8*>(sVt + TrTile<KT>::off(d, kq * 16 + h * 8)),
-                         pb[kq], acc[db]);
-    }
+        acc[db] = mfma32(cm_tr8(sV, lo, kq * 16, db * 32), pb[kq], acc[db]);
+  };
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    step(kt, sK0, sV0, sK1, sV1);
+    if (kt + 1 < kt_end) step(kt + 1, sK1, sV1, sK0, sV0);
   }
 
   const float lt = l + swap_halves(l);

@@ -34,6 +34,19 @@ bd_attn_status hip_status(hipError_t e, const char* what) {
   return fail(BD_ATTN_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// Records events[i] (if any) on the stream; i beyond n is ignored.
+struct EventMarks {
+  void* const* ev;
+  int n;
+  hipStream_t s;
+  hipError_t mark(int i) const {
+    if (!ev || i >= n || !ev[i]) return hipSuccess;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
+  }
+};
+
+int fwd_kernels(const Plan& p) { return (p.desc.dtype == BD_ATTN_BF16 && p.split) ? 2 : 1; }
+
 template <class T>
 const T* section(const void* meta, int64_t off) {
   return reinterpret_cast<const T*>(static_cast<const int32_t*>(meta) + off);
@@ -93,10 +106,13 @@ bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_
                     "hipMemcpyAsync(meta)");
 }
 
-bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
-                           const void* v, void* o, float* lse, void* ws, bd_attn_stream_t stream) {
+static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                               const void* v, void* o, float* lse, void* ws, bd_attn_stream_t stream,
+                               void* const* events, int n_events) {
   if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
   const Plan& p = plan->p;
+  if (events && n_events < fwd_kernels(p) + 1)
+    return fail(BD_ATTN_EINVAL, "n_events must be at least the number of forward kernels + 1");
   bd_attn_status st;
   if ((st = check_ptr(meta_dev, "meta_dev")) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
       (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
@@ -108,6 +124,7 @@ bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev, const void
     if (!aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const EventMarks ev{events, events ? n_events : 0, s};
   bdattn::FwdArgs a{};
   a.qtiles = section<int32_t>(meta_dev, p.off_qtiles);
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -116,35 +133,54 @@ bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev, const void
   a.scale_log2 = p.scale * 1.4426950408889634f;
   const int D = p.desc.head_dim;
   hipError_t e;
+  if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
   if (!bf16) {
     a.items = section<bdattn::FwdItem>(meta_dev, p.off_dq);
     e = bdattn::launch_fwd_f32(a, D, (int)p.dq_items.size(), s);
-    return hip_status(e, "fwd_f32 launch");
+    if ((st = hip_status(e, "fwd_f32 launch"))) return st;
+    return hip_status(ev.mark(1), "hipEventRecord");
   }
   a.items = section<bdattn::FwdItem>(meta_dev, p.off_fwd);
   if (!split) {
     e = bdattn::launch_fwd_bf16(a, D, (int)p.fwd_items.size(), s);
-    return hip_status(e, "fwd launch");
+    if ((st = hip_status(e, "fwd launch"))) return st;
+    return hip_status(ev.mark(1), "hipEventRecord");
   }
   a.order = section<int32_t>(meta_dev, p.off_fwd_order);
   a.part_o = static_cast<float*>(ws);
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_lse);
   e = bdattn::launch_fwd_bf16(a, D, (int)p.fwd_order.size(), s);
   if ((st = hip_status(e, "fwd (split) launch"))) return st;
+  if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
   bdattn::CombArgs c{};
   c.qtiles = a.qtiles;
   c.items = section<bdattn::CombItem>(meta_dev, p.off_comb);
   c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
   c.hq = a.hq; c.G = a.G;
   e = bdattn::launch_combine(c, D, true, (int)p.comb_items.size(), s);
-  return hip_status(e, "combine launch");
+  if ((st = hip_status(e, "combine launch"))) return st;
+  return hip_status(ev.mark(2), "hipEventRecord");
 }
 
-bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
-                           const void* v, const void* o, const float* lse, const void* dout, void* dq,
-                           void* dk, void* dv, void* ws, bd_attn_stream_t stream) {
+bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                           const void* v, void* o, float* lse, void* ws, bd_attn_stream_t stream) {
+  return fwd_impl(plan, meta_dev, q, k, v, o, lse, ws, stream, nullptr, 0);
+}
+
+bd_attn_status bd_attn_fwd_timed(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, void* ws, bd_attn_stream_t stream,
+                                 void* const* events, int n_events) {
+  if (!events) return fail(BD_ATTN_EINVAL, "events is NULL");
+  return fwd_impl(plan, meta_dev, q, k, v, o, lse, ws, stream, events, n_events);
+}
+
+static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                               const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                               void* dk, void* dv, void* ws, bd_attn_stream_t stream,
+                               void* const* events, int n_events) {
   if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
   const Plan& p = plan->p;
+  if (events && n_events < 4) return fail(BD_ATTN_EINVAL, "n_events must be at least 4 for the backward pass");
   bd_attn_status st;
   if ((st = check_ptr(meta_dev, "meta_dev")) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
       (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")) ||
@@ -154,6 +190,7 @@ bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev, const void
   if (!ws) return fail(BD_ATTN_EWORKSPACE, "bd_attn_bwd needs a workspace of ws_bwd_bytes");
   if (!aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const EventMarks ev{events, events ? n_events : 0, s};
   const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
   const int D = p.desc.head_dim;
   bdattn::BwdArgs a{};
@@ -169,18 +206,37 @@ bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev, const void
   a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.B = p.desc.block_size;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
+  if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
   hipError_t e = bdattn::launch_bwd_pre(a, D, bf16, s);
   if ((st = hip_status(e, "bwd_pre launch"))) return st;
-  if (bf16) {
-    e = bdattn::launch_dkdv_bf16(a, D, (int)p.bwd_items.size(), s);
-    if ((st = hip_status(e, "dkdv launch"))) return st;
-    e = bdattn::launch_dq_bf16(a, D, (int)p.dq_items.size(), s);
-    return hip_status(e, "dq launch");
-  }
-  e = bdattn::launch_dkdv_f32(a, D, (int)p.bwd_items.size(), s);
-  if ((st = hip_status(e, "dkdv_f32 launch"))) return st;
-  e = bdattn::launch_dq_f32(a, D, (int)p.dq_items.size(), s);
-  return hip_status(e, "dq_f32 launch");
+  if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
+  e = bf16 ? bdattn::launch_dkdv_bf16(a, D, (int)p.bwd_items.size(), s)
+           : bdattn::launch_dkdv_f32(a, D, (int)p.bwd_items.size(), s);
+  if ((st = hip_status(e, "dkdv launch"))) return st;
+  if ((st = hip_status(ev.mark(2), "hipEventRecord"))) return st;
+  e = bf16 ? bdattn::launch_dq_bf16(a, D, (int)p.dq_items.size(), s)
+           : bdattn::launch_dq_f32(a, D, (int)p.dq_items.size(), s);
+  if ((st = hip_status(e, "dq launch"))) return st;
+  return hip_status(ev.mark(3), "hipEventRecord");
+}
+
+bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                           void* dk, void* dv, void* ws, bd_attn_stream_t stream) {
+  return bwd_impl(plan, meta_dev, q, k, v, o, lse, dout, dq, dk, dv, ws, stream, nullptr, 0);
+}
+
+bd_attn_status bd_attn_bwd_timed(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                                 const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, void* ws, bd_attn_stream_t stream,
+                                 void* const* events, int n_events) {
+  if (!events) return fail(BD_ATTN_EINVAL, "events is NULL");
+  return bwd_impl(plan, meta_dev, q, k, v, o, lse, dout, dq, dk, dv, ws, stream, events, n_events);
+}
+
+int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward) {
+  if (!plan) return 0;
+  return backward ? 3 : fwd_kernels(plan->p);
 }
 
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan) {

@@ -21,9 +21,10 @@ namespace bdattn {
 constexpr int kQRows = 128;
 // Forward / dQ key tile (keys per main-loop step).
 constexpr int kKTile = 64;
-// dK/dV: keys per workgroup (4 waves x 32) and query rows per inner step.
-constexpr int kKBlock = 128;
-constexpr int kQChunk = 32;
+// dK/dV: keys per workgroup (2 groups of 32 keys x 2 halves of each query chunk).
+constexpr int kKBlock = 64;
+// Largest supported group size (query heads per kv head).
+constexpr int kMaxGroup = 32;
 
 // Serialized plan: a header of kBlobHeaderInts int32 (magic, format version,
 // then count and int32 offset of each section: query tiles, forward items,

@@ -102,7 +102,7 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   if (d->head_dim != 64 && d->head_dim != 128) { *err = "head_dim must be 64 or 128"; return BD_ATTN_EUNSUPPORTED; }
   if (!(std::isfinite(d->softmax_scale))) { *err = "softmax_scale must be finite"; return BD_ATTN_EINVAL; }
   const int G = d->num_q_heads / d->num_kv_heads;
-  if (G > kQChunk) { *err = "group size num_q_heads/num_kv_heads above 32 is not supported"; return BD_ATTN_EUNSUPPORTED; }
+  if (G > kMaxGroup) { *err = "group size num_q_heads/num_kv_heads above 32 is not supported"; return BD_ATTN_EUNSUPPORTED; }
   if (d->canvas_offsets[0] != 0) { *err = "canvas_offsets[0] must be 0"; return BD_ATTN_EINVAL; }
   for (int s = 0; s < S; ++s)
     if (d->canvas_offsets[s + 1] < d->canvas_offsets[s]) { *err = "canvas_offsets must be non-decreasing"; return BD_ATTN_EINVAL; }

@@ -135,6 +135,28 @@ bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev,
                            const void* o, const float* lse, const void* dout,
                            void* dq, void* dk, void* dv, void* ws, bd_attn_stream_t stream);
 
+/* Same as bd_attn_fwd / bd_attn_bwd, and in addition records caller-created
+ * hipEvent_t handles (passed as void*) on the stream around the kernels, for
+ * per-kernel timing on the stream that runs them: events[0] before the first
+ * kernel and events[i] right after the i-th one. The forward pass launches 1
+ * kernel (2 on the split path: partial results, then their merge; the count is
+ * bd_attn_plan_kernels(plan, 0)), the backward pass 3 (delta = rowsum(dO * O),
+ * dK/dV, dQ). n_events must be at least kernels + 1, else EINVAL and nothing is
+ * enqueued. */
+bd_attn_status bd_attn_fwd_timed(bd_attn_plan_t plan, const void* meta_dev,
+                                 const void* q, const void* k, const void* v,
+                                 void* o, float* lse, void* ws, bd_attn_stream_t stream,
+                                 void* const* events, int n_events);
+bd_attn_status bd_attn_bwd_timed(bd_attn_plan_t plan, const void* meta_dev,
+                                 const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse, const void* dout,
+                                 void* dq, void* dk, void* dv, void* ws, bd_attn_stream_t stream,
+                                 void* const* events, int n_events);
+
+/* Number of kernels bd_attn_fwd (backward = 0) or bd_attn_bwd (backward = 1)
+ * launches for this plan; 0 for a NULL plan. */
+int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward);
+
 /* Frees a plan (NULL is accepted). */
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan);
 
