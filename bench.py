@@ -54,6 +54,16 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (fp32 read + write), "
+                         "the reference for scaling HBM byte counters")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="summarise rocprofv3 CSV output under DIR (no GPU work) and exit")
+    ap.add_argument("--summary-out", default=None, help="with --summarize: write the text summary here")
+    ap.add_argument("--command", default="", help="with --summarize: the command that produced DIR")
+    ap.add_argument("--traffic-key", default=None,
+                    help="with --summarize: record per-launch HBM bytes of KERNEL@WORKLOAD in "
+                         "profiles/traffic.json, e.g. dkdv@3")
     return ap.parse_args()
 
 
@@ -86,6 +96,87 @@ def traffic_from_profiles(kernel, workload):
     if rec.get("src_sha256") != src_hash(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("bytes_per_launch")
+
+
+KERNEL_SYMBOLS = {"fwd": "fwd_bf16_kernel", "combine": "combine_kernel", "bwd_pre": "bwd_pre_kernel",
+                  "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
+COPY_SYMBOL = "MulFunctor"
+
+
+def _read_csvs(root, suffix):
+    import csv
+    rows = []
+    for dp, _dn, fn in os.walk(root):
+        for f in fn:
+            if f.endswith(suffix):
+                with open(os.path.join(dp, f), newline="") as fh:
+                    rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize(args):
+    """Text summary of rocprofv3 CSV output: kernel stats and, when present, the
+    per-dispatch FETCH_SIZE / WRITE_SIZE counters scaled by a plain copy kernel."""
+    import collections
+    root = args.summarize
+    lines = [f"# rocprofv3 summary of {os.path.basename(os.path.normpath(root))}", "",
+             f"command: {args.command}" if args.command else "command: (not given)", ""]
+    stats = _read_csvs(root, "kernel_stats.csv")
+    if stats:
+        lines += ["## kernel stats (rocprofv3 --kernel-trace --stats)", "",
+                  "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+        for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+            name = r["Name"]
+            short = name.split("(")[0].replace("void ", "")[:90]
+            lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                         f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f} |")
+        lines.append("")
+    pmc = _read_csvs(root, "counter_collection.csv")
+    traffic = {}
+    if pmc:
+        per = collections.defaultdict(list)     # (kernel, counter) -> values per dispatch
+        for r in pmc:
+            per[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+        copy_bytes = args.copy_probe_mb * 2**20 if args.copy_probe_mb else None
+        scale = {}
+        for (kn, cn), vals in per.items():
+            if COPY_SYMBOL in kn and copy_bytes:
+                # the largest elementwise dispatch is the copy probe (fp32 in, fp32 out)
+                scale[cn] = copy_bytes / (max(vals) * 1024.0)
+        lines += ["## HBM counters per dispatch (KiB as read; bytes after scaling)", "",
+                  f"copy probe: {args.copy_probe_mb} MiB read + written; scale factors "
+                  + ", ".join(f"{k}={v:.4f}" for k, v in sorted(scale.items())), "",
+                  "| kernel | counter | dispatches | mean KiB | scaled MB |", "|---|---|---|---|---|"]
+        for (kn, cn), vals in sorted(per.items()):
+            mean = sum(vals) / len(vals)
+            sc = scale.get(cn)
+            mb = f"{mean * 1024.0 * sc / 1e6:.2f}" if sc else "-"
+            short = kn.split("(")[0].replace("void ", "")[:90]
+            lines.append(f"| {short} | {cn} | {len(vals)} | {mean:.1f} | {mb} |")
+            for key, sym in KERNEL_SYMBOLS.items():
+                if sym in kn and sc:
+                    traffic.setdefault(key, 0.0)
+                    traffic[key] += mean * 1024.0 * sc
+        lines.append("")
+    text = "\n".join(lines)
+    if args.summary_out:
+        with open(args.summary_out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+    if args.traffic_key and traffic:
+        kern, wl = args.traffic_key.split("@")
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        try:
+            with open(path) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            rec = {}
+        rec[args.traffic_key] = {"bytes_per_launch": traffic[kern], "src_sha256": src_hash(KERNEL_SOURCES[kern]),
+                                 "command": args.command}
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+        print(f"traffic {args.traffic_key}: {traffic[kern] / 1e6:.2f} MB per launch -> {path}")
 
 
 def cpu_baseline(wl, budget_s):
@@ -132,6 +223,9 @@ def cpu_baseline(wl, budget_s):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -238,6 +332,14 @@ def main():
     roof["work_per_launch"] = work
     roof["avg_launch_ms"] = round(avg_ms[dom], 4)
     roof["traffic"] = traffic_from_profiles(dom, k)
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)        # one elementwise kernel: n*4 bytes read, n*4 written
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu:

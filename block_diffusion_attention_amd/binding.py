@@ -20,6 +20,12 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
 FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD = 1, 2, 4
 
+
+def flag_split_tiles(n: int) -> int:
+    """Plan flag: n key tiles (of 64 keys) per split on the forward split path."""
+    return (int(n) & 0xFF) << 8
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with block_diffusion_attention_amd/build.py")
 _lib = ctypes.CDLL(LIB_PATH)

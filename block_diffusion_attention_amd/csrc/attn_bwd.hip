@@ -3,8 +3,9 @@
 // Three deterministic kernels, no atomics (ORL paper, appendix D.2 paragraph
 // on the kernel: the backward pass uses the same visibility, dQ follows the
 // query traversal and dK/dV derive the valid query ranges of each key tile):
-//   bwd_pre : delta = rowsum(dO * O) per (token, query head), fp32;
-//   dkdv    : one workgroup per (key tile of up to 64 keys, kv head), looping
+//   bwd_pre : delta = rowsum(dO * O) per (token, query head), fp32, and the
+//             LSE in the log2 domain;
+//   dkdv    : one workgroup per (key tile of up to 128 keys, kv head), looping
 //             over the 64-row query chunks that can see the tile;
 //   dq      : one workgroup per (query tile, kv head), looping over the same key
 //             tiles as the forward pass.
@@ -43,7 +44,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, LPR);
-  if (row < a.rows_q && c == 0) a.delta[row] = s;
+  if (row < a.rows_q && c == 0) {
+    a.delta[row] = s;
+    a.lse2[row] = a.lse[row] * kLog2e;
+  }
 }
 
 // Geometry of query chunk c of a key tile: chunks of the clean range first,
@@ -66,7 +70,7 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const KTile& kt, const CanvasQ* 
   } else {
     const int cc = c - nc0;
     const int e = cc / cpc, sub = cc - e * cpc;
-    const int4 ev = reinterpret_cast<const int4*>(cv)[kt.cv_begin + e];
+    const int4 ev = ld_rec4(cv, kt.cv_begin + e);
     g.tok0 = ev.x + sub * qct;
     g.ntok = min(qct, ev.y - sub * qct);
     g.pos0 = -1;
@@ -76,30 +80,173 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const KTile& kt, const CanvasQ* 
 }
 
 // ---------------------------------------------------------------- dK / dV
-// Workgroup: one key tile of up to 64 keys and one kv head. Wave w owns keys
-// 32*(w&1) .. +31 and, of every 64-row query chunk, rows 32*(w>>1) .. +31; the
-// two waves that share keys add their partial dK/dV through LDS at the end.
-// Query chunks (rows = tokens x grouped heads, with their LSE and delta) go
-// from global memory straight into LDS, two chunks in flight. The transposed
-// operands dO^T and Q^T of dV^T = dO^T P and dK^T = Q^T dS are read with the
-// LDS transpose read from the natural tiles.
+// Workgroup: one key tile of up to 128 keys and one kv head. Wave w owns keys
+// 32w .. 32w+31 (K and V rows in registers, dK^T and dV^T accumulators) and
+// processes every 64-row query chunk that can see the tile, as two 32-row
+// halves. Query chunks (rows = tokens x grouped heads, with their log2-domain
+// LSE and delta) go from global memory straight into LDS, three stages deep, so
+// two chunks are in flight while one is consumed. The transposed operands dO^T
+// and Q^T of dV^T = dO^T P and dK^T = Q^T dS are read with the LDS transpose
+// read from the natural tiles.
+//
+// Per half: S = Q K^T and dP = dO V^T (16 MFMAs), then P = exp2(S*c - lse2),
+// dS = P (dP - delta) on the vector ALUs, then dV^T += dO^T P and
+// dK^T += Q^T dS (16 MFMAs). Chunks fully visible to a wave's keys take a
+// straight-line path in which the products of one half overlap the ALU work of
+// the other; boundary chunks take the predicated path.
+constexpr int kBwdStages = 3;
+
 template <int D>
-__global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(BwdArgs a) {
+struct DkdvGeom {
+  static constexpr int QC = 64;                 // query rows per chunk
+  static constexpr int TE = QC * D;             // elements of one Q or dO chunk
+  static constexpr int PW = D / 32;             // global_load_lds per wave per tile
+};
+
+// P and dS of one 32-row half from S and dP (in place), packed as MFMA B operands.
+__device__ __forceinline__ void dkdv_pointwise(f32x16& s, f32x16& dp, const float* cL, const float* cD, int r_lo,
+                                               int h, float scale_log2, bf16x8 (&pb)[2], bf16x8 (&sb)[2]) {
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int r0 = r_lo + 8 * g4 + 4 * h;
+    const f32x4 lv = *reinterpret_cast<const f32x4*>(cL + r0);
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(cD + r0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = g4 * 4 + e;
+      const float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lv[e]));
+      s[r] = p;
+      dp[r] = p * (dp[r] - dv[e]);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    float t0[8], t1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { t0[e] = s[ks * 8 + e]; t1[e] = dp[ks * 8 + e]; }
+    pb[ks] = pack8(t0);
+    sb[ks] = pack8(t1);
+  }
+}
+
+// One 64-row query chunk for the 32 keys of a wave, as a fixed program of
+// 4 * NS MFMA slots (NS = 2 * D / 16):
+//   slots [0, NS)      S = Q K^T, dP = dO V^T for rows 0..31 (alternating)
+//   slots [NS, 2NS)    the same for rows 32..63; vector work of rows 0..31
+//   slots [2NS, 3NS)   dV^T += dO^T P, dK^T += Q^T dS for rows 0..31; vector work
+//                      of rows 32..63
+//   slots [3NS, 4NS)   dV^T, dK^T for rows 32..63
+// Each slot issues one MFMA, the LDS reads of the operand kPrefetch slots ahead
+// and its share of the per-score vector work; scheduling barriers between slots
+// keep that order, so the vector ALU and the LDS run in the shadow of the MFMAs.
+// Every score takes the row-limit select (padding rows have limit -1): it is
+// cheaper than a second program and fits in the MFMA shadow.
+constexpr int kPrefetch = 4;
+
+template <int D>
+__device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
+                                           f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16* cQ,
+                                           const bf16* cG, const float* cL, const float* cD, const int* cM,
+                                           const CmLane& lo, int h, int kpos, float scale_log2) {
   constexpr int NKS = D / 16, NDB = D / 32;
-  constexpr int QC = 64;                       // query rows per chunk
-  constexpr int TE = QC * D;
+  constexpr int NS = 2 * NKS;                 // MFMA slots per phase
+  constexpr int NSLOT = 4 * NS;
+  constexpr int EPS = 16 / NS;                // score elements per slot in the vector phases
+  f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  bf16x8 pb[2][2], sb[2][2];
+  f32x4 lv[2][4], dl[2][4];
+  int4 lm[2][4];
+  bf16x8 op[NSLOT];
+
+  // operand of slot i (natural rows for S/dP, transposed for dV/dK)
+  auto fetch = [&](int i) {
+    if (i < 2 * NS) {
+      const int half = i / NS, k = i % NS;
+      return cm_row8((k & 1) ? cG : cQ, lo, 32 * half, k >> 1);
+    }
+    const int half = (i - 2 * NS) / NS, k = (i - 2 * NS) % NS;
+    const int ks = k / (2 * NDB), db = (k % (2 * NDB)) >> 1;
+    return cm_tr8((k & 1) ? cQ : cG, lo, 32 * half + 16 * ks, 32 * db);
+  };
+  auto rowterms = [&](int half) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = 32 * half + 8 * g4 + 4 * h;
+      lv[half][g4] = *reinterpret_cast<const f32x4*>(cL + r0);
+      dl[half][g4] = *reinterpret_cast<const f32x4*>(cD + r0);
+      lm[half][g4] = *reinterpret_cast<const int4*>(cM + r0);
+    }
+  };
+  // P and dS of score element e of a half
+  auto pointwise = [&](int half, int e) {
+    const int g4 = e >> 2, q = e & 3;
+    const int lim = q == 0 ? lm[half][g4].x : q == 1 ? lm[half][g4].y : q == 2 ? lm[half][g4].z : lm[half][g4].w;
+    const float x = kpos < lim ? sc[half][e] : -INFINITY;
+    const float p = fast_exp2(__builtin_fmaf(x, scale_log2, -lv[half][g4][q]));
+    sc[half][e] = p;
+    dp[half][e] = p * (dp[half][e] - dl[half][g4][q]);
+    if ((e & 7) == 7) {
+      const int ks = e >> 3;
+      float t0[8], t1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { t0[u] = sc[half][8 * ks + u]; t1[u] = dp[half][8 * ks + u]; }
+      pb[half][ks] = pack8(t0);
+      sb[half][ks] = pack8(t1);
+    }
+  };
+  auto mma = [&](int i) {
+    if (i < 2 * NS) {
+      const int half = i / NS, k = i % NS;
+      if (k & 1) dp[half] = mfma32(op[i], vf[k >> 1], dp[half]);
+      else sc[half] = mfma32(op[i], kf[k >> 1], sc[half]);
+    } else {
+      const int half = (i - 2 * NS) / NS, k = (i - 2 * NS) % NS;
+      const int ks = k / (2 * NDB), db = (k % (2 * NDB)) >> 1;
+      if (k & 1) dkt[db] = mfma32(op[i], sb[half][ks], dkt[db]);
+      else dvt[db] = mfma32(op[i], pb[half][ks], dvt[db]);
+    }
+  };
+
+  static_for<kPrefetch>([&](auto ic) { op[ic.value] = fetch(ic.value); });
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<NSLOT>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    mma(i);
+    if constexpr (i + kPrefetch < NSLOT) op[i + kPrefetch] = fetch(i + kPrefetch);
+    if constexpr (i == NS - 3) rowterms(0);
+    if constexpr (i == 2 * NS - 3) rowterms(1);
+    if constexpr (i >= NS && i < 2 * NS) {
+      static_for<EPS>([&](auto uc) { pointwise(0, (i - NS) * EPS + uc.value); });
+    }
+    if constexpr (i >= 2 * NS && i < 3 * NS) {
+      static_for<EPS>([&](auto uc) { pointwise(1, (i - 2 * NS) * EPS + uc.value); });
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) dkdv_bf16_kernel(BwdArgs a) {
+  using Gm = DkdvGeom<D>;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int QC = Gm::QC, TE = Gm::TE, PW = Gm::PW;
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[TE];
   __shared__ __attribute__((aligned(1024))) bf16 sG0[TE];
   __shared__ __attribute__((aligned(1024))) bf16 sQ1[TE];
   __shared__ __attribute__((aligned(1024))) bf16 sG1[TE];
-  __shared__ __attribute__((aligned(256))) float sL0[QC], sD0[QC], sL1[QC], sD1[QC];
-  __shared__ __attribute__((aligned(256))) int sM0[QC], sM1[QC];
+  __shared__ __attribute__((aligned(1024))) bf16 sQ2[TE];
+  __shared__ __attribute__((aligned(1024))) bf16 sG2[TE];
+  // per-stage row terms: LSE*log2(e), delta, row limit (one array per stage so the
+  // compiler can tell the stage being read from the ones being filled)
+  __shared__ __attribute__((aligned(256))) float sL0[QC], sL1[QC], sL2[QC];
+  __shared__ __attribute__((aligned(256))) float sD0[QC], sD1[QC], sD2[QC];
+  __shared__ __attribute__((aligned(256))) int sM0[QC], sM1[QC], sM2[QC];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 31, h = lane >> 5;
   const CmLane lo(lane);
-  const int kg = wave & 1, qh = wave >> 1;
-  const int4 itv = reinterpret_cast<const int4*>(a.bwd_items)[blockIdx.x];
+  const int4 itv = ld_rec4(a.bwd_items, blockIdx.x);
   if (itv.x < 0) return;
   const int kvh = itv.y;
   const KTile kt = load_ktile(a.ktiles, itv.x);
@@ -109,21 +256,22 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(BwdArgs a) {
   const bf16* __restrict__ dO = static_cast<const bf16*>(a.dout);
   const int G = a.G, B = a.B;
 
-  const int kidx = kg * 32 + j;
+  const int kidx = wave * 32 + j;
   const bool key_ok = kidx < kt.n_keys;
-  const bool wave_live = kg * 32 < kt.n_keys;
+  const bool wave_live = wave * 32 < kt.n_keys;
   const int64_t krow = (int64_t)(kt.k_tok + min(kidx, kt.n_keys - 1)) * a.hkv + kvh;
   const bool canvas_keys = kt.p0 < 0;
   const int kpos = canvas_keys ? 0 : kt.p0 + kidx;
-  const int wpos_lo = kt.p0 + kg * 32;
-  const int wpos_hi = kt.p0 + min(kg * 32 + 31, kt.n_keys - 1);
+  const int wpos_lo = kt.p0 + wave * 32;
+  const int wpos_hi = kt.p0 + min(wave * 32 + 31, kt.n_keys - 1);
 
   const int qct = QC / G;                               // tokens per chunk
   const int nc0 = (kt.cq_len + qct - 1) / qct;
   const int cpc = (B + qct - 1) / qct;
   const int nchunks = nc0 + kt.cv_count * cpc;
 
-  // async fetch of chunk c: Q and dO rows, LSE and delta per row, row limits
+  // async fetch of chunk c: Q and dO rows, log2-domain LSE and delta per row, row
+  // limits. Waves 0 and 1 issue one load more than waves 2 and 3.
   auto issue = [&](int c, bf16* dQ_, bf16* dG_, float* dL_, float* dD_, int* dM_) {
     const ChunkGeom g = chunk_geom(kt, a.canvq, c, nc0, cpc, qct);
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
@@ -139,7 +287,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(BwdArgs a) {
       const int r = min(lane, nrows - 1);
       const int t = r / G, gh = r - (r / G) * G;
       const int64_t qr = (int64_t)(g.tok0 + t) * a.hq + kvh * G + gh;
-      const float* src = wave == 0 ? a.lse + qr : a.delta + qr;
+      const float* src = wave == 0 ? a.lse2 + qr : a.delta + qr;
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(wave == 0 ? dL_ : dD_), 4, 0, 0);
     } else if (wave == 2) {
       const int r = lane, t = r / G;
@@ -155,99 +303,49 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(BwdArgs a) {
     kf[kk] = *reinterpret_cast<const bf16x8*>(K + krow * D + kk * 16 + h * 8);
     vf[kk] = *reinterpret_cast<const bf16x8*>(V + krow * D + kk * 16 + h * 8);
   }
+  // the K/V rows must be in registers before the pipelined loads start, so that no
+  // later wait for them has to drain the chunk loads in flight
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
 
   if (nchunks > 0) issue(0, sQ0, sG0, sL0, sD0, sM0);
+  if (nchunks > 1) issue(1, sQ1, sG1, sL1, sD1, sM1);
 
   auto step = [&](int c, const bf16* cQ, const bf16* cG, const float* cL, const float* cD, const int* cM,
                   bf16* nQ, bf16* nG, float* nL, float* nD, int* nM) __attribute__((always_inline)) {
-    wait_vmem();
-    __syncthreads();                                    // chunk c landed; the other stage is free
-    if (c + 1 < nchunks) issue(c + 1, nQ, nG, nL, nD, nM);
-    const ChunkGeom g = chunk_geom(kt, a.canvq, c, nc0, cpc, qct);
-    // visibility of this wave's 32 rows for its 32 keys
-    const int r_lo = qh * 32, r_hi = min(qh * 32 + 31, g.ntok * G - 1);
-    if (r_hi < r_lo || !wave_live) return;              // no valid row in this half, or no key
-    int lim_lo, lim_hi;
-    if (g.pos0 >= 0) {
-      lim_lo = ((g.pos0 + r_lo / G) / B + 1) * B;
-      lim_hi = ((g.pos0 + r_hi / G) / B + 1) * B;
+    // chunk c has landed once at most the loads of chunk c+1 are outstanding
+    if (c + 1 < nchunks) {
+      if (wave < 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PW + 1));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PW));
     } else {
-      lim_lo = lim_hi = g.lim;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    const bool half_pad = r_hi < qh * 32 + 31;
-    if (!canvas_keys && wpos_lo >= lim_hi) return;      // all of the wave's keys are invisible
-    const bool need_mask = half_pad || (!canvas_keys && wpos_hi >= lim_lo);
-
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) {
-      s = mfma32(cm_row8(cQ, lo, r_lo, kk), kf[kk], s);
-      dp = mfma32(cm_row8(cG, lo, r_lo, kk), vf[kk], dp);
+    lds_barrier();                                      // chunk c visible; stage of c-1 free
+    if (c + 2 < nchunks) issue(c + 2, nQ, nG, nL, nD, nM);
+    const ChunkGeom g = chunk_geom(kt, a.canvq, c, nc0, cpc, qct);
+    const int nrows = g.ntok * G;
+    // row limits of the two 32-row halves (clean limits grow with the row)
+    // row limits of the first and the last valid row (clean limits grow with the row)
+    int lim_first, lim_last;
+    if (g.pos0 >= 0) {
+      lim_first = (g.pos0 / B + 1) * B;
+      lim_last = ((g.pos0 + (nrows - 1) / G) / B + 1) * B;
+    } else {
+      lim_first = lim_last = g.lim;
     }
-    if (need_mask) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int4 mv = *reinterpret_cast<const int4*>(cM + r_lo + 8 * g4 + 4 * h);
-        const int lims[4] = {mv.x, mv.y, mv.z, mv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (kpos >= lims[e]) s[g4 * 4 + e] = -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int r0 = r_lo + 8 * g4 + 4 * h;
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(cL + r0);
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(cD + r0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = g4 * 4 + e;
-        const float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -lv[e] * kLog2e));
-        s[r] = p;
-        dp[r] = p * (dp[r] - dv[e]);
-      }
-    }
-    bf16x8 pb[2], sb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      float t0[8], t1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { t0[e] = s[ks * 8 + e]; t1[e] = dp[ks * 8 + e]; }
-      pb[ks] = pack8(t0);
-      sb[ks] = pack8(t1);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dvt[db] = mfma32(cm_tr8(cG, lo, r_lo + ks * 16, db * 32), pb[ks], dvt[db]);
-        dkt[db] = mfma32(cm_tr8(cQ, lo, r_lo + ks * 16, db * 32), sb[ks], dkt[db]);
-      }
+    // skip when no valid row sees any of the wave's keys
+    if (!wave_live || (!canvas_keys && wpos_lo >= lim_last)) return;
+    dkdv_chunk<D>(kf, vf, dkt, dvt, cQ, cG, cL, cD, cM, lo, h, kpos, a.scale_log2);
   };
-  for (int c = 0; c < nchunks; c += 2) {
-    step(c, sQ0, sG0, sL0, sD0, sM0, sQ1, sG1, sL1, sD1, sM1);
+  for (int c = 0; c < nchunks; c += kBwdStages) {
+    step(c, sQ0, sG0, sL0, sD0, sM0, sQ2, sG2, sL2, sD2, sM2);
     if (c + 1 < nchunks) step(c + 1, sQ1, sG1, sL1, sD1, sM1, sQ0, sG0, sL0, sD0, sM0);
+    if (c + 2 < nchunks) step(c + 2, sQ2, sG2, sL2, sD2, sM2, sQ1, sG1, sL1, sD1, sM1);
   }
 
-  // add the partial sums of the two query halves: waves 2, 3 hand theirs to 0, 1
-  wait_vmem();
-  __syncthreads();
-  float* redk = reinterpret_cast<float*>(kg == 0 ? sQ0 : sQ1);   // NDB*16*64 floats = one tile
-  float* redv = reinterpret_cast<float*>(kg == 0 ? sG0 : sG1);
-  if (qh == 1) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        redk[(db * 16 + r) * 64 + lane] = dkt[db][r];
-        redv[(db * 16 + r) * 64 + lane] = dvt[db][r];
-      }
-  }
-  __syncthreads();
-  if (qh == 0 && key_ok) {
+  if (key_ok) {
     bf16* dkp = static_cast<bf16*>(a.dk) + krow * D;
     bf16* dvp = static_cast<bf16*>(a.dv) + krow * D;
 #pragma unroll
@@ -257,9 +355,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(BwdArgs a) {
         float kx[4], vx[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = g4 * 4 + e;
-          kx[e] = (dkt[db][r] + redk[(db * 16 + r) * 64 + lane]) * a.scale;
-          vx[e] = dvt[db][r] + redv[(db * 16 + r) * 64 + lane];
+          kx[e] = dkt[db][g4 * 4 + e] * a.scale;
+          vx[e] = dvt[db][g4 * 4 + e];
         }
         const int d0 = db * 32 + g4 * 8 + h * 4;
         *reinterpret_cast<u32x2*>(dkp + d0) = u32x2{pack_bf16x2(kx[0], kx[1]), pack_bf16x2(kx[2], kx[3])};

@@ -188,41 +188,46 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
 }
 
 // Merges the split partial results of one query tile: lse = log sum_i exp(lse_i),
-// O = sum_i exp(lse_i - lse) O_i.
+// O = sum_i exp(lse_i - lse) O_i. Workgroup: kCombRows rows of one merge item,
+// one thread per (row, 4 columns); blockIdx.x = item * (kQRows / rows) + group.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
-  const int4 it = reinterpret_cast<const int4*>(a.items)[blockIdx.x];
+  constexpr int C4 = D / 4;
+  constexpr int RPW = 256 / C4;                    // rows per workgroup
+  constexpr int GROUPS = kQRows / RPW;
+  const int item = blockIdx.x / GROUPS;
+  const int row = (blockIdx.x - item * GROUPS) * RPW + threadIdx.x / C4;
+  const int c = threadIdx.x % C4;
+  const int4 it = reinterpret_cast<const int4*>(a.items)[item];
   const QTile qt = load_qtile(a.qtiles, it.x);
   const int kvh = it.y, first = it.z, count = it.w;
-  const int rows = qt.n_tok * a.G;
-  constexpr int C4 = D / 4;
-  for (int u = threadIdx.x; u < rows * C4; u += blockDim.x) {
-    const int row = u / C4, c = u - row * C4;
-    float mx = -INFINITY;
-    for (int i = 0; i < count; ++i) mx = fmaxf(mx, a.part_lse[(int64_t)(first + i) * kQRows + row]);
-    float wsum = 0.f;
-    f32x4 accv = f32x4{};
-    if (mx != -INFINITY) {
-      for (int i = 0; i < count; ++i) {
-        const float w = __expf(a.part_lse[(int64_t)(first + i) * kQRows + row] - mx);
-        wsum += w;
-        const f32x4 po = *reinterpret_cast<const f32x4*>(a.part_o + ((int64_t)(first + i) * kQRows + row) * D + c * 4);
-        accv += w * po;
-      }
+  if (row >= qt.n_tok * a.G) return;
+  const float* pl = a.part_lse + (int64_t)first * kQRows + row;
+  float mx = -INFINITY;
+  for (int i = 0; i < count; ++i) mx = fmaxf(mx, pl[(int64_t)i * kQRows]);
+  float wsum = 0.f;
+  f32x4 accv = f32x4{};
+  if (mx != -INFINITY) {
+    const float* po = a.part_o + ((int64_t)first * kQRows + row) * D + c * 4;
+#pragma unroll 4
+    for (int i = 0; i < count; ++i) {
+      const float w = __expf(pl[(int64_t)i * kQRows] - mx);
+      wsum += w;
+      accv += w * *reinterpret_cast<const f32x4*>(po + (int64_t)i * kQRows * D);
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const int t = row / a.G, gh = row - t * a.G;
-    const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * a.G + gh;
-    if (BF16) {
-      u32x2 v;
-      v[0] = pack_bf16x2(accv[0] * inv, accv[1] * inv);
-      v[1] = pack_bf16x2(accv[2] * inv, accv[3] * inv);
-      *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.o) + qrow * D + c * 4) = v;
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + qrow * D + c * 4) = accv * inv;
-    }
-    if (c == 0) a.lse[qrow] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int t = row / a.G, gh = row - t * a.G;
+  const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * a.G + gh;
+  if (BF16) {
+    u32x2 v;
+    v[0] = pack_bf16x2(accv[0] * inv, accv[1] * inv);
+    v[1] = pack_bf16x2(accv[2] * inv, accv[3] * inv);
+    *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.o) + qrow * D + c * 4) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + qrow * D + c * 4) = accv * inv;
+  }
+  if (c == 0) a.lse[qrow] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
 }
 
 }  // namespace
@@ -234,14 +239,16 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int items, hipStream_t s) {
+  if (items <= 0) return hipSuccess;
+  const int groups = kQRows / (256 / (head_dim / 4));
+  const dim3 grid((unsigned)(items * groups));
   if (head_dim == 128) {
-    if (bf16_out) hipLaunchKernelGGL((combine_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+    if (bf16_out) hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(256), 0, s, a);
   } else {
-    if (bf16_out) hipLaunchKernelGGL((combine_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+    if (bf16_out) hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

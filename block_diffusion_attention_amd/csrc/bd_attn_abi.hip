@@ -201,6 +201,7 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.bwd_items = section<bdattn::BwdItem>(meta_dev, p.off_bwd);
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = static_cast<float*>(ws);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_lse2);
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.rows_q = p.tq * p.desc.num_q_heads;
   a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.B = p.desc.block_size;

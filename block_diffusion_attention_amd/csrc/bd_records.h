@@ -21,8 +21,8 @@ namespace bdattn {
 constexpr int kQRows = 128;
 // Forward / dQ key tile (keys per main-loop step).
 constexpr int kKTile = 64;
-// dK/dV: keys per workgroup (2 groups of 32 keys x 2 halves of each query chunk).
-constexpr int kKBlock = 64;
+// dK/dV: keys per workgroup (4 waves of 32 keys each).
+constexpr int kKBlock = 128;
 // Largest supported group size (query heads per kv head).
 constexpr int kMaxGroup = 32;
 

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "bd_records.h"
 
 namespace bdattn {
@@ -16,6 +19,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1, fully
+// expanded, so register arrays are only ever indexed with constants.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -176,6 +190,26 @@ __device__ __forceinline__ void tile_fetch(bf16* tile, RowAddr row_ptr, int nval
 // Waits for this wave's outstanding global loads (including those into LDS).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of this
+// wave are outstanding and leaves the LDS/scalar and export counters unconstrained
+// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// ... and the one that waits for this wave's LDS operations only.
+constexpr int kLgkm0Imm = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// Workgroup barrier that orders LDS accesses only. Unlike __syncthreads() it does
+// not wait for this wave's outstanding global loads (a memory fence would, since
+// loads that write LDS asynchronously count as pending LDS writes), so loads
+// issued for later pipeline stages stay in flight; the caller first waits (vmcnt)
+// for the loads of the stage it is about to read. The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Value of x from lane l ^ 32 combined with the own one: returns (own, other).
 __device__ __forceinline__ float swap_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
@@ -189,9 +223,20 @@ __device__ __forceinline__ int row_limit(const QTile& qt, int t, int B) {
   return qt.pos0 >= 0 ? ((qt.pos0 + t) / B + 1) * B : qt.lim_min;
 }
 
+// Work-list records are read through the constant address space with a
+// wave-uniform index, so they come in with scalar loads (counted by lgkmcnt, not
+// by vmcnt: waiting for them never waits for the global loads in flight).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const i32x4 ci32x4;
+
+__device__ __forceinline__ int4 ld_rec4(const void* base, int i) {
+  const int u = __builtin_amdgcn_readfirstlane(i);
+  const i32x4 v = reinterpret_cast<ci32x4*>(reinterpret_cast<uintptr_t>(base))[u];
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ QTile load_qtile(const int32_t* base, int i) {
-  const int4* p = reinterpret_cast<const int4*>(base) + 2 * i;
-  int4 a = p[0], b = p[1];
+  int4 a = ld_rec4(base, 2 * i), b = ld_rec4(base, 2 * i + 1);
   QTile q;
   q.q_tok = a.x; q.n_tok = a.y; q.k_ctx = a.z; q.pos0 = a.w;
   q.lim_max = b.x; q.lim_min = b.y; q.k_own = b.z; q.n_own = b.w;
@@ -199,8 +244,7 @@ __device__ __forceinline__ QTile load_qtile(const int32_t* base, int i) {
 }
 
 __device__ __forceinline__ KTile load_ktile(const int32_t* base, int i) {
-  const int4* p = reinterpret_cast<const int4*>(base) + 2 * i;
-  int4 a = p[0], b = p[1];
+  int4 a = ld_rec4(base, 2 * i), b = ld_rec4(base, 2 * i + 1);
   KTile k;
   k.k_tok = a.x; k.n_keys = a.y; k.p0 = a.z; k.cq_tok = a.w;
   k.cq_len = b.x; k.cq_pos = b.y; k.cv_begin = b.z; k.cv_count = b.w;

@@ -46,6 +46,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   float* delta;              // [Tq, Hq] fp32 (workspace)
+  float* lse2;               // [Tq, Hq] fp32 (workspace): LSE * log2(e), written by bwd_pre
   void* dq;
   void* dk;
   void* dv;
@@ -56,7 +57,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
-hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int grid, hipStream_t s);
+hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int items, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);

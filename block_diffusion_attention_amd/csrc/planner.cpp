@@ -205,11 +205,14 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   int64_t tps = 0;   // key tiles per split
   if (!(d->flags & BD_ATTN_FLAG_NO_SPLIT)) {
     const int64_t target = 2 * 256;   // two workgroups per compute unit
+    const int64_t want = (d->flags >> 8) & 0xff;     // caller's key tiles per split
     if (d->flags & BD_ATTN_FLAG_FORCE_SPLIT) {
-      split = max_tiles > 1;
-      tps = std::max<int64_t>(1, (max_tiles + 1) / 2);
+      tps = want > 0 ? want : std::max<int64_t>(1, (max_tiles + 1) / 2);
+      split = tps < max_tiles;
     } else if (direct_items < target && max_tiles >= 4) {
-      tps = std::max<int64_t>(1, ceil_div(total_tiles * Hkv, target));
+      // at least 4 key tiles per split: fewer partial results to write and merge
+      // (measured best on the single-request denoising shape)
+      tps = want > 0 ? want : std::max<int64_t>(4, ceil_div(total_tiles * Hkv, target));
       split = tps < max_tiles;
     }
   }
@@ -377,7 +380,8 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
     p.off_ws_lse = nsplit * kQRows * D * 4;        // partial O (fp32), then partial LSE
     p.ws_fwd = (size_t)(p.off_ws_lse + nsplit * kQRows * 4);
   }
-  p.ws_bwd = (size_t)(ceil_div(tq * Hq * 4, 256) * 256);   // delta [Tq, Hq] fp32
+  p.off_ws_lse2 = ceil_div(tq * Hq * 4, 256) * 256;          // delta [Tq, Hq] fp32, then LSE*log2(e)
+  p.ws_bwd = (size_t)(2 * p.off_ws_lse2);
   return BD_ATTN_OK;
 }
 

@@ -33,6 +33,7 @@ struct Plan {
           off_ktiles = 0, off_canvq = 0, off_bwd = 0;   // int32 offsets into blob
   size_t ws_fwd = 0, ws_bwd = 0;
   int64_t off_ws_lse = 0;            // byte offset of the partial LSE in the forward workspace
+  int64_t off_ws_lse2 = 0;           // byte offset of LSE*log2(e) in the backward workspace
 };
 
 // Validates desc and fills *plan. On error returns a non-OK status and sets *err.

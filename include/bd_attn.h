@@ -71,6 +71,9 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
 #define BD_ATTN_FLAG_NO_SPLIT   1u  /* never split a query tile's key range (forward) */
 #define BD_ATTN_FLAG_FORCE_SPLIT 2u /* always split long key ranges (forward; for tests) */
 #define BD_ATTN_FLAG_NO_XCD     4u  /* plain largest-cost-first order, no XCD grouping */
+/* Bits 8..15: key tiles (of 64 keys) per split of the forward split path;
+ * 0 selects the library's choice. Ignored unless the plan splits. */
+#define BD_ATTN_FLAG_SPLIT_TILES(n) ((((uint32_t)(n)) & 0xffu) << 8)
 
 typedef struct bd_attn_plan_s* bd_attn_plan_t;
 
@@ -129,7 +132,8 @@ bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev,
  * Writes (does not accumulate) dq [Tq,Hq,D], dk and dv [Tk,Hkv,D]; dK and dV
  * are summed over the query heads of each kv head. Deterministic: no atomics,
  * bitwise identical across runs. ws: ws_bwd_bytes of device memory (holds the
- * float32 row terms delta = rowsum(dO * O), [Tq, Hq]). Errors as bd_attn_fwd. */
+ * float32 row terms delta = rowsum(dO * O) and LSE * log2(e), [Tq, Hq] each).
+ * Errors as bd_attn_fwd. */
 bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev,
                            const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout,

@@ -175,7 +175,16 @@ def test_named_workload_plans(k):
     rec = decode(p.host_blob())
     if k == 2:
         assert len(rec["comb"]) == 8, "the denoising-step shape is split along its key range"
-        assert len([o for o in rec["fwd_order"] if o >= 0]) >= 256
+        # 2048 context keys + 32 own keys = 33 key tiles of 64 per kv head, 4 tiles per split
+        launched = sorted(o for o in rec["fwd_order"] if o >= 0)
+        assert launched == list(range(len(rec["fwd"])))
+        assert len(rec["fwd"]) == 8 * 9
+        for qtile, kvh, first, count in rec["comb"]:
+            spans = [tuple(rec["fwd"][first + i][2:4]) for i in range(count)]
+            assert spans[0][0] == 0 and spans[-1][1] == 33
+            assert all(a[1] == b_[0] for a, b_ in zip(spans, spans[1:]))
+            assert all(rec["fwd"][first + i][0] == qtile and rec["fwd"][first + i][1] == kvh
+                       for i in range(count))
 
 
 def test_plan_is_deterministic():
