@@ -139,8 +139,8 @@ __device__ __forceinline__ void dkdv_pointwise(f32x16& s, f32x16& dp, const floa
 // Each slot issues one MFMA, the LDS reads of the operand kPrefetch slots ahead
 // and its share of the per-score vector work; scheduling barriers between slots
 // keep that order, so the vector ALU and the LDS run in the shadow of the MFMAs.
-// Every score takes the row-limit select (padding rows have limit -1): it is
-// cheaper than a second program and fits in the MFMA shadow.
+// Every score takes the row-limit select (padding rows have limit -1): one
+// program for all chunks keeps the accumulators in place across chunks.
 constexpr int kPrefetch = 4;
 
 template <int D>
@@ -306,6 +306,10 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // the K/V rows must be in registers before the pipelined loads start, so that no
   // later wait for them has to drain the chunk loads in flight
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // K/V fragments live in accumulation registers (MFMA reads its A/B operands from
+  // either file), leaving the vector registers to the scores the ALU works on
+#pragma unroll
+  for (int kk = 0; kk < NKS; ++kk) asm volatile("" : "+a"(kf[kk]), "+a"(vf[kk]));
   f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
