@@ -57,8 +57,8 @@ def parse():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (fp32 read + write), "
                          "the reference for scaling HBM byte counters")
-    ap.add_argument("--summarize", metavar="DIR", default=None,
-                    help="summarise rocprofv3 CSV output under DIR (no GPU work) and exit")
+    ap.add_argument("--summarize", metavar="DIR", nargs="+", default=None,
+                    help="summarise rocprofv3 CSV output under the DIRs (no GPU work) and exit")
     ap.add_argument("--summary-out", default=None, help="with --summarize: write the text summary here")
     ap.add_argument("--command", default="", help="with --summarize: the command that produced DIR")
     ap.add_argument("--traffic-key", default=None,
@@ -103,36 +103,49 @@ KERNEL_SYMBOLS = {"fwd": "fwd_bf16_kernel", "combine": "combine_kernel", "bwd_pr
 COPY_SYMBOL = "MulFunctor"
 
 
-def _read_csvs(root, suffix):
+def _read_csvs(roots, suffix):
     import csv
     rows = []
-    for dp, _dn, fn in os.walk(root):
-        for f in fn:
-            if f.endswith(suffix):
-                with open(os.path.join(dp, f), newline="") as fh:
-                    rows.extend(csv.DictReader(fh))
+    for root in roots:
+        for dp, _dn, fn in os.walk(root):
+            for f in fn:
+                if f.endswith(suffix):
+                    with open(os.path.join(dp, f), newline="") as fh:
+                        rows.extend(csv.DictReader(fh))
     return rows
+
+
+def _short(name):
+    """Kernel name without namespaces, return type and argument list."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    depth, out = 0, []
+    for ch in name:          # drop the argument list (the first top-level parenthesis)
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out)[:90]
 
 
 def summarize(args):
     """Text summary of rocprofv3 CSV output: kernel stats and, when present, the
     per-dispatch FETCH_SIZE / WRITE_SIZE counters scaled by a plain copy kernel."""
     import collections
-    root = args.summarize
-    lines = [f"# rocprofv3 summary of {os.path.basename(os.path.normpath(root))}", "",
+    roots = args.summarize
+    lines = ["# rocprofv3 summary of " + ", ".join(os.path.basename(os.path.normpath(r)) for r in roots), "",
              f"command: {args.command}" if args.command else "command: (not given)", ""]
-    stats = _read_csvs(root, "kernel_stats.csv")
+    stats = _read_csvs(roots, "kernel_stats.csv")
     if stats:
         lines += ["## kernel stats (rocprofv3 --kernel-trace --stats)", "",
                   "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
         for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
-            name = r["Name"]
-            short = name.split("(")[0].replace("void ", "")[:90]
+            short = _short(r["Name"])
             lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
                          f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | "
                          f"{float(r['Percentage']):.1f} |")
         lines.append("")
-    pmc = _read_csvs(root, "counter_collection.csv")
+    pmc = _read_csvs(roots, "counter_collection.csv")
     traffic = {}
     if pmc:
         per = collections.defaultdict(list)     # (kernel, counter) -> values per dispatch
@@ -152,7 +165,7 @@ def summarize(args):
             mean = sum(vals) / len(vals)
             sc = scale.get(cn)
             mb = f"{mean * 1024.0 * sc / 1e6:.2f}" if sc else "-"
-            short = kn.split("(")[0].replace("void ", "")[:90]
+            short = _short(kn)
             lines.append(f"| {short} | {cn} | {len(vals)} | {mean:.1f} | {mb} |")
             for key, sym in KERNEL_SYMBOLS.items():
                 if sym in kn and sc:
