@@ -270,10 +270,13 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int cpc = (B + qct - 1) / qct;
   const int nchunks = nc0 + kt.cv_count * cpc;
 
+  // Chunks are visited from the last one back: every key tile of a segment ends
+  // its query range at the same place, so tiles running at the same time start on
+  // the same chunks and share them in L2.
   // async fetch of chunk c: Q and dO rows, log2-domain LSE and delta per row, row
   // limits. Waves 0 and 1 issue one load more than waves 2 and 3.
   auto issue = [&](int c, bf16* dQ_, bf16* dG_, float* dL_, float* dD_, int* dM_) {
-    const ChunkGeom g = chunk_geom(kt, a.canvq, c, nc0, cpc, qct);
+    const ChunkGeom g = chunk_geom(kt, a.canvq, nchunks - 1 - c, nc0, cpc, qct);
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
     auto rowp = [&](const bf16* base) {
       return [=](int r) {
@@ -328,7 +331,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
     lds_barrier();                                      // chunk c visible; stage of c-1 free
     if (c + 2 < nchunks) issue(c + 2, nQ, nG, nL, nD, nM);
-    const ChunkGeom g = chunk_geom(kt, a.canvq, c, nc0, cpc, qct);
+    const ChunkGeom g = chunk_geom(kt, a.canvq, nchunks - 1 - c, nc0, cpc, qct);
     const int nrows = g.ntok * G;
     // row limits of the two 32-row halves (clean limits grow with the row)
     // row limits of the first and the last valid row (clean limits grow with the row)
