@@ -76,7 +76,8 @@ def src_hash(files):
 
 
 KERNEL_SOURCES = {
-    "fwd": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "fwd": ["attn_fwd.hip", "attn_fwd_vt.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "transpose_v": ["attn_fwd_vt.hip", "kcommon.h", "kernels.h"],
     "dkdv": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "dq": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "bwd_pre": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
@@ -98,8 +99,8 @@ def traffic_from_profiles(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-KERNEL_SYMBOLS = {"fwd": "fwd_bf16_kernel", "combine": "combine_kernel", "bwd_pre": "bwd_pre_kernel",
-                  "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"}
+KERNEL_SYMBOLS = {"fwd": "fwd_", "combine": "combine_kernel", "bwd_pre": "bwd_pre_kernel",
+                  "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel", "transpose_v": "transpose_v_kernel"}
 COPY_SYMBOL = "MulFunctor"
 
 
@@ -273,8 +274,8 @@ def main():
     dq, dk, dv = (torch.empty_like(q), torch.empty_like(kk), torch.empty_like(v)) if backward else (None,) * 3
 
     nf = plan.kernels(False)
-    fwd_names = ["fwd"] if nf == 1 else ["fwd", "combine"]
-    bwd_names = ["bwd_pre", "dkdv", "dq"]
+    fwd_names = plan.kernel_names(False)
+    bwd_names = plan.kernel_names(True)
 
     def step(evf=None, evb=None):
         b.fwd(plan, q, kk, v, o, lse, events=evf)
@@ -287,7 +288,8 @@ def main():
 
     K = args.steps
     evf = [[torch.cuda.Event(enable_timing=True) for _ in range(nf + 1)] for _ in range(K)]
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)] if backward else [None] * K
+    evb = ([[torch.cuda.Event(enable_timing=True) for _ in range(len(bwd_names) + 1)] for _ in range(K)]
+           if backward else [None] * K)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for e in [x for row in evf for x in row] + [x for row in evb if row for x in row]:
         e.record()          # creates the HIP events before the timed region
@@ -325,8 +327,9 @@ def main():
         "fwd": ("mfma", 4.0 * D * Hq * pairs),
         "dkdv": ("mfma", 8.0 * D * Hq * pairs),
         "dq": ("mfma", 6.0 * D * Hq * pairs),
-        "bwd_pre": ("hbm", 2.0 * q_bytes + plan.tq * Hq * 4),
+        "bwd_pre": ("hbm", 2.0 * q_bytes + 3.0 * plan.tq * Hq * 4),
         "combine": ("hbm", q_bytes + plan.tq * Hq * 4),
+        "transpose_v": ("hbm", 2.0 * kv_bytes),
     }
     if k == 2:   # the denoising step is bandwidth-bound: its forward is priced in bytes
         algo["fwd"] = ("hbm", float(q_bytes + 2 * kv_bytes))

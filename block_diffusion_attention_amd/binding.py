@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libbdattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
-FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD = 1, 2, 4
+FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD, FLAG_FWD_DIRECT = 1, 2, 4, 8
 
 
 def flag_split_tiles(n: int) -> int:
@@ -64,6 +64,8 @@ _lib.bd_attn_fwd_timed.argtypes = [_vp] * 10 + [ctypes.c_int]
 _lib.bd_attn_bwd_timed.argtypes = [_vp] * 14 + [ctypes.c_int]
 _lib.bd_attn_plan_kernels.argtypes = [_vp, ctypes.c_int32]
 _lib.bd_attn_plan_kernels.restype = ctypes.c_int32
+_lib.bd_attn_plan_kernel_name.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32]
+_lib.bd_attn_plan_kernel_name.restype = ctypes.c_char_p
 _lib.bd_attn_plan_destroy.argtypes = [_vp]
 _lib.bd_attn_last_error.restype = ctypes.c_char_p
 _lib.bd_attn_version.restype = ctypes.c_char_p
@@ -73,7 +75,7 @@ for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_a
 
 EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
             "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
-            "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version")
+            "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version")
 
 
 class BdAttnError(RuntimeError):
@@ -134,6 +136,10 @@ class Plan:
 
     def kernels(self, backward: bool) -> int:
         return int(_lib.bd_attn_plan_kernels(self.handle, 1 if backward else 0))
+
+    def kernel_names(self, backward: bool):
+        bw = 1 if backward else 0
+        return [_lib.bd_attn_plan_kernel_name(self.handle, bw, i).decode() for i in range(self.kernels(backward))]
 
     def host_blob(self):
         buf = (ctypes.c_int32 * (self.meta_bytes // 4))()

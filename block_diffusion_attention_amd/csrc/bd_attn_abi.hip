@@ -45,7 +45,22 @@ struct EventMarks {
   }
 };
 
-int fwd_kernels(const Plan& p) { return (p.desc.dtype == BD_ATTN_BF16 && p.split) ? 2 : 1; }
+// Kernels launched by bd_attn_fwd / bd_attn_bwd, in order.
+int fwd_kernels(const Plan& p) {
+  const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
+  return 1 + (bf16 && p.use_vt ? 1 : 0) + (bf16 && p.split ? 1 : 0);
+}
+const char* kernel_name(const Plan& p, bool backward, int i) {
+  static const char* const bwd[] = {"bwd_pre", "dkdv", "dq"};
+  if (backward) return (i >= 0 && i < 3) ? bwd[i] : nullptr;
+  if (i < 0 || i >= fwd_kernels(p)) return nullptr;
+  const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
+  if (bf16 && p.use_vt) {
+    if (i == 0) return "transpose_v";
+    --i;
+  }
+  return i == 0 ? "fwd" : "combine";
+}
 
 template <class T>
 const T* section(const void* meta, int64_t off) {
@@ -119,7 +134,7 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
     return st;
   const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
   const bool split = bf16 && p.split;
-  if (split) {
+  if (p.ws_fwd > 0) {
     if (!ws) return fail(BD_ATTN_EWORKSPACE, "this plan needs a forward workspace (ws_fwd_bytes)");
     if (!aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
   }
@@ -141,17 +156,29 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
     return hip_status(ev.mark(1), "hipEventRecord");
   }
   a.items = section<bdattn::FwdItem>(meta_dev, p.off_fwd);
+  int mark = 1;
+  if (p.use_vt) {
+    void* vt = static_cast<char*>(ws) + p.off_ws_vt;
+    e = bdattn::launch_transpose_v(v, vt, (int)p.tk, (int)p.tk_pad, a.hkv, D, s);
+    if ((st = hip_status(e, "transpose_v launch"))) return st;
+    if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
+    a.vt = vt;
+    a.tk_pad = (int)p.tk_pad;
+  }
+  auto launch = [&](int grid) {
+    return p.use_vt ? bdattn::launch_fwd_vt(a, D, grid, s) : bdattn::launch_fwd_bf16(a, D, grid, s);
+  };
   if (!split) {
-    e = bdattn::launch_fwd_bf16(a, D, (int)p.fwd_items.size(), s);
+    e = launch((int)p.fwd_items.size());
     if ((st = hip_status(e, "fwd launch"))) return st;
-    return hip_status(ev.mark(1), "hipEventRecord");
+    return hip_status(ev.mark(mark), "hipEventRecord");
   }
   a.order = section<int32_t>(meta_dev, p.off_fwd_order);
-  a.part_o = static_cast<float*>(ws);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_part);
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_lse);
-  e = bdattn::launch_fwd_bf16(a, D, (int)p.fwd_order.size(), s);
+  e = launch((int)p.fwd_order.size());
   if ((st = hip_status(e, "fwd (split) launch"))) return st;
-  if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
+  if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
   bdattn::CombArgs c{};
   c.qtiles = a.qtiles;
   c.items = section<bdattn::CombItem>(meta_dev, p.off_comb);
@@ -159,7 +186,7 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   c.hq = a.hq; c.G = a.G;
   e = bdattn::launch_combine(c, D, true, (int)p.comb_items.size(), s);
   if ((st = hip_status(e, "combine launch"))) return st;
-  return hip_status(ev.mark(2), "hipEventRecord");
+  return hip_status(ev.mark(mark), "hipEventRecord");
 }
 
 bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
@@ -238,6 +265,11 @@ bd_attn_status bd_attn_bwd_timed(bd_attn_plan_t plan, const void* meta_dev, cons
 int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward) {
   if (!plan) return 0;
   return backward ? 3 : fwd_kernels(plan->p);
+}
+
+const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int32_t i) {
+  if (!plan) return nullptr;
+  return kernel_name(plan->p, backward != 0, i);
 }
 
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan) {

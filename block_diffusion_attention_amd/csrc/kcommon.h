@@ -187,6 +187,55 @@ __device__ __forceinline__ void tile_fetch(bf16* tile, RowAddr row_ptr, int nval
   }
 }
 
+// ---------------------------------------------------------------------------
+// Padded row-major tiles. A tile of ROWS rows x CH 16-byte chunks keeps each row
+// in CH + 1 slots: chunk (r, c) sits in slot r * (CH + 1) + c (the last slot of a
+// row is padding). One global_load_lds instruction (lane l writes slot 64 m + l)
+// covers whole rows apart from the two ends, i.e. a few cache lines, and MFMA
+// operand reads of 16 consecutive rows at one chunk land in 16 distinct 16-byte
+// bank groups of the 64-bank LDS (the row stride is odd in 16-byte units), with
+// addresses affine in the chunk index (one base register per lane).
+template <int ROWS, int CH>
+struct PadTile {
+  static constexpr int kStride = CH + 1;                      // slots per row
+  static constexpr int kSlots = ROWS * kStride;
+  static constexpr int kInstr = kSlots / 64;                  // DMA instructions per tile
+  static_assert(kSlots % 64 == 0, "tile must be whole DMA instructions");
+  static constexpr int kElems = kSlots * 8;                   // bf16 elements of LDS
+};
+
+// Issues the async copy of one padded tile, instructions m = wave, wave + 4, ...
+// Row r is read from base + min(r, nvalid - 1) * row_stride (elements; the offset
+// of the last row fits in 31 bits) and padding slots read chunk 0 of their row,
+// so every address is inside the tensor.
+template <int ROWS, int CH>
+__device__ __forceinline__ void pad_tile_fetch(bf16* tile, const bf16* base, int row_stride, int nvalid, int wave,
+                                               int lane) {
+  using T = PadTile<ROWS, CH>;
+#pragma unroll
+  for (int m0 = 0; m0 < T::kInstr; m0 += 4) {
+    const int m = m0 + wave;
+    if (m < T::kInstr) {
+      const int s = m * 64 + lane;
+      const int r = s / T::kStride, c = s - r * T::kStride;
+      const uint32_t boff = 2u * (uint32_t)(min(r, nvalid - 1) * row_stride + (c < CH ? c : 0) * 8);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(base) + boff,
+                                       (lds_void*)(tile + m * 64 * 8), 16, 0, 0);
+    }
+  }
+}
+
+// Natural MFMA operand from a padded tile: row rbase + lane%32, chunk
+// 2kk + lane/32; base = 16 * ((lane%32) * (CH + 1) + lane/32).
+template <int CH>
+__device__ __forceinline__ int pad_base(int lane) { return 16 * ((lane & 31) * (CH + 1) + (lane >> 5)); }
+
+template <int CH>
+__device__ __forceinline__ bf16x8 pad_row8(const bf16* tile, int base, int rbase, int kk) {
+  const char* p = reinterpret_cast<const char*>(tile) + base + 16 * (rbase * (CH + 1) + 2 * kk);
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
 // Waits for this wave's outstanding global loads (including those into LDS).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -18,6 +18,8 @@ struct FwdArgs {
   float* lse;
   float* part_o;             // split mode: partial O [slot][kQRows][D] fp32, else NULL
   float* part_lse;           // split mode: partial LSE [slot][kQRows]
+  const void* vt;            // V transposed, [Hkv][D][tk_pad] (pipelined kernel)
+  int tk_pad;
   int hq, hkv, G, B;
   float scale_log2;          // softmax scale * log2(e)
   float scale;               // softmax scale
@@ -61,6 +63,9 @@ hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int it
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
+
+hipError_t launch_transpose_v(const void* v, void* vt, int tk, int tk_pad, int hkv, int head_dim, hipStream_t s);
+hipError_t launch_fwd_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_dkdv_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s);

@@ -374,12 +374,19 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
 
   const int64_t D = d->head_dim;
   const int64_t Hq = d->num_q_heads;
-  p.ws_fwd = 0;
+  // forward workspace: [V transposed (pipelined path)] [partial O fp32] [partial LSE]
+  p.use_vt = !(d->flags & BD_ATTN_FLAG_FWD_DIRECT) && d->dtype == BD_ATTN_BF16 && B % 8 == 0;
+  p.tk_pad = ceil_div(tk, 64) * 64 + 64;
+  int64_t off = 0;
+  p.off_ws_vt = 0;
+  if (p.use_vt) off = ceil_div((int64_t)Hkv * D * p.tk_pad * 2, 256) * 256;
+  p.off_ws_part = off;
   if (split) {
     const int64_t nsplit = (int64_t)p.fwd_items.size();
-    p.off_ws_lse = nsplit * kQRows * D * 4;        // partial O (fp32), then partial LSE
-    p.ws_fwd = (size_t)(p.off_ws_lse + nsplit * kQRows * 4);
+    p.off_ws_lse = off + nsplit * kQRows * D * 4;
+    off = p.off_ws_lse + nsplit * kQRows * 4;
   }
+  p.ws_fwd = (size_t)off;
   p.off_ws_lse2 = ceil_div(tq * Hq * 4, 256) * 256;          // delta [Tq, Hq] fp32, then LSE*log2(e)
   p.ws_bwd = (size_t)(2 * p.off_ws_lse2);
   return BD_ATTN_OK;

@@ -71,6 +71,8 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
 #define BD_ATTN_FLAG_NO_SPLIT   1u  /* never split a query tile's key range (forward) */
 #define BD_ATTN_FLAG_FORCE_SPLIT 2u /* always split long key ranges (forward; for tests) */
 #define BD_ATTN_FLAG_NO_XCD     4u  /* plain largest-cost-first order, no XCD grouping */
+#define BD_ATTN_FLAG_FWD_DIRECT 8u /* bf16 forward without the transposed V copy (the
+                                       default uses it when the block size is a multiple of 8) */
 /* Bits 8..15: key tiles (of 64 keys) per split of the forward split path;
  * 0 selects the library's choice. Ignored unless the plan splits. */
 #define BD_ATTN_FLAG_SPLIT_TILES(n) ((((uint32_t)(n)) & 0xffu) << 8)
@@ -121,7 +123,9 @@ bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_
 
 /* Forward. q [Tq,Hq,D], k/v [Tk,Hkv,D] in desc.dtype; writes o [Tq,Hq,D] and
  * lse [Tq,Hq] (float32). ws: ws_fwd_bytes of device memory (may be NULL when
- * that size is 0). All pointers device pointers, 16-byte aligned.
+ * that size is 0): for bf16 plans with a block size that is a multiple of 8 it
+ * holds a transposed copy of V (rewritten by every call), and on the split path
+ * the partial results. All pointers device pointers, 16-byte aligned.
  * Errors: EINVAL (NULL or misaligned pointer), EWORKSPACE (ws NULL while
  * needed), EHIP (launch failure). */
 bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev,
@@ -142,11 +146,12 @@ bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev,
 /* Same as bd_attn_fwd / bd_attn_bwd, and in addition records caller-created
  * hipEvent_t handles (passed as void*) on the stream around the kernels, for
  * per-kernel timing on the stream that runs them: events[0] before the first
- * kernel and events[i] right after the i-th one. The forward pass launches 1
- * kernel (2 on the split path: partial results, then their merge; the count is
- * bd_attn_plan_kernels(plan, 0)), the backward pass 3 (delta = rowsum(dO * O),
- * dK/dV, dQ). n_events must be at least kernels + 1, else EINVAL and nothing is
- * enqueued. */
+ * kernel and events[i] right after the i-th one. The forward pass launches 1 to
+ * 3 kernels (V transpose on the pipelined path, the attention kernel, and the
+ * merge of partial results on the split path; bd_attn_plan_kernels(plan, 0) and
+ * bd_attn_plan_kernel_name give the count and names), the backward pass 3
+ * (delta = rowsum(dO * O), dK/dV, dQ). n_events must be at least kernels + 1,
+ * else EINVAL and nothing is enqueued. */
 bd_attn_status bd_attn_fwd_timed(bd_attn_plan_t plan, const void* meta_dev,
                                  const void* q, const void* k, const void* v,
                                  void* o, float* lse, void* ws, bd_attn_stream_t stream,
@@ -160,6 +165,12 @@ bd_attn_status bd_attn_bwd_timed(bd_attn_plan_t plan, const void* meta_dev,
 /* Number of kernels bd_attn_fwd (backward = 0) or bd_attn_bwd (backward = 1)
  * launches for this plan; 0 for a NULL plan. */
 int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward);
+
+/* Short name of the i-th kernel (0-based, launch order) that bd_attn_fwd
+ * (backward = 0) or bd_attn_bwd (backward = 1) launches for this plan, e.g.
+ * "transpose_v", "fwd", "combine", "bwd_pre", "dkdv", "dq"; NULL when i is out of
+ * range or the plan is NULL. The string is static. */
+const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int32_t i);
 
 /* Frees a plan (NULL is accepted). */
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan);

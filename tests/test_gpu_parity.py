@@ -89,7 +89,7 @@ def test_denoise_step_split(seed):
     wl = W.make_config(2, seed=seed, with_do=False)
     _say(f"case {wl.name} seed {seed}")
     gpu, plan = run_gpu(wl, backward=False)
-    assert plan.ws_fwd_bytes > 0, "the single-request shape takes the split path"
+    assert "combine" in plan.kernel_names(False), "the single-request shape takes the split path"
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
@@ -97,15 +97,16 @@ def test_denoise_step_no_split_matches_split():
     wl = W.make_config(2, with_do=False)
     g1, _ = run_gpu(wl, backward=False)
     g2, p2 = run_gpu(wl, flags=b.FLAG_NO_SPLIT, backward=False)
-    assert p2.ws_fwd_bytes == 0
+    assert "combine" not in p2.kernel_names(False)
     st = error_stats(g1["o"], g2["o"])
     assert st["max_abs"] <= 4e-3, st
 
 
-def test_staircase_full_kv_group_samples():
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+def test_staircase_full_kv_group_samples(flags):
     wl = W.make_config(4)
-    _say(f"case {wl.name} seed 4")
-    gpu, _ = run_gpu(wl)
+    _say(f"case {wl.name} seed 4 flags {flags}")
+    gpu, _ = run_gpu(wl, flags=flags)
     for g in (0, 5):
         sub = W.kv_group_slice(wl, g)
         ref = run_oracle(sub)
@@ -169,35 +170,38 @@ CASES = [
 
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("seed", [0, 1])
-def test_random_packs(case, seed):
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+def test_random_packs(case, seed, flags):
     B, hq, hkv, D, dt, sigma = CASES[case]
     rng = np.random.default_rng(7000 + 31 * case + seed)
     max_blocks = max(2, min(12, 600 // B))
     meta = W.random_meta(rng, max_segments=3, max_blocks=max_blocks, block_sizes=(B,), max_canvases=4,
                          hq=hq, hkv=hkv, d=D, dtype=dt)
     wl = W.random_workload(rng, meta, sigma=sigma)
-    _say(f"case random B={B} hq={hq} hkv={hkv} D={D} {dt} seed={seed} tq={meta.tq} tk={meta.tk}")
-    gpu, _ = run_gpu(wl)
+    _say(f"case random B={B} hq={hq} hkv={hkv} D={D} {dt} seed={seed} flags={flags} tq={meta.tq} tk={meta.tk}")
+    gpu, _ = run_gpu(wl, flags=flags)
     _compare(wl, gpu, run_oracle(wl))
 
 
-def test_forced_split_matches_oracle():
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+def test_forced_split_matches_oracle(flags):
     rng = np.random.default_rng(42)
     meta = W.Meta([1024, 512], [0, 512], [[5, 32, 0], [16]], 32, 8, 2, 128, "bf16")
     wl = W.random_workload(rng, meta, sigma=0.3)
-    gpu, plan = run_gpu(wl, flags=b.FLAG_FORCE_SPLIT)
-    assert plan.ws_fwd_bytes > 0
+    gpu, plan = run_gpu(wl, flags=b.FLAG_FORCE_SPLIT | flags)
+    assert "combine" in plan.kernel_names(False)
     _compare(wl, gpu, run_oracle(wl))
 
 
-def test_key_shift_stress():
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+def test_key_shift_stress(flags):
     # scores shifted by a large common offset exercise the running-maximum rescaling
     rng = np.random.default_rng(43)
     meta = W.Meta([512], [0], [[3, 16, 9]], 32, 4, 1, 128, "bf16")
     wl = W.random_workload(rng, meta, sigma=1.0)
     c = W.round_bf16(np.full((1, 1, 128), 2.0, np.float32))
     wl.k = W.round_bf16(wl.k + c)
-    gpu, _ = run_gpu(wl)
+    gpu, _ = run_gpu(wl, flags=flags)
     _compare(wl, gpu, run_oracle(wl))
 
 
