@@ -79,6 +79,7 @@ KERNEL_SOURCES = {
     "fwd": ["attn_fwd.hip", "attn_fwd_vt.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "transpose_v": ["attn_fwd_vt.hip", "kcommon.h", "kernels.h"],
     "dkdv": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "dkdv_masked": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "dq": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "bwd_pre": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "combine": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
@@ -333,6 +334,7 @@ def main():
     }
     if k == 2:   # the denoising step is bandwidth-bound: its forward is priced in bytes
         algo["fwd"] = ("hbm", float(q_bytes + 2 * kv_bytes))
+    algo["dkdv_masked"] = algo["dkdv"]
     dom = max(avg_ms, key=lambda n: avg_ms[n])
     bound, work = algo[dom]
     dur_s = avg_ms[dom] * 1e-3

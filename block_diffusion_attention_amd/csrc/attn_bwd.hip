@@ -139,11 +139,12 @@ __device__ __forceinline__ void dkdv_pointwise(f32x16& s, f32x16& dp, const floa
 // Each slot issues one MFMA, the LDS reads of the operand kPrefetch slots ahead
 // and its share of the per-score vector work; scheduling barriers between slots
 // keep that order, so the vector ALU and the LDS run in the shadow of the MFMAs.
-// Every score takes the row-limit select (padding rows have limit -1): one
-// program for all chunks keeps the accumulators in place across chunks.
+// MASKED applies the row limits to every score (padding rows have limit -1);
+// plans whose chunks are all either seen whole by a wave's keys or skipped use
+// the program without it (a separate kernel, chosen by the planner).
 constexpr int kPrefetch = 4;
 
-template <int D>
+template <int D, bool MASKED>
 __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
                                            f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16* cQ,
                                            const bf16* cG, const float* cL, const float* cD, const int* cM,
@@ -174,14 +175,17 @@ __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf1
       const int r0 = 32 * half + 8 * g4 + 4 * h;
       lv[half][g4] = *reinterpret_cast<const f32x4*>(cL + r0);
       dl[half][g4] = *reinterpret_cast<const f32x4*>(cD + r0);
-      lm[half][g4] = *reinterpret_cast<const int4*>(cM + r0);
+      if (MASKED) lm[half][g4] = *reinterpret_cast<const int4*>(cM + r0);
     }
   };
   // P and dS of score element e of a half
   auto pointwise = [&](int half, int e) {
     const int g4 = e >> 2, q = e & 3;
-    const int lim = q == 0 ? lm[half][g4].x : q == 1 ? lm[half][g4].y : q == 2 ? lm[half][g4].z : lm[half][g4].w;
-    const float x = kpos < lim ? sc[half][e] : -INFINITY;
+    float x = sc[half][e];
+    if (MASKED) {
+      const int lim = q == 0 ? lm[half][g4].x : q == 1 ? lm[half][g4].y : q == 2 ? lm[half][g4].z : lm[half][g4].w;
+      x = kpos < lim ? x : -INFINITY;
+    }
     const float p = fast_exp2(__builtin_fmaf(x, scale_log2, -lv[half][g4][q]));
     sc[half][e] = p;
     dp[half][e] = p * (dp[half][e] - dl[half][g4][q]);
@@ -225,7 +229,7 @@ __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf1
   });
 }
 
-template <int D>
+template <int D, bool MASKED>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) dkdv_bf16_kernel(BwdArgs a) {
   using Gm = DkdvGeom<D>;
   constexpr int NKS = D / 16, NDB = D / 32;
@@ -275,24 +279,42 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // the same chunks and share them in L2.
   // async fetch of chunk c: Q and dO rows, log2-domain LSE and delta per row, row
   // limits. Waves 0 and 1 issue one load more than waves 2 and 3.
+  // Row offsets of the chunk fetch: chunk column cc holds row lane ^ (4 * (cc & 3))
+  // (chunk-major tile layout); row r of a chunk is the (token r / G, head r % G)
+  // pair, at element offset ((r / G) * Hq + r % G) * D from the chunk's first row.
+  // Computed at each fetch: offsets held across the chunk loop have made the
+  // compiler wait for every load in flight before the LDS reads.
+  constexpr int PER_WAVE = (D / 8) / 4;
+  auto row_off = [&](int r) { return ((r / G) * a.hq + (r - (r / G) * G)) * D; };
+
+  // async fetch of chunk c: Q and dO rows, log2-domain LSE and delta per row, and
+  // (masked kernel) row limits. Waves 0 and 1 issue one load more than 2 and 3.
   auto issue = [&](int c, bf16* dQ_, bf16* dG_, float* dL_, float* dD_, int* dM_) {
     const ChunkGeom g = chunk_geom(kt, a.canvq, nchunks - 1 - c, nc0, cpc, qct);
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
-    auto rowp = [&](const bf16* base) {
-      return [=](int r) {
-        const int t = r / G, gh = r - (r / G) * G;
-        return base + ((int64_t)(g.tok0 + t) * a.hq + kvh * G + gh) * D;
-      };
-    };
-    tile_fetch<D>(dQ_, rowp(Q), nrows, wave, lane);
-    tile_fetch<D>(dG_, rowp(dO), nrows, wave, lane);
+    const int64_t row0 = (int64_t)g.tok0 * a.hq + kvh * G;
+    const bf16* qb = Q + row0 * D;
+    const bf16* gb = dO + row0 * D;
+    // rows past the chunk's end read its last row
+#pragma unroll
+    for (int n = 0; n < PER_WAVE; ++n) {
+      const int cc = wave * PER_WAVE + n;
+      const int64_t off = row_off(min(lane ^ ((cc & 3) << 2), nrows - 1)) + cc * 8;
+      __builtin_amdgcn_global_load_lds(qb + off, (lds_void*)(dQ_ + cc * kTileRows * 8), 16, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < PER_WAVE; ++n) {
+      const int cc = wave * PER_WAVE + n;
+      const int64_t off = row_off(min(lane ^ ((cc & 3) << 2), nrows - 1)) + cc * 8;
+      __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(dG_ + cc * kTileRows * 8), 16, 0, 0);
+    }
     if (wave < 2) {                                     // 64 rows x 4 bytes each
       const int r = min(lane, nrows - 1);
       const int t = r / G, gh = r - (r / G) * G;
       const int64_t qr = (int64_t)(g.tok0 + t) * a.hq + kvh * G + gh;
       const float* src = wave == 0 ? a.lse2 + qr : a.delta + qr;
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(wave == 0 ? dL_ : dD_), 4, 0, 0);
-    } else if (wave == 2) {
+    } else if (MASKED && wave == 2) {
       const int r = lane, t = r / G;
       int lim = -1;                                     // padding rows see nothing
       if (r < nrows) lim = g.pos0 >= 0 ? ((g.pos0 + t) / B + 1) * B : g.lim;
@@ -344,7 +366,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
     // skip when no valid row sees any of the wave's keys
     if (!wave_live || (!canvas_keys && wpos_lo >= lim_last)) return;
-    dkdv_chunk<D>(kf, vf, dkt, dvt, cQ, cG, cL, cD, cM, lo, h, kpos, a.scale_log2);
+    dkdv_chunk<D, MASKED>(kf, vf, dkt, dvt, cQ, cG, cL, cD, cM, lo, h, kpos, a.scale_log2);
   };
   for (int c = 0; c < nchunks; c += kBwdStages) {
     step(c, sQ0, sG0, sL0, sD0, sM0, sQ2, sG2, sL2, sD2, sM2);
@@ -517,10 +539,15 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s) {
+hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, bool masked, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+  if (head_dim == 128) {
+    if (masked) hipLaunchKernelGGL((dkdv_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dkdv_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (masked) hipLaunchKernelGGL((dkdv_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dkdv_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -52,7 +52,10 @@ int fwd_kernels(const Plan& p) {
 }
 const char* kernel_name(const Plan& p, bool backward, int i) {
   static const char* const bwd[] = {"bwd_pre", "dkdv", "dq"};
-  if (backward) return (i >= 0 && i < 3) ? bwd[i] : nullptr;
+  if (backward) {
+    if (i == 1 && p.desc.dtype == BD_ATTN_BF16 && p.dkdv_masked) return "dkdv_masked";
+    return (i >= 0 && i < 3) ? bwd[i] : nullptr;
+  }
   if (i < 0 || i >= fwd_kernels(p)) return nullptr;
   const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
   if (bf16 && p.use_vt) {
@@ -238,7 +241,7 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   hipError_t e = bdattn::launch_bwd_pre(a, D, bf16, s);
   if ((st = hip_status(e, "bwd_pre launch"))) return st;
   if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
-  e = bf16 ? bdattn::launch_dkdv_bf16(a, D, (int)p.bwd_items.size(), s)
+  e = bf16 ? bdattn::launch_dkdv_bf16(a, D, p.dkdv_masked, (int)p.bwd_items.size(), s)
            : bdattn::launch_dkdv_f32(a, D, (int)p.bwd_items.size(), s);
   if ((st = hip_status(e, "dkdv launch"))) return st;
   if ((st = hip_status(ev.mark(2), "hipEventRecord"))) return st;

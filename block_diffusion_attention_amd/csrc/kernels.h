@@ -61,7 +61,7 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int items, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
-hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, bool masked, int grid, hipStream_t s);
 hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
 
 hipError_t launch_transpose_v(const void* v, void* vt, int tk, int tk_pad, int hkv, int head_dim, hipStream_t s);

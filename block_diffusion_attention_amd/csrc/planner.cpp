@@ -387,6 +387,17 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
     off = p.off_ws_lse + nsplit * kQRows * 4;
   }
   p.ws_fwd = (size_t)off;
+  // dK/dV without per-score limits: a wave's 32 keys start at a multiple of 32;
+  // if every row limit is a multiple of 32 (block size a multiple of 32), every
+  // 64-row query chunk lies inside one block (64 / G tokens dividing B, query
+  // ranges starting at block boundaries) and no chunk is partial (B * G a multiple
+  // of 64), each (chunk, wave) pair is seen either whole or not at all.
+  {
+    const int qct = 64 / G;
+    bool aligned = B % 32 == 0 && 64 % G == 0 && B % qct == 0;
+    for (int s = 0; s < S && aligned; ++s) aligned = p.q0[s] % B == 0;
+    p.dkdv_masked = !aligned;
+  }
   p.off_ws_lse2 = ceil_div(tq * Hq * 4, 256) * 256;          // delta [Tq, Hq] fp32, then LSE*log2(e)
   p.ws_bwd = (size_t)(2 * p.off_ws_lse2);
   return BD_ATTN_OK;

@@ -32,7 +32,8 @@ struct Plan {
   int64_t off_qtiles = 0, off_fwd = 0, off_fwd_order = 0, off_comb = 0, off_dq = 0,
           off_ktiles = 0, off_canvq = 0, off_bwd = 0;   // int32 offsets into blob
   size_t ws_fwd = 0, ws_bwd = 0;
-  bool use_vt = false;               // bf16 forward through the pipelined kernel (B % 8 == 0)
+  bool use_vt = false;               // bf16 forward through the transposed V copy (B % 8 == 0)
+  bool dkdv_masked = true;           // dK/dV needs per-score row limits (see build_plan)
   int64_t tk_pad = 0;                // row length of the transposed V copy
   int64_t off_ws_vt = 0;             // byte offsets in the forward workspace: V transposed,
   int64_t off_ws_part = 0;           // partial O,

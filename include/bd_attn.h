@@ -169,7 +169,11 @@ int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward);
 /* Short name of the i-th kernel (0-based, launch order) that bd_attn_fwd
  * (backward = 0) or bd_attn_bwd (backward = 1) launches for this plan, e.g.
  * "transpose_v", "fwd", "combine", "bwd_pre", "dkdv", "dq"; NULL when i is out of
- * range or the plan is NULL. The string is static. */
+ * range or the plan is NULL. "dkdv_masked" names the bf16 dK/dV kernel that
+ * applies a row limit to every score: plans whose query chunks are not all either
+ * seen whole by a 32-key group or not at all (block size not a multiple of 32,
+ * 64 / G not dividing it, or a query range starting inside a block). The string
+ * is static. */
 const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int32_t i);
 
 /* Frees a plan (NULL is accepted). */

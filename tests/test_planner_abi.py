@@ -202,3 +202,20 @@ def test_metadata_grows_with_tiles_not_n_squared():
     # doubling the context about doubles the work lists (linear), never quadruples them
     for s0, s1 in zip(sizes, sizes[1:]):
         assert s1 < 2.3 * s0
+
+
+@pytest.mark.parametrize("ctx,q0,B,hq,hkv,dt,want", [
+    # block a multiple of 32, 64 / G tokens dividing it, ranges at block starts
+    ([256, 128], [0, 128], 32, 32, 8, "bf16", "dkdv"),
+    ([256, 128], [0, 64], 64, 8, 8, "bf16", "dkdv"),          # G = 1: 64 tokens per chunk
+    ([256, 128], [0, 40], 32, 32, 8, "bf16", "dkdv_masked"),  # query range inside a block
+    ([256, 128], [0, 128], 16, 32, 8, "bf16", "dkdv_masked"),  # block below 32 keys
+    ([288, 192], [0, 96], 96, 12, 4, "bf16", "dkdv_masked"),   # G = 3 does not divide 64
+    ([256, 128], [0, 96], 32, 8, 8, "bf16", "dkdv_masked"),    # 64 tokens per chunk > block
+    ([256, 128], [0, 40], 32, 32, 8, "fp32", "dkdv"),          # fp32 has one dK/dV kernel
+])
+def test_dkdv_variant_selection(ctx, q0, B, hq, hkv, dt, want):
+    """The unmasked dK/dV program is only chosen when every (64-row query chunk,
+    32-key group) pair is either wholly visible or wholly hidden."""
+    meta = Meta(ctx, q0, [[1], [0, 2]], B, hq, hkv, 64, dt)
+    assert b.Plan(meta).kernel_names(True) == ["bwd_pre", want, "dq"]
