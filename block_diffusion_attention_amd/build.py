@@ -18,6 +18,11 @@ CXX_SOURCES = ["planner.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # packed fp32 VALU instructions stay disabled for all device code
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Extra flags per source. attn_bwd.hip: MFMA results go to vector registers even
+# in kernels that keep operands in accumulation registers (the dK/dV kernel holds
+# its K/V fragments there); otherwise the scores come out in accumulation
+# registers and every element costs an extra copy before the vector ALU sees it.
+HIP_FILE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 
@@ -35,7 +40,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, s.replace(".hip", ".o"))
-        jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj], obj))
+        jobs.append(([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj], obj))
     for s in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, s.replace(".cpp", ".o"))
         jobs.append((["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj], obj))
