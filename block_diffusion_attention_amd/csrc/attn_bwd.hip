@@ -300,20 +300,20 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     for (int n = 0; n < PER_WAVE; ++n) {
       const int cc = wave * PER_WAVE + n;
       const int64_t off = row_off(min(lane ^ ((cc & 3) << 2), nrows - 1)) + cc * 8;
-      __builtin_amdgcn_global_load_lds(qb + off, (lds_void*)(dQ_ + cc * kTileRows * 8), 16, 0, 0);
+      dma_b128(qb + off, (lds_void*)(dQ_ + cc * kTileRows * 8));
     }
 #pragma unroll
     for (int n = 0; n < PER_WAVE; ++n) {
       const int cc = wave * PER_WAVE + n;
       const int64_t off = row_off(min(lane ^ ((cc & 3) << 2), nrows - 1)) + cc * 8;
-      __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(dG_ + cc * kTileRows * 8), 16, 0, 0);
+      dma_b128(gb + off, (lds_void*)(dG_ + cc * kTileRows * 8));
     }
     if (wave < 2) {                                     // 64 rows x 4 bytes each
       const int r = min(lane, nrows - 1);
       const int t = r / G, gh = r - (r / G) * G;
       const int64_t qr = (int64_t)(g.tok0 + t) * a.hq + kvh * G + gh;
       const float* src = wave == 0 ? a.lse2 + qr : a.delta + qr;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(wave == 0 ? dL_ : dD_), 4, 0, 0);
+      dma_b32(src, (lds_void*)(wave == 0 ? dL_ : dD_));
     } else if (MASKED && wave == 2) {
       const int r = lane, t = r / G;
       int lim = -1;                                     // padding rows see nothing

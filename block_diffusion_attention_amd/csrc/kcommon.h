@@ -119,6 +119,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //     land in 4 different 64-byte quarters of a 256-byte bank line.
 // Every per-lane address is a lane constant plus a compile-time offset.
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous copy global -> LDS of 16 (dma_b128) or 4 (dma_b32) bytes per lane:
+// lane l writes LDS bytes dst + 16 l (4 l); dst is the same for the whole wave
+// (it goes into M0). Written as inline assembly rather than the compiler builtin:
+// the compiler counts a builtin copy in flight as a pending LDS access of the
+// kind that completes out of order, and then turns every wait for an LDS read
+// into a full drain (lgkmcnt(0)), which defeats any read-ahead of MFMA operands.
+// The hardware tracks these copies with the vector memory counter only; callers
+// wait for them with explicit vmcnt waits (or a barrier that waits vmcnt(0))
+// before reading the destination.
+__device__ __forceinline__ void dma_b128(const void* src, lds_void* dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void* src, lds_void* dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m) : "memory");
+}
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileRows = 64;
