@@ -84,16 +84,18 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const KTile& kt, const CanvasQ* 
 // 32w .. 32w+31 (K and V rows in registers, dK^T and dV^T accumulators) and
 // processes every 64-row query chunk that can see the tile, as two 32-row
 // halves. Query chunks (rows = tokens x grouped heads, with their log2-domain
-// LSE and delta) go from global memory straight into LDS, three stages deep, so
-// two chunks are in flight while one is consumed. The transposed operands dO^T
-// and Q^T of dV^T = dO^T P and dK^T = Q^T dS are read with the LDS transpose
-// read from the natural tiles.
+// LSE and delta) go from global memory straight into LDS (swizzled row-major
+// tiles, a few cache lines per copy instruction), three stages deep, so two
+// chunks are in flight while one is consumed. The transposed operands dO^T and
+// Q^T of dV^T = dO^T P and dK^T = Q^T dS are read with the LDS transpose read
+// from the same tiles.
 //
 // Per half: S = Q K^T and dP = dO V^T (16 MFMAs), then P = exp2(S*c - lse2),
 // dS = P (dP - delta) on the vector ALUs, then dV^T += dO^T P and
-// dK^T += Q^T dS (16 MFMAs). Chunks fully visible to a wave's keys take a
-// straight-line path in which the products of one half overlap the ALU work of
-// the other; boundary chunks take the predicated path.
+// dK^T += Q^T dS (16 MFMAs), in one fixed slot program where the products of
+// one half overlap the ALU work of the other. The masked instantiation applies
+// per-score row limits; the planner picks the other one when every (chunk,
+// 32-key group) pair is either wholly visible or skipped.
 constexpr int kBwdStages = 3;
 
 template <int D>
@@ -148,7 +150,7 @@ template <int D, bool MASKED>
 __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
                                            f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], const bf16* cQ,
                                            const bf16* cG, const float* cL, const float* cD, const int* cM,
-                                           const CmLane& lo, int h, int kpos, float scale_log2) {
+                                           const SwLane<D>& lo, int h, int kpos, float scale_log2) {
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int NS = 2 * NKS;                 // MFMA slots per phase
   constexpr int NSLOT = 4 * NS;
@@ -163,11 +165,11 @@ __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf1
   auto fetch = [&](int i) {
     if (i < 2 * NS) {
       const int half = i / NS, k = i % NS;
-      return cm_row8((k & 1) ? cG : cQ, lo, 32 * half, k >> 1);
+      return sw_row8<D>((k & 1) ? cG : cQ, lo, 32 * half, k >> 1);
     }
     const int half = (i - 2 * NS) / NS, k = (i - 2 * NS) % NS;
     const int ks = k / (2 * NDB), db = (k % (2 * NDB)) >> 1;
-    return cm_tr8((k & 1) ? cQ : cG, lo, 32 * half + 16 * ks, 32 * db);
+    return sw_tr8<D>((k & 1) ? cQ : cG, lo, 32 * half + 16 * ks, 32 * db);
   };
   auto rowterms = [&](int half) {
 #pragma unroll
@@ -249,7 +251,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 31, h = lane >> 5;
-  const CmLane lo(lane);
+  const SwLane<D> lo(lane);
   const int4 itv = ld_rec4(a.bwd_items, blockIdx.x);
   if (itv.x < 0) return;
   const int kvh = itv.y;
@@ -277,37 +279,21 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // Chunks are visited from the last one back: every key tile of a segment ends
   // its query range at the same place, so tiles running at the same time start on
   // the same chunks and share them in L2.
-  // async fetch of chunk c: Q and dO rows, log2-domain LSE and delta per row, row
-  // limits. Waves 0 and 1 issue one load more than waves 2 and 3.
-  // Row offsets of the chunk fetch: chunk column cc holds row lane ^ (4 * (cc & 3))
-  // (chunk-major tile layout); row r of a chunk is the (token r / G, head r % G)
-  // pair, at element offset ((r / G) * Hq + r % G) * D from the chunk's first row.
-  // Computed at each fetch: offsets held across the chunk loop have made the
-  // compiler wait for every load in flight before the LDS reads.
-  constexpr int PER_WAVE = (D / 8) / 4;
+  // Row r of a chunk is the (token r / G, head r % G) pair, at element offset
+  // ((r / G) * Hq + r % G) * D from the chunk's first row. Offsets are computed at
+  // each fetch: offsets held across the chunk loop have made the compiler wait for
+  // every load in flight before the LDS reads.
   auto row_off = [&](int r) { return ((r / G) * a.hq + (r - (r / G) * G)) * D; };
 
-  // async fetch of chunk c: Q and dO rows, log2-domain LSE and delta per row, and
-  // (masked kernel) row limits. Waves 0 and 1 issue one load more than 2 and 3.
+  // async fetch of chunk c: Q and dO rows (swizzled row-major tiles; rows past the
+  // chunk's end read its last row), log2-domain LSE and delta per row, and (masked
+  // kernel) row limits. Waves 0 and 1 issue one load more than 2 and 3.
   auto issue = [&](int c, bf16* dQ_, bf16* dG_, float* dL_, float* dD_, int* dM_) {
     const ChunkGeom g = chunk_geom(kt, a.canvq, nchunks - 1 - c, nc0, cpc, qct);
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
     const int64_t row0 = (int64_t)g.tok0 * a.hq + kvh * G;
-    const bf16* qb = Q + row0 * D;
-    const bf16* gb = dO + row0 * D;
-    // rows past the chunk's end read its last row
-#pragma unroll
-    for (int n = 0; n < PER_WAVE; ++n) {
-      const int cc = wave * PER_WAVE + n;
-      const int64_t off = row_off(min(lane ^ ((cc & 3) << 2), nrows - 1)) + cc * 8;
-      dma_b128(qb + off, (lds_void*)(dQ_ + cc * kTileRows * 8));
-    }
-#pragma unroll
-    for (int n = 0; n < PER_WAVE; ++n) {
-      const int cc = wave * PER_WAVE + n;
-      const int64_t off = row_off(min(lane ^ ((cc & 3) << 2), nrows - 1)) + cc * 8;
-      dma_b128(gb + off, (lds_void*)(dG_ + cc * kTileRows * 8));
-    }
+    sw_tile_fetch<D>(dQ_, Q + row0 * D, row_off, nrows, wave, lane);
+    sw_tile_fetch<D>(dG_, dO + row0 * D, row_off, nrows, wave, lane);
     if (wave < 2) {                                     // 64 rows x 4 bytes each
       const int r = min(lane, nrows - 1);
       const int t = r / G, gh = r - (r / G) * G;

@@ -206,6 +206,82 @@ __device__ __forceinline__ void tile_fetch(bf16* tile, RowAddr row_ptr, int nval
 }
 
 // ---------------------------------------------------------------------------
+// Swizzled row-major tiles. A tile holds 64 rows of D bf16 (CH = D/8 16-byte
+// chunks per row) with chunk c of row r in 16-byte slot
+//   r * CH + (c ^ sw(r)),  sw(r) = 4 (r & 3) + ((r >> 2) & 3)            (D = 128)
+//                          sw(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3)     (D = 64)
+// One copy instruction (lane l to slot 64 m + l) covers 4 (8) whole rows, so it
+// touches a few cache lines instead of 64. Reads with the 64-bank LDS:
+//   - natural MFMA operands (16 rows at one chunk per 16-lane pass) hit 16
+//     distinct 16-byte bank groups, since sw is a bijection on r mod 16 (for
+//     D = 64 on each parity class);
+//   - transposed reads (4 rows x 4 aligned chunks per 32-lane pass) too, since
+//     the 4 rows differ in sw's high bits, which select the aligned chunk group.
+// The XOR mixes lane-dependent bits with the compile-time chunk index, so each
+// lane keeps one offset per operand variant (NKS natural, 2 NDB transposed).
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+template <int D>
+struct SwLane {
+  static constexpr int CH = D / 8, NKS = D / 16, NDB = D / 32;
+  int a[NKS];        // natural operand: row j = lane%32 of a 32-row block, chunk 2kk + lane/32
+  int t[NDB][2];     // transposed operand: 32-column block db, 8-row half jj of a 16-row step
+  __device__ explicit SwLane(int lane) {
+    const int j = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) a[kk] = 16 * (j * CH + ((2 * kk + h) ^ swz<D>(j)));
+    const int g = lane >> 4, s = lane & 15;
+    const int cl = 2 * (g & 1) + ((s & 3) >> 1);
+    const int rl = 4 * (g >> 1) + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int w = swz<D>(rl + 8 * jj);
+        t[db][jj] = 16 * ((rl + 8 * jj) * CH + 4 * (db ^ (w >> 2)) + (cl ^ (w & 3))) + 8 * (s & 1);
+      }
+  }
+};
+
+// Natural MFMA operand: row rbase + lane%32 (rbase a multiple of 32), elements
+// 16kk + 8h .. +7 (h = lane/32).
+template <int D>
+__device__ __forceinline__ bf16x8 sw_row8(const bf16* tile, const SwLane<D>& o, int rbase, int kk) {
+  const char* p = reinterpret_cast<const char*>(tile) + 16 * rbase * (D / 8) + o.a[kk];
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposed MFMA A operand, same element order as cm_tr8: A[i][k] = T[row0 +
+// r(k)][col0 + i] with slot 8h + 4jj + e reading row row0 + 8jj + 4h + e. row0 is
+// a multiple of 16, col0 of 32.
+template <int D>
+__device__ __forceinline__ bf16x8 sw_tr8(const bf16* tile, const SwLane<D>& o, int row0, int col0) {
+  const char* base = reinterpret_cast<const char*>(tile) + 16 * row0 * (D / 8);
+  const u32x2 lo = __builtin_bit_cast(u32x2, lds_tr4(base + o.t[col0 >> 5][0]));
+  const u32x2 hi = __builtin_bit_cast(u32x2, lds_tr4(base + o.t[col0 >> 5][1]));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Issues the async copy of one 64-row swizzled tile. Row r starts at element
+// offset row_off(min(r, nvalid - 1)) from base; the 4 waves issue D/32 copy
+// instructions each (instruction m = wave * D/32 + n).
+template <int D, class RowOff>
+__device__ __forceinline__ void sw_tile_fetch(bf16* tile, const bf16* base, RowOff row_off, int nvalid, int wave,
+                                              int lane) {
+  constexpr int CH = D / 8, RPI = 64 / CH, PER_WAVE = CH / 4;
+#pragma unroll
+  for (int n = 0; n < PER_WAVE; ++n) {
+    const int m = wave * PER_WAVE + n;
+    const int r = m * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz<D>(r);
+    dma_b128(base + row_off(min(r, nvalid - 1)) + c * 8, (lds_void*)(tile + m * 64 * 8));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Padded row-major tiles. A tile of ROWS rows x CH 16-byte chunks keeps each row
 // in CH + 1 slots: chunk (r, c) sits in slot r * (CH + 1) + c (the last slot of a
 // row is padding). One global_load_lds instruction (lane l writes slot 64 m + l)
