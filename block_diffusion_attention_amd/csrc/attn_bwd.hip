@@ -280,31 +280,31 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // its query range at the same place, so tiles running at the same time start on
   // the same chunks and share them in L2.
   // Row r of a chunk is the (token r / G, head r % G) pair, at element offset
-  // ((r / G) * Hq + r % G) * D from the chunk's first row. Offsets are computed at
-  // each fetch: offsets held across the chunk loop have made the compiler wait for
-  // every load in flight before the LDS reads.
-  auto row_off = [&](int r) { return ((r / G) * a.hq + (r - (r / G) * G)) * D; };
+  // ((r / G) * Hq + r % G) * D from the chunk's first row; the per-lane offsets
+  // are the same for every chunk and are computed once.
+  auto row_elems = [&](int r) { return ((r / G) * a.hq + (r - (r / G) * G)) * D; };
+  const SwFetch<D> fetch(row_elems, wave, lane);
+  const int lane_tok = lane / G;                        // token of chunk row `lane`
+  const int lane_row = lane_tok * a.hq + (lane - lane_tok * G);  // its LSE/delta row
 
-  // async fetch of chunk c: Q and dO rows (swizzled row-major tiles; rows past the
-  // chunk's end read its last row), log2-domain LSE and delta per row, and (masked
-  // kernel) row limits. Waves 0 and 1 issue one load more than 2 and 3.
+  // async fetch of chunk c: Q and dO rows (swizzled row-major tiles), log2-domain
+  // LSE and delta per row, and (masked kernel) row limits. Rows past the chunk's
+  // end read its last row. Waves 0 and 1 issue one load more than 2 and 3.
   auto issue = [&](int c, bf16* dQ_, bf16* dG_, float* dL_, float* dD_, int* dM_) {
     const ChunkGeom g = chunk_geom(kt, a.canvq, nchunks - 1 - c, nc0, cpc, qct);
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
     const int64_t row0 = (int64_t)g.tok0 * a.hq + kvh * G;
-    sw_tile_fetch<D>(dQ_, Q + row0 * D, row_off, nrows, wave, lane);
-    sw_tile_fetch<D>(dG_, dO + row0 * D, row_off, nrows, wave, lane);
+    const int last = ((nrows - 1) / G) * a.hq + (nrows - 1) % G;   // uniform
+    fetch.issue(dQ_, Q + row0 * D, nrows, last * D, wave);
+    fetch.issue(dG_, dO + row0 * D, nrows, last * D, wave);
     if (wave < 2) {                                     // 64 rows x 4 bytes each
-      const int r = min(lane, nrows - 1);
-      const int t = r / G, gh = r - (r / G) * G;
-      const int64_t qr = (int64_t)(g.tok0 + t) * a.hq + kvh * G + gh;
+      const int64_t qr = row0 + (lane < nrows ? lane_row : last);
       const float* src = wave == 0 ? a.lse2 + qr : a.delta + qr;
       dma_b32(src, (lds_void*)(wave == 0 ? dL_ : dD_));
     } else if (MASKED && wave == 2) {
-      const int r = lane, t = r / G;
       int lim = -1;                                     // padding rows see nothing
-      if (r < nrows) lim = g.pos0 >= 0 ? ((g.pos0 + t) / B + 1) * B : g.lim;
-      dM_[r] = lim;
+      if (lane < nrows) lim = g.pos0 >= 0 ? ((g.pos0 + lane_tok) / B + 1) * B : g.lim;
+      dM_[lane] = lim;
     }
   };
 

@@ -265,21 +265,35 @@ __device__ __forceinline__ bf16x8 sw_tr8(const bf16* tile, const SwLane<D>& o, i
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// Issues the async copy of one 64-row swizzled tile. Row r starts at element
-// offset row_off(min(r, nvalid - 1)) from base; the 4 waves issue D/32 copy
-// instructions each (instruction m = wave * D/32 + n).
-template <int D, class RowOff>
-__device__ __forceinline__ void sw_tile_fetch(bf16* tile, const bf16* base, RowOff row_off, int nvalid, int wave,
-                                              int lane) {
-  constexpr int CH = D / 8, RPI = 64 / CH, PER_WAVE = CH / 4;
+// Async copy of 64-row swizzled tiles whose rows sit at fixed element offsets
+// from a per-tile base pointer (offsets of rows 0..63 are the same for every
+// tile). The per-lane parts (row, swizzled chunk and offset of each of the
+// wave's D/32 copy instructions) are computed once; a fetch then only selects
+// the last valid row for rows at or past nvalid.
+template <int D>
+struct SwFetch {
+  static constexpr int CH = D / 8, RPI = 64 / CH, PER_WAVE = CH / 4;
+  int row[PER_WAVE], col[PER_WAVE], off[PER_WAVE];
+  template <class RowOff>
+  __device__ SwFetch(RowOff row_off, int wave, int lane) {
 #pragma unroll
-  for (int n = 0; n < PER_WAVE; ++n) {
-    const int m = wave * PER_WAVE + n;
-    const int r = m * RPI + lane / CH;
-    const int c = (lane % CH) ^ swz<D>(r);
-    dma_b128(base + row_off(min(r, nvalid - 1)) + c * 8, (lds_void*)(tile + m * 64 * 8));
+    for (int n = 0; n < PER_WAVE; ++n) {
+      const int r = (wave * PER_WAVE + n) * RPI + lane / CH;
+      row[n] = r;
+      col[n] = ((lane % CH) ^ swz<D>(r)) * 8;
+      off[n] = row_off(r) + col[n];
+    }
   }
-}
+  // last_off: element offset of row nvalid - 1 (any valid row works for the rows
+  // past the end: their values are never used)
+  __device__ __forceinline__ void issue(bf16* tile, const bf16* base, int nvalid, int last_off, int wave) const {
+#pragma unroll
+    for (int n = 0; n < PER_WAVE; ++n) {
+      const int o = row[n] < nvalid ? off[n] : last_off + col[n];
+      dma_b128(base + o, (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Padded row-major tiles. A tile of ROWS rows x CH 16-byte chunks keeps each row
