@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
-  const CmLane lo(lane);
+  const SwLane<D> lo(lane);
   const int4 itv = reinterpret_cast<const int4*>(a.dq_items)[blockIdx.x];
   if (itv.x < 0) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
@@ -418,14 +418,16 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   const int n1 = (qt.lim_max + KT - 1) / KT;
   const int64_t kv_stride = (int64_t)a.hkv * D;
 
+  // K and V tiles: 64 key rows at stride Hkv*D, swizzled row-major in LDS
+  const SwFetch<D> fetch([&](int r) { return r * (int)kv_stride; }, wave, lane);
   auto issue = [&](int kt, bf16* dK, bf16* dV) {
     int base, nvalid;
     if (kt < n1) { base = qt.k_ctx + kt * KT; nvalid = min(KT, qt.lim_max - kt * KT); }
     else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
-    const bf16* kb = K + (int64_t)base * kv_stride + kvh * D;
-    const bf16* vb = V + (int64_t)base * kv_stride + kvh * D;
-    tile_fetch<D>(dK, [&](int r) { return kb + r * kv_stride; }, nvalid, wave, lane);
-    tile_fetch<D>(dV, [&](int r) { return vb + r * kv_stride; }, nvalid, wave, lane);
+    const int64_t off0 = (int64_t)base * kv_stride + kvh * D;
+    const int last = (nvalid - 1) * (int)kv_stride;
+    fetch.issue(dK, K + off0, nvalid, last, wave);
+    fetch.issue(dV, V + off0, nvalid, last, wave);
   };
   if (kt_begin < kt_end) issue(kt_begin, sK0, sV0);
 
@@ -458,8 +460,8 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
     for (int kk = 0; kk < NKS; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32(cm_row8(sK, lo, kb * 32, kk), qf[kk], s[kb]);
-        dp[kb] = mfma32(cm_row8(sV, lo, kb * 32, kk), df[kk], dp[kb]);
+        s[kb] = mfma32(sw_row8<D>(sK, lo, kb * 32, kk), qf[kk], s[kb]);
+        dp[kb] = mfma32(sw_row8<D>(sV, lo, kb * 32, kk), df[kk], dp[kb]);
       }
     if (need_mask) {
 #pragma unroll
@@ -487,7 +489,7 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
     for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = mfma32(cm_tr8(sK, lo, kq * 16, db * 32), sb[kq], acc[db]);
+        acc[db] = mfma32(sw_tr8<D>(sK, lo, kq * 16, db * 32), sb[kq], acc[db]);
   };
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
     step(kt, sK0, sV0, sK1, sV1);
