@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libbdattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
-FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD, FLAG_FWD_DIRECT = 1, 2, 4, 8
+FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD, FLAG_FWD_DIRECT, FLAG_FWD_VT = 1, 2, 4, 8, 16
 
 
 def flag_split_tiles(n: int) -> int:

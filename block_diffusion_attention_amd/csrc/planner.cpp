@@ -375,7 +375,15 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   const int64_t D = d->head_dim;
   const int64_t Hq = d->num_q_heads;
   // forward workspace: [V transposed (pipelined path)] [partial O fp32] [partial LSE]
-  p.use_vt = !(d->flags & BD_ATTN_FLAG_FWD_DIRECT) && d->dtype == BD_ATTN_BF16 && B % 8 == 0;
+  // The transposed V copy costs a read and a write of V and one launch; it pays
+  // when the forward reads every V tile several times (many query tiles per kv
+  // head), not for a short query over a long key arena.
+  int64_t visits = 0;
+  for (const FwdItem& it : p.fwd_items)
+    if (it.qtile >= 0) visits += it.kt_end - it.kt_begin;
+  const int64_t distinct = ceil_div(tk, 64) * Hkv;
+  p.use_vt = !(d->flags & BD_ATTN_FLAG_FWD_DIRECT) && d->dtype == BD_ATTN_BF16 && B % 8 == 0 &&
+             (visits >= 4 * distinct || (d->flags & BD_ATTN_FLAG_FWD_VT));
   p.tk_pad = ceil_div(tk, 64) * 64 + 64;
   int64_t off = 0;
   p.off_ws_vt = 0;

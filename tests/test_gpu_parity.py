@@ -85,10 +85,12 @@ def test_tiny_fp32_canvas_only():
 
 
 @pytest.mark.parametrize("seed", [2, 102, 202])
-def test_denoise_step_split(seed):
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
+def test_denoise_step_split(seed, flags):
     wl = W.make_config(2, seed=seed, with_do=False)
-    _say(f"case {wl.name} seed {seed}")
-    gpu, plan = run_gpu(wl, backward=False)
+    _say(f"case {wl.name} seed {seed} flags {flags}")
+    gpu, plan = run_gpu(wl, flags=flags, backward=False)
+    assert ("transpose_v" in plan.kernel_names(False)) == bool(flags & b.FLAG_FWD_VT)
     assert "combine" in plan.kernel_names(False), "the single-request shape takes the split path"
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
@@ -102,7 +104,7 @@ def test_denoise_step_no_split_matches_split():
     assert st["max_abs"] <= 4e-3, st
 
 
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
 def test_staircase_full_kv_group_samples(flags):
     wl = W.make_config(4)
     _say(f"case {wl.name} seed 4 flags {flags}")
@@ -170,7 +172,7 @@ CASES = [
 
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("seed", [0, 1])
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
 def test_random_packs(case, seed, flags):
     B, hq, hkv, D, dt, sigma = CASES[case]
     rng = np.random.default_rng(7000 + 31 * case + seed)
@@ -183,7 +185,7 @@ def test_random_packs(case, seed, flags):
     _compare(wl, gpu, run_oracle(wl))
 
 
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
 def test_forced_split_matches_oracle(flags):
     rng = np.random.default_rng(42)
     meta = W.Meta([1024, 512], [0, 512], [[5, 32, 0], [16]], 32, 8, 2, 128, "bf16")
@@ -193,7 +195,7 @@ def test_forced_split_matches_oracle(flags):
     _compare(wl, gpu, run_oracle(wl))
 
 
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
 def test_key_shift_stress(flags):
     # scores shifted by a large common offset exercise the running-maximum rescaling
     rng = np.random.default_rng(43)

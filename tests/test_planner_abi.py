@@ -219,3 +219,18 @@ def test_dkdv_variant_selection(ctx, q0, B, hq, hkv, dt, want):
     32-key group) pair is either wholly visible or wholly hidden."""
     meta = Meta(ctx, q0, [[1], [0, 2]], B, hq, hkv, 64, dt)
     assert b.Plan(meta).kernel_names(True) == ["bwd_pre", want, "dq"]
+
+
+def test_transposed_v_copy_only_where_it_pays():
+    """The V transpose pre-pass is planned when the forward reads each V tile
+    several times (packed replay), not for one short query over a long arena
+    (denoising step), unless forced; FWD_DIRECT always wins."""
+    step = config_meta(2, np.random.default_rng(2))
+    replay = config_meta(3, np.random.default_rng(3))
+    assert "transpose_v" not in b.Plan(step).kernel_names(False)
+    assert "transpose_v" in b.Plan(step, b.FLAG_FWD_VT).kernel_names(False)
+    assert "transpose_v" in b.Plan(replay).kernel_names(False)
+    assert "transpose_v" not in b.Plan(replay, b.FLAG_FWD_DIRECT | b.FLAG_FWD_VT).kernel_names(False)
+    # block sizes that are not a multiple of 8 never take it
+    odd = Meta([96, 60], [0, 60], [[1], [0, 2]], 12, 8, 2, 64, "bf16")
+    assert "transpose_v" not in b.Plan(odd, b.FLAG_FWD_VT).kernel_names(False)
