@@ -254,7 +254,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const SwLane<D> lo(lane);
   const int4 itv = ld_rec4(a.bwd_items, blockIdx.x);
   if (itv.x < 0) return;
-  const int kvh = itv.y;
+  const int kvh = itv.y % a.hkv;
+  const int slot = itv.y / a.hkv - 1;                   // partial slot of a split tile, or -1
   const KTile kt = load_ktile(a.ktiles, itv.x);
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
@@ -274,7 +275,10 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int qct = QC / G;                               // tokens per chunk
   const int nc0 = (kt.cq_len + qct - 1) / qct;
   const int cpc = (B + qct - 1) / qct;
-  const int nchunks = nc0 + kt.cv_count * cpc;
+  const int nall = nc0 + kt.cv_count * cpc;             // chunks that may see the tile
+  // this item's part of them, in visiting order: [c0, c0 + nchunks)
+  const int c0 = min(itv.z, nall);
+  const int nchunks = min(itv.w, nall) - c0;
 
   // Chunks are visited from the last one back: every key tile of a segment ends
   // its query range at the same place, so tiles running at the same time start on
@@ -291,7 +295,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // LSE and delta per row, and (masked kernel) row limits. Rows past the chunk's
   // end read its last row. Waves 0 and 1 issue one load more than 2 and 3.
   auto issue = [&](int c, bf16* dQ_, bf16* dG_, float* dL_, float* dD_, int* dM_) {
-    const ChunkGeom g = chunk_geom(kt, a.canvq, nchunks - 1 - c, nc0, cpc, qct);
+    const ChunkGeom g = chunk_geom(kt, a.canvq, nall - 1 - (c0 + c), nc0, cpc, qct);
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
     const int64_t row0 = (int64_t)g.tok0 * a.hq + kvh * G;
     const int last = ((nrows - 1) / G) * a.hq + (nrows - 1) % G;   // uniform
@@ -339,7 +343,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
     lds_barrier();                                      // chunk c visible; stage of c-1 free
     if (c + 2 < nchunks) issue(c + 2, nQ, nG, nL, nD, nM);
-    const ChunkGeom g = chunk_geom(kt, a.canvq, nchunks - 1 - c, nc0, cpc, qct);
+    const ChunkGeom g = chunk_geom(kt, a.canvq, nall - 1 - (c0 + c), nc0, cpc, qct);
     const int nrows = g.ntok * G;
     // row limits of the two 32-row halves (clean limits grow with the row)
     // row limits of the first and the last valid row (clean limits grow with the row)
@@ -360,7 +364,24 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     if (c + 2 < nchunks) step(c + 2, sQ2, sG2, sL2, sD2, sM2, sQ1, sG1, sL1, sD1, sM1);
   }
 
-  if (key_ok) {
+  if (key_ok && slot >= 0) {                            // part of a split tile: fp32 partials
+    float* pk = a.dkv_part + ((int64_t)slot * 2 * kKBlock + kidx) * D;
+    float* pv = pk + (int64_t)kKBlock * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 kx, vx;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kx[e] = dkt[db][g4 * 4 + e];
+          vx[e] = dvt[db][g4 * 4 + e];
+        }
+        const int d0 = db * 32 + g4 * 8 + h * 4;
+        *reinterpret_cast<f32x4*>(pk + d0) = kx;
+        *reinterpret_cast<f32x4*>(pv + d0) = vx;
+      }
+  } else if (key_ok) {
     bf16* dkp = static_cast<bf16*>(a.dk) + krow * D;
     bf16* dvp = static_cast<bf16*>(a.dv) + krow * D;
 #pragma unroll
@@ -378,6 +399,33 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
         *reinterpret_cast<u32x2*>(dvp + d0) = u32x2{pack_bf16x2(vx[0], vx[1]), pack_bf16x2(vx[2], vx[3])};
       }
   }
+}
+
+// ---------------------------------------------------------------- dK/dV merge
+// Sums the fp32 partial dK/dV of a split key tile in slot order, applies the
+// softmax scale to dK and writes both in bf16. Workgroup: 256 threads, each four
+// consecutive dimensions of one key; (kKBlock * D / 4) / 256 workgroups per tile.
+template <int D>
+__global__ void __launch_bounds__(256) dkdv_merge_kernel(BwdArgs a) {
+  constexpr int Q4 = D / 4;
+  constexpr int WG_PER = kKBlock * Q4 / 256;
+  const int4 mv = ld_rec4(a.bmerge, blockIdx.x / WG_PER);
+  const KTile kt = load_ktile(a.ktiles, mv.x);
+  const int idx = (blockIdx.x % WG_PER) * 256 + threadIdx.x;
+  const int key = idx / Q4, d0 = (idx % Q4) * 4;
+  if (key >= kt.n_keys) return;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < mv.w; ++i) {
+    const float* pk = a.dkv_part + ((int64_t)(mv.z + i) * 2 * kKBlock + key) * D + d0;
+    sk += *reinterpret_cast<const f32x4*>(pk);
+    sv += *reinterpret_cast<const f32x4*>(pk + (int64_t)kKBlock * D);
+  }
+  const int64_t krow = (int64_t)(kt.k_tok + key) * a.hkv + mv.y;
+  bf16* dkp = static_cast<bf16*>(a.dk) + krow * D + d0;
+  bf16* dvp = static_cast<bf16*>(a.dv) + krow * D + d0;
+  *reinterpret_cast<u32x2*>(dkp) = u32x2{pack_bf16x2(sk[0] * a.scale, sk[1] * a.scale),
+                                         pack_bf16x2(sk[2] * a.scale, sk[3] * a.scale)};
+  *reinterpret_cast<u32x2*>(dvp) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
 }
 
 // ---------------------------------------------------------------- dQ
@@ -536,6 +584,15 @@ hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, bool masked, int gri
     if (masked) hipLaunchKernelGGL((dkdv_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((dkdv_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv_merge(const BwdArgs& a, int head_dim, int n_merge, hipStream_t s) {
+  if (n_merge <= 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(dkdv_merge_kernel<128>, dim3(n_merge * (kKBlock * 32 / 256)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(dkdv_merge_kernel<64>, dim3(n_merge * (kKBlock * 16 / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

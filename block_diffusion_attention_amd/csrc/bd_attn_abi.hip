@@ -50,11 +50,13 @@ int fwd_kernels(const Plan& p) {
   const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
   return 1 + (bf16 && p.use_vt ? 1 : 0) + (bf16 && p.split ? 1 : 0);
 }
+int bwd_kernels(const Plan& p) { return p.bwd_merge.empty() ? 3 : 4; }
 const char* kernel_name(const Plan& p, bool backward, int i) {
-  static const char* const bwd[] = {"bwd_pre", "dkdv", "dq"};
   if (backward) {
-    if (i == 1 && p.desc.dtype == BD_ATTN_BF16 && p.dkdv_masked) return "dkdv_masked";
-    return (i >= 0 && i < 3) ? bwd[i] : nullptr;
+    if (i < 0 || i >= bwd_kernels(p)) return nullptr;
+    if (i == 0) return "bwd_pre";
+    if (i == 1) return p.desc.dtype == BD_ATTN_BF16 && p.dkdv_masked ? "dkdv_masked" : "dkdv";
+    return (i == 2 && !p.bwd_merge.empty()) ? "dkdv_merge" : "dq";
   }
   if (i < 0 || i >= fwd_kernels(p)) return nullptr;
   const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
@@ -210,7 +212,9 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
                                void* const* events, int n_events) {
   if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
   const Plan& p = plan->p;
-  if (events && n_events < 4) return fail(BD_ATTN_EINVAL, "n_events must be at least 4 for the backward pass");
+  const int nk = bwd_kernels(p);
+  if (events && n_events < nk + 1)
+    return fail(BD_ATTN_EINVAL, "n_events must be at least bd_attn_plan_kernels(plan, 1) + 1");
   bd_attn_status st;
   if ((st = check_ptr(meta_dev, "meta_dev")) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
       (st = check_ptr(v, "v")) || (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")) ||
@@ -232,6 +236,8 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.delta = static_cast<float*>(ws);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_lse2);
+  a.dkv_part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_dkv);
+  a.bmerge = section<bdattn::BwdMerge>(meta_dev, p.off_bmerge);
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.rows_q = p.tq * p.desc.num_q_heads;
   a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.B = p.desc.block_size;
@@ -245,10 +251,16 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
            : bdattn::launch_dkdv_f32(a, D, (int)p.bwd_items.size(), s);
   if ((st = hip_status(e, "dkdv launch"))) return st;
   if ((st = hip_status(ev.mark(2), "hipEventRecord"))) return st;
+  int mk = 3;
+  if (!p.bwd_merge.empty()) {                           // bf16 plans only
+    e = bdattn::launch_dkdv_merge(a, D, (int)p.bwd_merge.size(), s);
+    if ((st = hip_status(e, "dkdv merge launch"))) return st;
+    if ((st = hip_status(ev.mark(mk++), "hipEventRecord"))) return st;
+  }
   e = bf16 ? bdattn::launch_dq_bf16(a, D, (int)p.dq_items.size(), s)
            : bdattn::launch_dq_f32(a, D, (int)p.dq_items.size(), s);
   if ((st = hip_status(e, "dq launch"))) return st;
-  return hip_status(ev.mark(3), "hipEventRecord");
+  return hip_status(ev.mark(mk), "hipEventRecord");
 }
 
 bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
@@ -267,7 +279,7 @@ bd_attn_status bd_attn_bwd_timed(bd_attn_plan_t plan, const void* meta_dev, cons
 
 int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward) {
   if (!plan) return 0;
-  return backward ? 3 : fwd_kernels(plan->p);
+  return backward ? bwd_kernels(plan->p) : fwd_kernels(plan->p);
 }
 
 const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int32_t i) {

@@ -23,14 +23,20 @@ constexpr int kQRows = 128;
 constexpr int kKTile = 64;
 // dK/dV: keys per workgroup (4 waves of 32 keys each).
 constexpr int kKBlock = 128;
+// dK/dV workgroups resident at once (one per CU of a 256-CU device); the planner
+// splits key tiles whose chunk count is far above the per-workgroup average.
+constexpr int kDkdvResident = 256;
 // Largest supported group size (query heads per kv head).
 constexpr int kMaxGroup = 32;
 
 // Serialized plan: a header of kBlobHeaderInts int32 (magic, format version,
 // then count and int32 offset of each section: query tiles, forward items,
 // forward launch order, combine items, dQ items, key tiles, canvas-query
-// entries, dK/dV items), followed by the sections, each 16-byte aligned.
+// entries, dK/dV items, dK/dV merge items), followed by the sections, each
+// 16-byte aligned.
 constexpr int kBlobHeaderInts = 32;
+constexpr int kBlobVersion = 2;
+constexpr int kBlobSections = 9;
 constexpr int32_t kBlobMagic = 0x62646174;   // "bdat"
 
 struct QTile {         // 8 x int32
@@ -78,9 +84,17 @@ struct CanvasQ {       // 4 x int32
 
 struct BwdItem {       // 4 x int32: one workgroup of the dK/dV kernel
   int32_t ktile;       // index into the key-tile list, or -1 for an empty slot
+  int32_t kvh_slot;    // kv head + Hkv * (partial slot + 1); slot -1: the item covers
+                       // all of the tile's chunks and writes dK/dV itself
+  int32_t c_begin;     // chunk range [c_begin, min(c_end, chunks)) in visiting order
+  int32_t c_end;
+};
+
+struct BwdMerge {      // 4 x int32: sum of the partial dK/dV of one split key tile
+  int32_t ktile;
   int32_t kvh;
-  int32_t pad0;
-  int32_t pad1;
+  int32_t first;       // first partial slot
+  int32_t count;       // consecutive partial slots, summed in slot order
 };
 
 static_assert(sizeof(QTile) == 32, "QTile layout");

@@ -49,6 +49,8 @@ struct BwdArgs {
   const float* lse;
   float* delta;              // [Tq, Hq] fp32 (workspace)
   float* lse2;               // [Tq, Hq] fp32 (workspace): LSE * log2(e), written by bwd_pre
+  float* dkv_part;           // partial dK/dV slots (workspace): [slot][dK, dV][kKBlock][D] fp32
+  const BwdMerge* bmerge;    // merge items of the split key tiles
   void* dq;
   void* dk;
   void* dv;
@@ -63,6 +65,7 @@ hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int it
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, bool masked, int grid, hipStream_t s);
 hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_dkdv_merge(const BwdArgs& a, int head_dim, int n_merge, hipStream_t s);
 
 hipError_t launch_transpose_v(const void* v, void* vt, int tk, int tk_pad, int hkv, int head_dim, hipStream_t s);
 hipError_t launch_fwd_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s);

@@ -10,6 +10,7 @@
 #include "planner.h"
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <numeric>
@@ -336,14 +337,57 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
     }
   }
   {
+    // dK/dV items: one per (key tile, kv head), over the tile's 64-row query
+    // chunks (64/G tokens of one block each; the same count as the kernel's).
+    // The kernel runs one workgroup per CU. When a few key tiles see far more
+    // chunks than the average CU has to process (the first key tiles of one long
+    // context, which every later query sees), the bf16 plan splits their chunk
+    // ranges into parts of about that average; the parts write fp32 partial
+    // dK/dV that a merge kernel sums in part order (deterministic).
+    const int64_t qct = 64 / G;
+    const int64_t cpc = ceil_div(B, qct);
+    std::vector<int64_t> nch(p.ktiles.size());
+    int64_t total = 0;
+    for (size_t i = 0; i < p.ktiles.size(); ++i) {
+      nch[i] = ceil_div(p.ktiles[i].cq_len, qct) + (int64_t)p.ktiles[i].cv_count * cpc;
+      total += nch[i] * Hkv;
+    }
+    const bool can_split = d->dtype == BD_ATTN_BF16 && !(d->flags & BD_ATTN_FLAG_NO_SPLIT);
+    const bool force = (d->flags & BD_ATTN_FLAG_FORCE_SPLIT) != 0;
+    // parts of at most 3/4 of the per-workgroup average: the largest-cost-first
+    // order then packs them with a short tail (0.89 of the ideal on the staircase
+    // workload, against 0.53 unsplit)
+    const int64_t cap = std::max<int64_t>(ceil_div(3 * total, 4 * kDkdvResident), 16);
+    auto parts_of = [&](int64_t n) -> int64_t {
+      if (!can_split || n < 2) return 1;
+      if (force) return 2;
+      return n > cap ? ceil_div(n, cap) : 1;
+    };
     std::vector<BwdItem> raw;
     std::vector<int64_t> cost, cls;
-    for (size_t i = 0; i < p.ktiles.size(); ++i)
+    p.bwd_merge.clear();
+    int64_t slots = 0;
+    for (size_t i = 0; i < p.ktiles.size(); ++i) {
+      const int64_t n = nch[i], np = parts_of(n);
       for (int h = 0; h < Hkv; ++h) {
-        raw.push_back(BwdItem{(int32_t)i, h, 0, 0});
-        cost.push_back(ceil_div(kcost[i], 8) + 1);
-        cls.push_back((int64_t)ktile_seg[i] * Hkv + h);
+        if (np == 1) {
+          raw.push_back(BwdItem{(int32_t)i, h, 0, INT32_MAX});
+          cost.push_back(n + 1);
+          cls.push_back((int64_t)ktile_seg[i] * Hkv + h);
+          continue;
+        }
+        p.bwd_merge.push_back(BwdMerge{(int32_t)i, h, (int32_t)slots, (int32_t)np});
+        for (int64_t k = 0; k < np; ++k) {
+          const int64_t c0 = n * k / np, c1 = n * (k + 1) / np;
+          raw.push_back(BwdItem{(int32_t)i, (int32_t)(h + (int64_t)Hkv * (slots + k + 1)), (int32_t)c0, (int32_t)c1});
+          cost.push_back(c1 - c0 + 1);
+          cls.push_back((int64_t)ktile_seg[i] * Hkv + h);
+        }
+        slots += np;
       }
+    }
+    p.n_dkv_slots = slots;
+    if ((int64_t)Hkv * (slots + 1) + Hkv > INT32_MAX) { *err = "too many dK/dV partial slots"; return BD_ATTN_EUNSUPPORTED; }
     auto ord = launch_order(cost, cls, xcd);
     for (int32_t o : ord) p.bwd_items.push_back(o < 0 ? BwdItem{-1, 0, 0, 0} : raw[o]);
   }
@@ -359,17 +403,20 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   append_records(p.blob, p.ktiles, p.off_ktiles);
   append_records(p.blob, p.canvq, p.off_canvq);
   append_records(p.blob, p.bwd_items, p.off_bwd);
+  append_records(p.blob, p.bwd_merge, p.off_bmerge);
   while (p.blob.size() % 4) p.blob.push_back(0);
   {
     int32_t* hd = p.blob.data();
     hd[0] = kBlobMagic;
-    hd[1] = 1;
-    const int64_t cnt[8] = {(int64_t)p.qtiles.size(), (int64_t)p.fwd_items.size(), (int64_t)p.fwd_order.size(),
-                            (int64_t)p.comb_items.size(), (int64_t)p.dq_items.size(), (int64_t)p.ktiles.size(),
-                            (int64_t)p.canvq.size(), (int64_t)p.bwd_items.size()};
-    const int64_t off[8] = {p.off_qtiles, p.off_fwd, p.off_fwd_order, p.off_comb, p.off_dq, p.off_ktiles,
-                            p.off_canvq, p.off_bwd};
-    for (int i = 0; i < 8; ++i) { hd[2 + 2 * i] = (int32_t)cnt[i]; hd[3 + 2 * i] = (int32_t)off[i]; }
+    hd[1] = kBlobVersion;
+    const int64_t cnt[kBlobSections] = {
+        (int64_t)p.qtiles.size(), (int64_t)p.fwd_items.size(), (int64_t)p.fwd_order.size(),
+        (int64_t)p.comb_items.size(), (int64_t)p.dq_items.size(), (int64_t)p.ktiles.size(),
+        (int64_t)p.canvq.size(), (int64_t)p.bwd_items.size(), (int64_t)p.bwd_merge.size()};
+    const int64_t off[kBlobSections] = {p.off_qtiles, p.off_fwd, p.off_fwd_order, p.off_comb, p.off_dq,
+                                        p.off_ktiles, p.off_canvq, p.off_bwd, p.off_bmerge};
+    static_assert(2 + 2 * kBlobSections <= kBlobHeaderInts, "blob header too small");
+    for (int i = 0; i < kBlobSections; ++i) { hd[2 + 2 * i] = (int32_t)cnt[i]; hd[3 + 2 * i] = (int32_t)off[i]; }
   }
 
   const int64_t D = d->head_dim;
@@ -407,7 +454,8 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
     p.dkdv_masked = !aligned;
   }
   p.off_ws_lse2 = ceil_div(tq * Hq * 4, 256) * 256;          // delta [Tq, Hq] fp32, then LSE*log2(e)
-  p.ws_bwd = (size_t)(2 * p.off_ws_lse2);
+  p.off_ws_dkv = 2 * p.off_ws_lse2;                          // then the partial dK/dV slots
+  p.ws_bwd = (size_t)(p.off_ws_dkv + p.n_dkv_slots * 2 * kKBlock * D * 4);
   return BD_ATTN_OK;
 }
 

@@ -27,10 +27,12 @@ struct Plan {
   std::vector<KTile> ktiles;
   std::vector<CanvasQ> canvq;
   std::vector<BwdItem> bwd_items;    // launch order
+  std::vector<BwdMerge> bwd_merge;   // split key tiles
+  int64_t n_dkv_slots = 0;           // partial dK/dV slots of the split key tiles
 
   std::vector<int32_t> blob;         // device metadata image
   int64_t off_qtiles = 0, off_fwd = 0, off_fwd_order = 0, off_comb = 0, off_dq = 0,
-          off_ktiles = 0, off_canvq = 0, off_bwd = 0;   // int32 offsets into blob
+          off_ktiles = 0, off_canvq = 0, off_bwd = 0, off_bmerge = 0;   // int32 offsets into blob
   size_t ws_fwd = 0, ws_bwd = 0;
   bool use_vt = false;               // bf16 forward through the transposed V copy (B % 8 == 0)
   bool dkdv_masked = true;           // dK/dV needs per-score row limits (see build_plan)
@@ -39,6 +41,7 @@ struct Plan {
   int64_t off_ws_part = 0;           // partial O,
   int64_t off_ws_lse = 0;            // partial LSE
   int64_t off_ws_lse2 = 0;           // byte offset of LSE*log2(e) in the backward workspace
+  int64_t off_ws_dkv = 0;            // byte offset of the partial dK/dV slots (fp32)
 };
 
 // Validates desc and fills *plan. On error returns a non-OK status and sets *err.

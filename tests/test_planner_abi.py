@@ -112,8 +112,38 @@ def _check_plan(meta, flags=0):
     # launch lists: every (tile, kv head) exactly once, empty slots marked -1
     dq = [tuple(x[:2]) for x in rec["dq"] if x[0] >= 0]
     assert sorted(dq) == sorted(itertools.product(range(nq), range(hkv)))
-    bw = [tuple(x[:2]) for x in rec["bwd"] if x[0] >= 0]
-    assert sorted(bw) == sorted(itertools.product(range(nk), range(hkv)))
+    # dK/dV items: every (key tile, kv head) once, either whole or split into
+    # parts whose chunk ranges tile [0, chunks) in slot order, listed by one
+    # merge record
+    qct = 64 // G
+    cpc = -(-meta.block_size // qct)
+
+    def chunks(i):
+        t = rec["ktiles"][i]
+        return -(-t[4] // qct) + t[7] * cpc
+
+    whole, parts = [], {}
+    for ktile, ys, c0, c1 in rec["bwd"]:
+        if ktile < 0:
+            continue
+        h, slot = ys % hkv, ys // hkv - 1
+        if slot < 0:
+            assert c0 == 0 and c1 >= chunks(ktile)
+            whole.append((int(ktile), int(h)))
+        else:
+            assert slot not in parts
+            parts[int(slot)] = (int(ktile), int(h), int(c0), int(c1))
+    merged = []
+    for ktile, h, first, count in rec["bmerge"]:
+        spans = [parts[s] for s in range(first, first + count)]
+        assert all(sp[:2] == (ktile, h) for sp in spans)
+        assert spans[0][2] == 0 and spans[-1][3] == chunks(ktile)
+        assert all(a_[3] == b_[2] and a_[3] > a_[2] for a_, b_ in zip(spans, spans[1:]))
+        merged.append((int(ktile), int(h)))
+    assert len(parts) == sum(int(c) for *_, c in rec["bmerge"])
+    assert sorted(whole + merged) == sorted(itertools.product(range(nk), range(hkv)))
+    if meta.dtype != "bf16" or flags & b.FLAG_NO_SPLIT:
+        assert len(rec["bmerge"]) == 0
     if len(rec["comb"]) == 0:
         fw = [tuple(x[:2]) for x in rec["fwd"] if x[0] >= 0]
         assert sorted(fw) == sorted(dq)
@@ -218,7 +248,8 @@ def test_dkdv_variant_selection(ctx, q0, B, hq, hkv, dt, want):
     """The unmasked dK/dV program is only chosen when every (64-row query chunk,
     32-key group) pair is either wholly visible or wholly hidden."""
     meta = Meta(ctx, q0, [[1], [0, 2]], B, hq, hkv, 64, dt)
-    assert b.Plan(meta).kernel_names(True) == ["bwd_pre", want, "dq"]
+    names = b.Plan(meta).kernel_names(True)
+    assert names[0] == "bwd_pre" and names[1] == want and names[-1] == "dq"
 
 
 def test_transposed_v_copy_only_where_it_pays():
@@ -234,3 +265,23 @@ def test_transposed_v_copy_only_where_it_pays():
     # block sizes that are not a multiple of 8 never take it
     odd = Meta([96, 60], [0, 60], [[1], [0, 2]], 12, 8, 2, 64, "bf16")
     assert "transpose_v" not in b.Plan(odd, b.FLAG_FWD_VT).kernel_names(False)
+
+
+def test_dkdv_split_of_long_key_tiles():
+    """One long context (the staircase shape): its first key tiles see far more
+    query chunks than the average workgroup, so their ranges are split and
+    merged; the packed replay is balanced without splitting. FORCE_SPLIT splits
+    every multi-chunk item, NO_SPLIT none."""
+    stair = config_meta(4, np.random.default_rng(4))
+    p = b.Plan(stair)
+    assert p.kernel_names(True)[2] == "dkdv_merge"
+    rec = decode(p.host_blob())
+    assert len(rec["bmerge"]) > 0
+    assert "dkdv_merge" not in b.Plan(stair, b.FLAG_NO_SPLIT).kernel_names(True)
+    replay = config_meta(3, np.random.default_rng(3))
+    assert "dkdv_merge" not in b.Plan(replay).kernel_names(True)
+    small = Meta([96, 64], [0, 64], [[2, 0, 3], [4]], 16, 8, 2, 64, "bf16")
+    _check_plan(small, b.FLAG_FORCE_SPLIT)
+    _check_plan(small, b.FLAG_NO_SPLIT)
+    f32 = Meta([96, 64], [0, 64], [[2, 0, 3], [4]], 16, 8, 2, 64, "fp32")
+    _check_plan(f32, b.FLAG_FORCE_SPLIT)
