@@ -1,14 +1,17 @@
 // Backward staircase block-diffusion attention for gfx950 (bf16 in, fp32 accumulate).
 //
-// Three deterministic kernels, no atomics (ORL paper, appendix D.2 paragraph
-// on the kernel: the backward pass uses the same visibility, dQ follows the
-// query traversal and dK/dV derive the valid query ranges of each key tile):
-//   bwd_pre : delta = rowsum(dO * O) per (token, query head), fp32, and the
-//             LSE in the log2 domain;
-//   dkdv    : one workgroup per (key tile of up to 128 keys, kv head), looping
-//             over the 64-row query chunks that can see the tile;
-//   dq      : one workgroup per (query tile, kv head), looping over the same key
-//             tiles as the forward pass.
+// Deterministic kernels, no atomics (ORL paper, appendix D.2 paragraph on the
+// kernel: the backward pass uses the same visibility, dQ follows the query
+// traversal and dK/dV derive the valid query ranges of each key tile), in
+// launch order:
+//   dq         : one workgroup per (query tile, kv head), looping over the same
+//                key tiles as the forward pass; it also writes the row terms
+//                delta = rowsum(dO * O) and LSE * log2(e) of its rows;
+//   dkdv       : one workgroup per (key tile of up to 128 keys, kv head), looping
+//                over the 64-row query chunks that can see the tile (or a
+//                contiguous part of them);
+//   dkdv_merge : sums the partial dK/dV of split key tiles in part order.
+// (bwd_pre computes the row terms on their own for the fp32 path.)
 // Gradients of L = <dO, O>: dp = dO V^T, ds = p (dp - delta), dQ = scale ds K,
 // dK = scale ds^T Q, dV = p^T dO (dK, dV summed over the heads of a kv group).
 #include "kcommon.h"
@@ -430,7 +433,8 @@ __global__ void __launch_bounds__(256) dkdv_merge_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dQ
 // Workgroup: one query tile (up to 128 rows) and one kv head, over the same key
-// tiles as the forward pass. Per wave 32 rows; scores transposed as in the
+// tiles as the forward pass. It also computes and stores the row terms (delta,
+// LSE * log2(e)) that the dK/dV kernel reads, so it runs first. Per wave 32 rows; scores transposed as in the
 // forward pass. K and V tiles go straight into LDS (two stages); K^T for
 // dQ^T = K^T dS^T is read with the LDS transpose read.
 template <int D>
@@ -485,8 +489,29 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
     qf[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow * D + kk * 16 + h * 8);
     df[kk] = *reinterpret_cast<const bf16x8*>(dO + qrow * D + kk * 16 + h * 8);
   }
+  // Row terms of the wave's rows: delta = rowsum(dO * O) (each lane half holds
+  // half of the row) and LSE * log2(e). Stored for the dK/dV kernel, which runs
+  // after this one; every row belongs to exactly one dQ item.
+  float dl = 0.f;
+  {
+    const bf16* orow = static_cast<const bf16*>(a.o) + qrow * D + h * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) {
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(orow + kk * 16);
+      const u32x4 gv = __builtin_bit_cast(u32x4, df[kk]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dl += __builtin_bit_cast(float, ov[w] << 16) * __builtin_bit_cast(float, gv[w] << 16);
+        dl += __builtin_bit_cast(float, ov[w] & 0xffff0000u) * __builtin_bit_cast(float, gv[w] & 0xffff0000u);
+      }
+    }
+    dl += swap_halves(dl);
+  }
   const float lse2 = a.lse[qrow] * kLog2e;
-  const float dl = a.delta[qrow];
+  if (row_ok && h == 0) {
+    a.delta[qrow] = dl;
+    a.lse2[qrow] = lse2;
+  }
 
   f32x16 acc[NDB];
 #pragma unroll

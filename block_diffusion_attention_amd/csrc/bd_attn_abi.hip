@@ -50,13 +50,21 @@ int fwd_kernels(const Plan& p) {
   const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
   return 1 + (bf16 && p.use_vt ? 1 : 0) + (bf16 && p.split ? 1 : 0);
 }
-int bwd_kernels(const Plan& p) { return p.bwd_merge.empty() ? 3 : 4; }
+// bf16: dQ (which also writes the row terms), dK/dV, [merge of split key tiles];
+// fp32: row terms, dK/dV, dQ.
+int bwd_kernels(const Plan& p) {
+  return p.desc.dtype == BD_ATTN_BF16 ? (p.bwd_merge.empty() ? 2 : 3) : 3;
+}
 const char* kernel_name(const Plan& p, bool backward, int i) {
   if (backward) {
     if (i < 0 || i >= bwd_kernels(p)) return nullptr;
-    if (i == 0) return "bwd_pre";
-    if (i == 1) return p.desc.dtype == BD_ATTN_BF16 && p.dkdv_masked ? "dkdv_masked" : "dkdv";
-    return (i == 2 && !p.bwd_merge.empty()) ? "dkdv_merge" : "dq";
+    if (p.desc.dtype != BD_ATTN_BF16) {
+      static const char* const f32[] = {"bwd_pre", "dkdv", "dq"};
+      return f32[i];
+    }
+    if (i == 0) return "dq";
+    if (i == 1) return p.dkdv_masked ? "dkdv_masked" : "dkdv";
+    return "dkdv_merge";
   }
   if (i < 0 || i >= fwd_kernels(p)) return nullptr;
   const bool bf16 = p.desc.dtype == BD_ATTN_BF16;
@@ -244,23 +252,28 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
   if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
-  hipError_t e = bdattn::launch_bwd_pre(a, D, bf16, s);
-  if ((st = hip_status(e, "bwd_pre launch"))) return st;
-  if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
-  e = bf16 ? bdattn::launch_dkdv_bf16(a, D, p.dkdv_masked, (int)p.bwd_items.size(), s)
-           : bdattn::launch_dkdv_f32(a, D, (int)p.bwd_items.size(), s);
-  if ((st = hip_status(e, "dkdv launch"))) return st;
-  if ((st = hip_status(ev.mark(2), "hipEventRecord"))) return st;
-  int mk = 3;
-  if (!p.bwd_merge.empty()) {                           // bf16 plans only
+  hipError_t e;
+  if (bf16) {
+    e = bdattn::launch_dq_bf16(a, D, (int)p.dq_items.size(), s);
+    if ((st = hip_status(e, "dq launch"))) return st;
+    if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
+    e = bdattn::launch_dkdv_bf16(a, D, p.dkdv_masked, (int)p.bwd_items.size(), s);
+    if ((st = hip_status(e, "dkdv launch"))) return st;
+    if ((st = hip_status(ev.mark(2), "hipEventRecord"))) return st;
+    if (p.bwd_merge.empty()) return BD_ATTN_OK;
     e = bdattn::launch_dkdv_merge(a, D, (int)p.bwd_merge.size(), s);
     if ((st = hip_status(e, "dkdv merge launch"))) return st;
-    if ((st = hip_status(ev.mark(mk++), "hipEventRecord"))) return st;
+    return hip_status(ev.mark(3), "hipEventRecord");
   }
-  e = bf16 ? bdattn::launch_dq_bf16(a, D, (int)p.dq_items.size(), s)
-           : bdattn::launch_dq_f32(a, D, (int)p.dq_items.size(), s);
+  e = bdattn::launch_bwd_pre(a, D, bf16, s);
+  if ((st = hip_status(e, "bwd_pre launch"))) return st;
+  if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
+  e = bdattn::launch_dkdv_f32(a, D, (int)p.bwd_items.size(), s);
+  if ((st = hip_status(e, "dkdv launch"))) return st;
+  if ((st = hip_status(ev.mark(2), "hipEventRecord"))) return st;
+  e = bdattn::launch_dq_f32(a, D, (int)p.dq_items.size(), s);
   if ((st = hip_status(e, "dq launch"))) return st;
-  return hip_status(ev.mark(mk), "hipEventRecord");
+  return hip_status(ev.mark(3), "hipEventRecord");
 }
 
 bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,

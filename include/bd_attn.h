@@ -141,7 +141,8 @@ bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev,
  * Writes (does not accumulate) dq [Tq,Hq,D], dk and dv [Tk,Hkv,D]; dK and dV
  * are summed over the query heads of each kv head. Deterministic: no atomics,
  * bitwise identical across runs. ws: ws_bwd_bytes of device memory (holds the
- * float32 row terms delta = rowsum(dO * O) and LSE * log2(e), [Tq, Hq] each).
+ * float32 row terms delta = rowsum(dO * O) and LSE * log2(e), [Tq, Hq] each, and
+ * for plans that split dK/dV key tiles the float32 partial dK/dV of the parts).
  * Errors as bd_attn_fwd. */
 bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev,
                            const void* q, const void* k, const void* v,
@@ -154,9 +155,10 @@ bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev,
  * kernel and events[i] right after the i-th one. The forward pass launches 1 to
  * 3 kernels (V transpose on the pipelined path, the attention kernel, and the
  * merge of partial results on the split path; bd_attn_plan_kernels(plan, 0) and
- * bd_attn_plan_kernel_name give the count and names), the backward pass 3
- * (delta = rowsum(dO * O), dK/dV, dQ). n_events must be at least kernels + 1,
- * else EINVAL and nothing is enqueued. */
+ * bd_attn_plan_kernel_name give the count and names), the backward pass 2 or 3
+ * in bf16 (dQ, which also computes delta = rowsum(dO * O); dK/dV; the merge of
+ * split key tiles when the plan splits them) and 3 in fp32 (delta, dK/dV, dQ).
+ * n_events must be at least kernels + 1, else EINVAL and nothing is enqueued. */
 bd_attn_status bd_attn_fwd_timed(bd_attn_plan_t plan, const void* meta_dev,
                                  const void* q, const void* k, const void* v,
                                  void* o, float* lse, void* ws, bd_attn_stream_t stream,
@@ -173,7 +175,7 @@ int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward);
 
 /* Short name of the i-th kernel (0-based, launch order) that bd_attn_fwd
  * (backward = 0) or bd_attn_bwd (backward = 1) launches for this plan, e.g.
- * "transpose_v", "fwd", "combine", "bwd_pre", "dkdv", "dq"; NULL when i is out of
+ * "transpose_v", "fwd", "combine", "bwd_pre", "dq", "dkdv", "dkdv_merge"; NULL when i is out of
  * range or the plan is NULL. "dkdv_masked" names the bf16 dK/dV kernel that
  * applies a row limit to every score: plans whose query chunks are not all either
  * seen whole by a 32-key group or not at all (block size not a multiple of 32,
