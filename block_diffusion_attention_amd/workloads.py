@@ -185,8 +185,9 @@ def random_meta(rng, *, max_segments=3, max_blocks=5, block_sizes=(1, 2, 3, 4), 
     return Meta(ctx, q0s, cvs, B, hq, hkv, d, dtype)
 
 
-def random_workload(rng, meta: Meta, sigma: float = 1.0, with_do: bool = True, name="random") -> Workload:
-    q, k, v, do = draw_tensors(meta, rng, sigma, with_do)
+def random_workload(rng, meta: Meta, sigma: float = 1.0, with_do: bool = True, name="random",
+                    do_sigma: float = 1.0) -> Workload:
+    q, k, v, do = draw_tensors(meta, rng, sigma, with_do, do_sigma)
     return Workload(name, meta, q, k, v, do, "fwd+bwd" if with_do else "fwd")
 
 

@@ -165,6 +165,9 @@ CASES = [
     (64, 4, 1, 128, "bf16", 0.3),
     (256, 8, 2, 128, "bf16", 0.2),
     (3, 6, 2, 64, "bf16", 0.5),          # group size 3
+    (32, 16, 2, 128, "bf16", 0.3),       # group size 8: 8 tokens per 64-row chunk
+    (16, 32, 2, 64, "bf16", 0.3),        # group size 16
+    (8, 32, 1, 128, "bf16", 0.3),        # group size 32: 4 tokens per query tile
     (8, 4, 2, 64, "fp32", 1.0),
     (32, 4, 1, 128, "fp32", 0.5),
 ]
@@ -179,7 +182,11 @@ def test_random_packs(case, seed, flags):
     max_blocks = max(2, min(12, 600 // B))
     meta = W.random_meta(rng, max_segments=3, max_blocks=max_blocks, block_sizes=(B,), max_canvases=4,
                          hq=hq, hkv=hkv, d=D, dtype=dt)
-    wl = W.random_workload(rng, meta, sigma=sigma)
+    # dK and dV sum G query heads: with unit dO their magnitude grows as sqrt(G), and
+    # beyond |x| ~ 8 the bf16 rounding of the output alone exceeds the 2e-2 bar.
+    # Groups above 4 draw dO at sqrt(4/G), i.e. the gradient scale of 4 heads.
+    G = hq // hkv
+    wl = W.random_workload(rng, meta, sigma=sigma, do_sigma=min(1.0, (4.0 / G) ** 0.5))
     _say(f"case random B={B} hq={hq} hkv={hkv} D={D} {dt} seed={seed} flags={flags} tq={meta.tq} tk={meta.tk}")
     gpu, _ = run_gpu(wl, flags=flags)
     _compare(wl, gpu, run_oracle(wl))
@@ -192,6 +199,7 @@ def test_forced_split_matches_oracle(flags):
     wl = W.random_workload(rng, meta, sigma=0.3)
     gpu, plan = run_gpu(wl, flags=b.FLAG_FORCE_SPLIT | flags)
     assert "combine" in plan.kernel_names(False)
+    assert "dkdv_merge" in plan.kernel_names(True), "FORCE_SPLIT also splits the dK/dV key tiles"
     _compare(wl, gpu, run_oracle(wl))
 
 
