@@ -12,8 +12,9 @@
 // the 32x32x16 MFMA so that each lane owns one query row: row maxima and sums
 // need one cross-half exchange instead of a 32-lane reduction, and the
 // probabilities feed the P V product straight from registers. K and V tiles go
-// from global memory straight into LDS (global_load_lds, two pipeline stages,
-// no register staging); the V^T operand is read with the LDS transpose read.
+// from global memory straight into swizzled row-major LDS tiles (two pipeline
+// stages, no register staging); the V^T operand is read with the LDS transpose
+// read.
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -36,7 +37,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
-  const CmLane lo(lane);
+  const SwLane<D> lo(lane);
   const int idx = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
   const int4 itv = reinterpret_cast<const int4*>(a.items)[idx];
   if (itv.x < 0) return;
@@ -58,14 +59,16 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int n1 = (qt.lim_max + KT - 1) / KT;
   const int64_t kv_stride = (int64_t)a.hkv * D;
 
+  // K and V tiles: 64 key rows at stride Hkv*D, swizzled row-major in LDS
+  const SwFetch<D> fetch([&](int r) { return r * (int)kv_stride; }, wave, lane);
   auto issue = [&](int kt, bf16* dK, bf16* dV) {
     int base, nvalid;
     if (kt < n1) { base = qt.k_ctx + kt * KT; nvalid = min(KT, qt.lim_max - kt * KT); }
     else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
-    const bf16* kb = K + (int64_t)base * kv_stride + kvh * D;
-    const bf16* vb = V + (int64_t)base * kv_stride + kvh * D;
-    tile_fetch<D>(dK, [&](int r) { return kb + r * kv_stride; }, nvalid, wave, lane);
-    tile_fetch<D>(dV, [&](int r) { return vb + r * kv_stride; }, nvalid, wave, lane);
+    const int64_t off0 = (int64_t)base * kv_stride + kvh * D;
+    const int last = (nvalid - 1) * (int)kv_stride;
+    fetch.issue(dK, K + off0, nvalid, last, wave);
+    fetch.issue(dV, V + off0, nvalid, last, wave);
   };
   issue(kt_begin, sK0, sV0);
 
@@ -97,7 +100,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
       s[kb] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKS; ++kk)
-        s[kb] = mfma32(cm_row8(sK, lo, kb * 32, kk), qf[kk], s[kb]);
+        s[kb] = mfma32(sw_row8<D>(sK, lo, kb * 32, kk), qf[kk], s[kb]);
     }
 
     // masking only on tiles that cross a row limit or the end of a range
@@ -150,7 +153,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq)
-        acc[db] = mfma32(cm_tr8(sV, lo, kq * 16, db * 32), pb[kq], acc[db]);
+        acc[db] = mfma32(sw_tr8<D>(sV, lo, kq * 16, db * 32), pb[kq], acc[db]);
   };
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
     step(kt, sK0, sV0, sK1, sV1);

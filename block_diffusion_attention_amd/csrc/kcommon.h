@@ -105,19 +105,7 @@ __device__ __forceinline__ uint32_t pick_pair(uint32_t x, uint32_t y, int odd) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// LDS tiles filled straight from global memory, chunk-major. A tile holds 64
-// rows of D bf16 as 16-byte chunks; chunk c of row r sits in 16-byte slot
-//   c * 64 + (r ^ (4 * (c & 3)))
-// i.e. every chunk column is 1 KiB and rows are XOR-permuted inside aligned
-// groups of 16. global_load_lds (16 bytes per lane) writes one contiguous 1 KiB
-// block per wave instruction (lane l to byte 16*l), so one instruction fills one
-// chunk column, lane l fetching row l ^ (4 * (c & 3)).
-// Reads, with the 64-bank LDS of gfx950:
-//   - MFMA operands of the natural layout (16 rows, one 16-byte chunk per lane
-//     per 16-lane group) are 256 contiguous bytes: no bank conflict;
-//   - transposed reads (ds_read_b64_tr_b16: 4 rows x 64 bytes per 32 lanes)
-//     land in 4 different 64-byte quarters of a 256-byte bank line.
-// Every per-lane address is a lane constant plus a compile-time offset.
+// Global -> LDS copies and LDS reads shared by the tile layouts below.
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Asynchronous copy global -> LDS of 16 (dma_b128) or 4 (dma_b32) bytes per lane:
@@ -139,70 +127,12 @@ __device__ __forceinline__ void dma_b32(const void* src, lds_void* dst) {
 }
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-constexpr int kTileRows = 64;
-
-__device__ __forceinline__ constexpr int cm_slot(int r, int c) { return c * kTileRows + (r ^ ((c & 3) << 2)); }
-
 // ds_read_b64_tr_b16. Within each group of 16 lanes, lane s supplies the address
 // of 4 consecutive bf16 M[s][0..3]; lane i of the group receives
 // M[i/4 + 4e][i%4] for e = 0..3.
 __device__ __forceinline__ v4i16 lds_tr4(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4i16*)((__attribute__((address_space(3))) char*)(lds_void*)(p)));
-}
-
-// Per-lane byte offsets into chunk-major tiles, computed once per kernel.
-struct CmLane {
-  int a[2];   // natural operand: row j = lane%32 of a 32-row block, chunk 2kk+h; index kk&1
-  int t[2];   // transposed operand: the two 8-row halves of a 16-row k step
-  __device__ explicit CmLane(int lane) {
-    const int j = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int cl = 2 * p + h;
-      a[p] = 16 * (cl * kTileRows + (j ^ (4 * cl)));
-    }
-    const int g = lane >> 4, s = lane & 15;
-    const int cl = 2 * (g & 1) + ((s & 3) >> 1);
-    const int rl = 4 * (g >> 1) + (s >> 2);
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) t[jj] = 16 * (cl * kTileRows + ((rl + 8 * jj) ^ (4 * cl))) + 8 * (s & 1);
-  }
-};
-
-// MFMA operand of the natural layout: row rbase + lane%32 (rbase a multiple of
-// 32), elements 16kk + 8h .. +7 (h = lane/32).
-__device__ __forceinline__ bf16x8 cm_row8(const bf16* tile, const CmLane& o, int rbase, int kk) {
-  const char* p = reinterpret_cast<const char*>(tile) + o.a[kk & 1] + 16 * (4 * (kk >> 1) * kTileRows + rbase);
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// Transposed MFMA A operand: A[i][k] = T[row0 + r(k)][col0 + i] for output row
-// i = lane%32, where slot 8h + 4jj + e reads row row0 + 8jj + 4h + e (jj = 0, 1;
-// e = 0..3) -- the slot order of a 32x32 MFMA result's registers 0..7 (c_row),
-// so a packed previous result is the matching B operand. row0 is a multiple of
-// 16, col0 of 32.
-__device__ __forceinline__ bf16x8 cm_tr8(const bf16* tile, const CmLane& o, int row0, int col0) {
-  const char* base = reinterpret_cast<const char*>(tile) + 16 * ((col0 >> 3) * kTileRows + row0);
-  const u32x2 lo = __builtin_bit_cast(u32x2, lds_tr4(base + o.t[0]));
-  const u32x2 hi = __builtin_bit_cast(u32x2, lds_tr4(base + o.t[1]));
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-// Issues the async copy of one 64-row tile (row r = global row row_ptr(r),
-// clamped to nvalid - 1 so every address is inside the tensor). The 4 waves of
-// the workgroup each fill D/32 chunk columns.
-template <int D, class RowAddr>
-__device__ __forceinline__ void tile_fetch(bf16* tile, RowAddr row_ptr, int nvalid, int wave, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int PER_WAVE = CH / 4;
-#pragma unroll
-  for (int n = 0; n < PER_WAVE; ++n) {
-    const int c = wave * PER_WAVE + n;
-    const int row = lane ^ ((c & 3) << 2);
-    const bf16* src = row_ptr(min(row, nvalid - 1)) + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(tile + c * kTileRows * 8), 16, 0, 0);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -254,9 +184,11 @@ __device__ __forceinline__ bf16x8 sw_row8(const bf16* tile, const SwLane<D>& o, 
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Transposed MFMA A operand, same element order as cm_tr8: A[i][k] = T[row0 +
-// r(k)][col0 + i] with slot 8h + 4jj + e reading row row0 + 8jj + 4h + e. row0 is
-// a multiple of 16, col0 of 32.
+// Transposed MFMA A operand: A[i][k] = T[row0 + r(k)][col0 + i] for output row
+// i = lane%32, where slot 8h + 4jj + e reads row row0 + 8jj + 4h + e (jj = 0, 1;
+// e = 0..3) -- the slot order of a 32x32 MFMA result's registers 0..7 (c_row),
+// so a packed previous result is the matching B operand. row0 is a multiple of
+// 16, col0 of 32.
 template <int D>
 __device__ __forceinline__ bf16x8 sw_tr8(const bf16* tile, const SwLane<D>& o, int row0, int col0) {
   const char* base = reinterpret_cast<const char*>(tile) + 16 * row0 * (D / 8);
