@@ -422,15 +422,12 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   const int64_t D = d->head_dim;
   const int64_t Hq = d->num_q_heads;
   // forward workspace: [V transposed (pipelined path)] [partial O fp32] [partial LSE]
-  // The transposed V copy costs a read and a write of V and one launch; it pays
-  // when the forward reads every V tile several times (many query tiles per kv
-  // head), not for a short query over a long key arena.
-  int64_t visits = 0;
-  for (const FwdItem& it : p.fwd_items)
-    if (it.qtile >= 0) visits += it.kt_end - it.kt_begin;
-  const int64_t distinct = ceil_div(tk, 64) * Hkv;
-  p.use_vt = !(d->flags & BD_ATTN_FLAG_FWD_DIRECT) && d->dtype == BD_ATTN_BF16 && B % 8 == 0 &&
-             (visits >= 4 * distinct || (d->flags & BD_ATTN_FLAG_FWD_VT));
+  // The forward through a transposed V copy (a pre-pass writing V^T once per
+  // call) is taken only on request: with swizzled row-major K/V tiles, the direct
+  // kernel's transposing LDS reads of V measured faster than the copy plus its
+  // launch on every workload here.
+  p.use_vt = !(d->flags & BD_ATTN_FLAG_FWD_DIRECT) && (d->flags & BD_ATTN_FLAG_FWD_VT) &&
+             d->dtype == BD_ATTN_BF16 && B % 8 == 0;
   p.tk_pad = ceil_div(tk, 64) * 64 + 64;
   int64_t off = 0;
   p.off_ws_vt = 0;

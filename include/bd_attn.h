@@ -72,12 +72,10 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
 #define BD_ATTN_FLAG_FORCE_SPLIT 2u /* always split long key ranges (forward; for tests) */
 #define BD_ATTN_FLAG_NO_XCD     4u  /* plain largest-cost-first order, no XCD grouping */
 #define BD_ATTN_FLAG_FWD_DIRECT 8u /* bf16 forward without the transposed V copy (the
-                                       default uses it when the block size is a multiple of 8
-                                       and the forward reads each V tile at least 4 times on
-                                       average, i.e. not for a short query over a long arena) */
-#define BD_ATTN_FLAG_FWD_VT     16u /* bf16 forward through the transposed V copy whenever
-                                       the block size allows it (overrides the cost rule;
-                                       FWD_DIRECT wins if both are set) */
+                                       default; kept for callers that set it) */
+#define BD_ATTN_FLAG_FWD_VT     16u /* bf16 forward through a transposed copy of V (a
+                                       pre-pass) when the block size is a multiple of 8;
+                                       FWD_DIRECT wins if both are set */
 /* Bits 8..15: key tiles (of 64 keys) per split of the forward split path;
  * 0 selects the library's choice. Ignored unless the plan splits. */
 #define BD_ATTN_FLAG_SPLIT_TILES(n) ((((uint32_t)(n)) & 0xffu) << 8)

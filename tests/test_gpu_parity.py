@@ -104,7 +104,7 @@ def test_denoise_step_no_split_matches_split():
     assert st["max_abs"] <= 4e-3, st
 
 
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_staircase_full_kv_group_samples(flags):
     wl = W.make_config(4)
     _say(f"case {wl.name} seed 4 flags {flags}")
@@ -175,7 +175,7 @@ CASES = [
 
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("seed", [0, 1])
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_random_packs(case, seed, flags):
     B, hq, hkv, D, dt, sigma = CASES[case]
     rng = np.random.default_rng(7000 + 31 * case + seed)
@@ -192,7 +192,7 @@ def test_random_packs(case, seed, flags):
     _compare(wl, gpu, run_oracle(wl))
 
 
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_forced_split_matches_oracle(flags):
     rng = np.random.default_rng(42)
     meta = W.Meta([1024, 512], [0, 512], [[5, 32, 0], [16]], 32, 8, 2, 128, "bf16")
@@ -203,7 +203,7 @@ def test_forced_split_matches_oracle(flags):
     _compare(wl, gpu, run_oracle(wl))
 
 
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_DIRECT, b.FLAG_FWD_VT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_key_shift_stress(flags):
     # scores shifted by a large common offset exercise the running-maximum rescaling
     rng = np.random.default_rng(43)

@@ -254,15 +254,15 @@ def test_dkdv_variant_selection(ctx, q0, B, hq, hkv, dt, want):
     assert names[0] == ("dq" if dt == "bf16" else "bwd_pre")
 
 
-def test_transposed_v_copy_only_where_it_pays():
-    """The V transpose pre-pass is planned when the forward reads each V tile
-    several times (packed replay), not for one short query over a long arena
-    (denoising step), unless forced; FWD_DIRECT always wins."""
+def test_transposed_v_copy_only_on_request():
+    """The V transpose pre-pass runs only with FWD_VT (block size a multiple of
+    8, bf16); FWD_DIRECT wins over it."""
     step = config_meta(2, np.random.default_rng(2))
     replay = config_meta(3, np.random.default_rng(3))
     assert "transpose_v" not in b.Plan(step).kernel_names(False)
+    assert "transpose_v" not in b.Plan(replay).kernel_names(False)
     assert "transpose_v" in b.Plan(step, b.FLAG_FWD_VT).kernel_names(False)
-    assert "transpose_v" in b.Plan(replay).kernel_names(False)
+    assert "transpose_v" in b.Plan(replay, b.FLAG_FWD_VT).kernel_names(False)
     assert "transpose_v" not in b.Plan(replay, b.FLAG_FWD_DIRECT | b.FLAG_FWD_VT).kernel_names(False)
     # block sizes that are not a multiple of 8 never take it
     odd = Meta([96, 60], [0, 60], [[1], [0, 2]], 12, 8, 2, 64, "bf16")
