@@ -98,7 +98,9 @@ __device__ __forceinline__ ChunkGeom chunk_geom(const KTile& kt, const CanvasQ* 
 // dK^T += Q^T dS (16 MFMAs), in one fixed slot program where the products of
 // one half overlap the ALU work of the other. The masked instantiation applies
 // per-score row limits; the planner picks the other one when every (chunk,
-// 32-key group) pair is either wholly visible or skipped.
+// 32-key group) pair is either wholly visible or skipped. An item may cover a
+// contiguous part of a key tile's chunks only (a split tile); it then writes
+// fp32 partial dK/dV for dkdv_merge instead of the bf16 result.
 constexpr int kBwdStages = 3;
 
 template <int D>
@@ -107,32 +109,6 @@ struct DkdvGeom {
   static constexpr int TE = QC * D;             // elements of one Q or dO chunk
   static constexpr int PW = D / 32;             // global_load_lds per wave per tile
 };
-
-// P and dS of one 32-row half from S and dP (in place), packed as MFMA B operands.
-__device__ __forceinline__ void dkdv_pointwise(f32x16& s, f32x16& dp, const float* cL, const float* cD, int r_lo,
-                                               int h, float scale_log2, bf16x8 (&pb)[2], bf16x8 (&sb)[2]) {
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) {
-    const int r0 = r_lo + 8 * g4 + 4 * h;
-    const f32x4 lv = *reinterpret_cast<const f32x4*>(cL + r0);
-    const f32x4 dv = *reinterpret_cast<const f32x4*>(cD + r0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = g4 * 4 + e;
-      const float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lv[e]));
-      s[r] = p;
-      dp[r] = p * (dp[r] - dv[e]);
-    }
-  }
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    float t0[8], t1[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { t0[e] = s[ks * 8 + e]; t1[e] = dp[ks * 8 + e]; }
-    pb[ks] = pack8(t0);
-    sb[ks] = pack8(t1);
-  }
-}
 
 // One 64-row query chunk for the 32 keys of a wave, as a fixed program of
 // 4 * NS MFMA slots (NS = 2 * D / 16):

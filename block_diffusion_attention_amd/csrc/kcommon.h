@@ -47,39 +47,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // Row of a 32x32 MFMA result held by register r of a lane in half h (= lane/32).
 __device__ __forceinline__ constexpr int c_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Column permutation of transposed LDS tiles. An MFMA result's column values in
-// registers 8s..8s+7 of half h are the rows 16s + {0..3, 8..11} + 4h; packing
-// them in register order gives the B operand of the next product, so the
-// matching A operand must hold those rows at k slots 16s + 8h + 0..7. Storing
-// index i of a transposed tile at column kperm(i) makes those 8 slots one
-// contiguous 16-byte LDS read. kperm keeps aligned groups of 4 contiguous.
-__device__ __forceinline__ constexpr int kperm(int i) {
-  return (i & ~15) | (((i >> 2) & 1) << 3) | (((i >> 3) & 1) << 2) | (i & 3);
-}
-
-// Natural tile [rows][D + 8] (bf16): 16-byte row padding keeps 8 consecutive
-// rows on distinct bank groups for 16-byte reads.
-template <int D>
-struct NatTile {
-  static constexpr int kStride = D + 8;
-  __device__ static __forceinline__ int off(int row, int col) { return row * kStride + col; }
-};
-
-// Transposed tile [D][NCOL] (bf16) with 16-byte chunks XOR-swizzled per row, so
-// that 8 consecutive rows read at one column chunk hit distinct banks.
-template <int NCOL>
-struct TrTile {
-  static constexpr int kChunks = NCOL / 8;
-  __device__ static __forceinline__ int swz(int d) {
-    if (kChunks == 8) return (d ^ (d >> 3)) & 7;
-    return ((d >> 1) ^ (d >> 3)) & (kChunks - 1);
-  }
-  // element offset of (row d, column c)
-  __device__ static __forceinline__ int off(int d, int c) {
-    return d * NCOL + ((((c >> 3) ^ swz(d))) << 3) + (c & 7);
-  }
-};
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v;
   v[0] = (bf16)a;
@@ -95,11 +62,6 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   u[2] = pack_bf16x2(x[4], x[5]);
   u[3] = pack_bf16x2(x[6], x[7]);
   return __builtin_bit_cast(bf16x8, u);
-}
-
-// bf16 element (odd ? high : low) of dword x, then of dword y, packed as one dword.
-__device__ __forceinline__ uint32_t pick_pair(uint32_t x, uint32_t y, int odd) {
-  return odd ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
