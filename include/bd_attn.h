@@ -126,9 +126,10 @@ bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_
 
 /* Forward. q [Tq,Hq,D], k/v [Tk,Hkv,D] in desc.dtype; writes o [Tq,Hq,D] and
  * lse [Tq,Hq] (float32). ws: ws_fwd_bytes of device memory (may be NULL when
- * that size is 0): for bf16 plans with a block size that is a multiple of 8 it
- * holds a transposed copy of V (rewritten by every call), and on the split path
- * the partial results. All pointers device pointers, 16-byte aligned.
+ * that size is 0): for bf16 plans made with BD_ATTN_FLAG_FWD_VT (and a block
+ * size that is a multiple of 8) it holds a transposed copy of V (rewritten by
+ * every call), and on the split path the partial results. All pointers device
+ * pointers, 16-byte aligned.
  * Errors: EINVAL (NULL or misaligned pointer), EWORKSPACE (ws NULL while
  * needed), EHIP (launch failure). */
 bd_attn_status bd_attn_fwd(bd_attn_plan_t plan, const void* meta_dev,
