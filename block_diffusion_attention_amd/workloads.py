@@ -8,7 +8,8 @@ Packed layout of one segment (the boundary's contract):
   keys    : [ C clean context tokens | m canvases of B tokens ]
   queries : [ clean tokens from position q0 to C | the same m canvases ]
 Replay rows (q0 = 0) make the context tokens queries too; the single-request
-denoising step (q0 = C) queries only with the canvas.
+denoising step (q0 = C) queries only with the canvas, and the commit-folded
+step (q0 = C - B) with the just-finished block and the next canvas.
 
 The five named workloads follow the shapes the method is used at: packed
 replay rows of captured canvases after their clean contexts, and one
@@ -33,15 +34,23 @@ DTYPE_FP32 = "fp32"
 @dataclasses.dataclass
 class Meta:
     """Per-segment metadata of one packed batch."""
-    ctx_len: List[int]                 # C_s, multiple of block_size
+    ctx_len: List[int]                 # C_s; C_s + o_s a multiple of block_size
     ctx_q_begin: List[int]             # q0_s in [0, C_s]
-    canvas_block_idx: List[List[int]]  # per segment, block index b in [0, C_s/B], any order
+    canvas_block_idx: List[List[int]]  # per segment, block index b in [0, (C_s+o_s)/B], any order
     block_size: int
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
     dtype: str = DTYPE_BF16
     softmax_scale: float = 0.0         # <= 0 means 1/sqrt(head_dim)
+    # o_s in [0, B): the segment's block grid starts o_s positions before its
+    # first context token (a prompt whose length is not a multiple of B followed
+    # by whole blocks); None means 0 for every segment
+    block_offset: Optional[List[int]] = None
+    clean_causal: bool = False         # clean queries see clean keys token-causally
+
+    def offset(self, s: int) -> int:
+        return 0 if self.block_offset is None else int(self.block_offset[s])
 
     @property
     def num_segments(self) -> int:
@@ -165,14 +174,21 @@ def make_config(k: int, seed: Optional[int] = None, with_do: Optional[bool] = No
 
 
 def random_meta(rng, *, max_segments=3, max_blocks=5, block_sizes=(1, 2, 3, 4), max_canvases=3,
-                hq=2, hkv=1, d=8, dtype=DTYPE_FP32, canvas_only_prob=0.3, allow_empty_ctx=True) -> Meta:
-    """Small random metadata for exhaustive and randomized checks."""
+                hq=2, hkv=1, d=8, dtype=DTYPE_FP32, canvas_only_prob=0.3, allow_empty_ctx=True,
+                offsets=False, clean_causal=False) -> Meta:
+    """Small random metadata for exhaustive and randomized checks.
+
+    ``offsets`` draws a block-grid offset o in [0, B) per segment (the context
+    then holds n*B - o tokens); ``clean_causal`` sets the token-causal clean rule.
+    """
     B = int(rng.choice(block_sizes))
     S = int(rng.integers(1, max_segments + 1))
-    ctx, q0s, cvs = [], [], []
+    ctx, q0s, cvs, offs = [], [], [], []
     for _ in range(S):
         n = int(rng.integers(0 if allow_empty_ctx else 1, max_blocks + 1))
-        C = n * B
+        o = int(rng.integers(0, B)) if (offsets and n > 0) else 0
+        offs.append(o)
+        C = n * B - o
         m = int(rng.integers(0, max_canvases + 1))
         cv = [int(x) for x in rng.integers(0, n + 1, size=m)]
         if rng.random() < canvas_only_prob:
@@ -182,7 +198,8 @@ def random_meta(rng, *, max_segments=3, max_blocks=5, block_sizes=(1, 2, 3, 4), 
         if (C - q0) + m * B == 0:       # keep at least one query per segment
             cv = [n]
         ctx.append(C); q0s.append(q0); cvs.append(cv)
-    return Meta(ctx, q0s, cvs, B, hq, hkv, d, dtype)
+    return Meta(ctx, q0s, cvs, B, hq, hkv, d, dtype, block_offset=offs if offsets else None,
+                clean_causal=clean_causal)
 
 
 def random_workload(rng, meta: Meta, sigma: float = 1.0, with_do: bool = True, name="random",
@@ -196,7 +213,8 @@ def segment_slice(wl: Workload, s: int) -> Workload:
     m = wl.meta
     qo, ko = m.q_offsets(), m.k_offsets()
     sub = Meta([m.ctx_len[s]], [m.ctx_q_begin[s]], [list(m.canvas_block_idx[s])], m.block_size,
-               m.num_q_heads, m.num_kv_heads, m.head_dim, m.dtype, m.softmax_scale)
+               m.num_q_heads, m.num_kv_heads, m.head_dim, m.dtype, m.softmax_scale,
+               None if m.block_offset is None else [m.offset(s)], m.clean_causal)
     q = wl.q[qo[s]:qo[s + 1]]
     k = wl.k[ko[s]:ko[s + 1]]
     v = wl.v[ko[s]:ko[s + 1]]
@@ -209,7 +227,8 @@ def kv_group_slice(wl: Workload, g: int) -> Workload:
     m = wl.meta
     G = m.num_q_heads // m.num_kv_heads
     sub = dataclasses.replace(m, num_q_heads=G, num_kv_heads=1,
-                              canvas_block_idx=[list(c) for c in m.canvas_block_idx])
+                              canvas_block_idx=[list(c) for c in m.canvas_block_idx],
+                              block_offset=None if m.block_offset is None else list(m.block_offset))
     hs = slice(g * G, (g + 1) * G)
     return Workload(f"{wl.name}[kv{g}]", sub, wl.q[:, hs], wl.k[:, g:g + 1], wl.v[:, g:g + 1],
                     None if wl.do is None else wl.do[:, hs], wl.passes)

@@ -20,9 +20,19 @@ queries (the single-request denoising step, appendix F.1 "Kernels").
 Readings of points the pages leave open (each one is a single place below):
   * clean queries see clean keys block-causally: key block <= query block,
     bidirectional inside a block (the pages only say clean queries never see
-    noisy keys);
+    noisy keys); with ``meta.clean_causal`` they see clean keys token-causally
+    (key position <= query position), the reading of the causal commit pass
+    that writes a finished block's keys and values (ORL appendix F.1, the
+    single-request engine's block loop);
   * a canvas with block index b sees the clean blocks 0..b-1 and its own B
-    tokens; b ranges over 0..C/B;
+    tokens; b ranges over 0..(C+o)/B;
+  * the block grid of a segment may start o positions (0 <= o < B) before its
+    first context token, so that a prompt whose length is not a multiple of B is
+    followed by whole blocks: context position p lies in block (p + o) // B, the
+    first block holds B - o tokens and C + o is a multiple of B (o = 0 unless
+    ``meta.block_offset`` says otherwise);
+  * the commit-folded step (ORL section 3.3 "Commit folding": one pass over the
+    finished block and the next canvas) is q0 = C - B with one canvas b = (C+o)/B;
   * query head h reads kv head h // (Hq / Hkv);
   * scale defaults to 1/sqrt(D); LSE is the natural-log log-sum-exp of the
     scaled scores.
@@ -54,6 +64,12 @@ __all__ = [
 def _canvas_lists(meta):
     """Per-segment canvas block indices as plain lists."""
     return [list(map(int, c)) for c in meta.canvas_block_idx]
+
+
+def _offset(meta, s):
+    """Block-grid offset o of segment s (0 when the metadata gives none)."""
+    off = getattr(meta, "block_offset", None)
+    return 0 if off is None else int(off[s])
 
 
 def segment_layout(meta):
@@ -102,22 +118,30 @@ def key_roles(meta):
     return roles
 
 
-def visible(qr, kr, block_size):
+def visible(qr, kr, block_size, block_offset=0, clean_causal=False):
     """Block-diffusion visibility of key role ``kr`` from query role ``qr``.
 
     ORL section 3.2 "Staircase attention kernel" / appendix D.2: a noisy block
     (canvas) sees the prompt and the clean blocks before it and itself, never
     its own clean copy, later blocks, other noisy blocks or other documents;
-    clean queries never see noisy keys.
+    clean queries never see noisy keys. ``block_offset`` is the offset o of the
+    query's segment (context position p lies in block (p + o) // B);
+    ``clean_causal`` selects token-causal clean rows.
     """
     qs, q_canvas, qpos, qc, qb = qr
     ks, k_canvas, kpos, kc, _kb = kr
     if qs != ks:                       # packed documents are mutually invisible
         return False
-    if not q_canvas:                   # clean query: clean keys, block-causal
-        return (not k_canvas) and (kpos // block_size) <= (qpos // block_size)
+
+    def block(p):
+        return (p + block_offset) // block_size
+
+    if not q_canvas:                   # clean query: clean keys, block- or token-causal
+        if k_canvas:
+            return False
+        return kpos <= qpos if clean_causal else block(kpos) <= block(qpos)
     if not k_canvas:                   # canvas query, clean key: blocks before b
-        return (kpos // block_size) < qb
+        return block(kpos) < qb
     return kc == qc                    # canvas key: only its own canvas
 
 
@@ -126,10 +150,12 @@ def dense_mask(meta):
     qr = query_roles(meta)
     kr = key_roles(meta)
     B = int(meta.block_size)
+    causal = bool(getattr(meta, "clean_causal", False))
     m = np.zeros((len(qr), len(kr)), dtype=bool)
     for i, a in enumerate(qr):
+        o = _offset(meta, a[0])
         for j, b in enumerate(kr):
-            m[i, j] = visible(a, b, B)
+            m[i, j] = visible(a, b, B, o, causal)
     return m
 
 
@@ -219,28 +245,36 @@ def _groups(meta, segments=None):
     """Groups of query tokens that see the same keys, with those keys.
 
     Yields (segment, query token indices, key token indices). The sets follow
-    the same rule as ``visible``: the clean queries of context block j see the
-    clean keys [0, (j+1)B); canvas c (block index b) sees the clean keys
-    [0, bB) and its own B tokens.
+    the same rule as ``visible``. With block-grid offset o, block j covers the
+    context positions [jB - o, (j+1)B - o): the clean queries of block j see
+    the clean keys [0, (j+1)B - o); with token-causal clean rows, the clean
+    query at position p sees [0, p + 1); canvas c (block index b) sees the
+    clean keys [0, bB - o) and its own B tokens.
     """
     B = int(meta.block_size)
+    causal = bool(getattr(meta, "clean_causal", False))
     for s, (C, q0, cv, qo, ko) in enumerate(segment_layout(meta)):
         if segments is not None and s not in segments:
             continue
+        o = _offset(meta, s)
         nq_clean = C - q0
-        for j in range(q0 // B, (C + B - 1) // B):
-            lo = max(q0, j * B)
-            hi = min(C, (j + 1) * B)
-            if hi <= lo:
-                continue
-            qidx = np.arange(qo + (lo - q0), qo + (hi - q0))
-            kidx = np.arange(ko, ko + min(C, (j + 1) * B))
-            yield s, qidx, kidx
+        if causal:
+            for p in range(q0, C):
+                yield s, np.arange(qo + (p - q0), qo + (p - q0) + 1), np.arange(ko, ko + p + 1)
+        else:
+            for j in range((q0 + o) // B, (C + o + B - 1) // B):
+                lo = max(q0, j * B - o)
+                hi = min(C, (j + 1) * B - o)
+                if hi <= lo:
+                    continue
+                qidx = np.arange(qo + (lo - q0), qo + (hi - q0))
+                kidx = np.arange(ko, ko + hi)
+                yield s, qidx, kidx
         for c, b in enumerate(cv):
             qstart = qo + nq_clean + c * B
             kstart = ko + C + c * B
             qidx = np.arange(qstart, qstart + B)
-            kidx = np.concatenate([np.arange(ko, ko + b * B), np.arange(kstart, kstart + B)])
+            kidx = np.concatenate([np.arange(ko, ko + max(0, b * B - o)), np.arange(kstart, kstart + B)])
             yield s, qidx, kidx
 
 

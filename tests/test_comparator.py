@@ -30,7 +30,7 @@ def test_rounded_oracle_passes_and_zeros_fail():
         assert not within(zero, "bf16")
 
 
-def _mutant_sees_own_block(qr, kr, B):
+def _mutant_sees_own_block(qr, kr, B, *_):
     qs, qc, _, _, qb = qr
     ks, kc, kp, _, _ = kr
     if qs == ks and qc and not kc:
@@ -38,7 +38,7 @@ def _mutant_sees_own_block(qr, kr, B):
     return ORIG(qr, kr, B)
 
 
-def _mutant_token_causal(qr, kr, B):
+def _mutant_token_causal(qr, kr, B, *_):
     qs, qc, qp, _, _ = qr
     ks, kc, kp, _, _ = kr
     if qs == ks and not qc and not kc:

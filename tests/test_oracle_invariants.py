@@ -29,6 +29,53 @@ def _tiny_metas():
                     yield Meta([C], [q0], [cv], B, 2, 1, 4)
 
 
+def _tiny_metas_shifted():
+    """Grid offsets o in [1, B) and the token-causal clean rule, on tiny metadata."""
+    for B in (2, 3):
+        for n in range(1, 4):
+            for o in range(0, B):
+                C = n * B - o
+                for causal in (False, True):
+                    for q0 in sorted({0, C, min(C, B - o), max(0, C - B)}):
+                        cands = list(range(n + 1))
+                        for cv in [[]] + [[b] for b in cands] + [list(p) for p in itertools.permutations(cands, 2)]:
+                            if (C - q0) + len(cv) * B == 0:
+                                continue
+                            yield Meta([C], [q0], [cv], B, 2, 1, 4, block_offset=[o], clean_causal=causal)
+
+
+def _dense_vs_range(meta, rng):
+    wl = random_workload(rng, meta)
+    mask = orc.dense_mask(meta)
+    assert mask.any(axis=1).all(), "every query sees at least its own block"
+    assert orc.visible_pairs(meta) == int(mask.sum())
+    o1, l1 = orc.attention_fwd_dense(wl.q, wl.k, wl.v, meta, mask=mask)
+    o2, l2 = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+    g1 = orc.attention_bwd_dense(wl.q, wl.k, wl.v, wl.do, meta, mask=mask)
+    g2 = orc.attention_bwd(wl.q, wl.k, wl.v, wl.do, meta)
+    for a, b in zip(g2, g1):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_range_form_equals_dense_shifted_grid_and_causal_exhaustive():
+    rng = np.random.default_rng(1)
+    count = 0
+    for meta in _tiny_metas_shifted():
+        _dense_vs_range(meta, rng)
+        count += 1
+    assert count > 300
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_range_form_equals_dense_shifted_random(seed):
+    rng = np.random.default_rng(700 + seed)
+    meta = random_meta(rng, hq=4, hkv=2, d=8, max_segments=4, max_blocks=6, offsets=True,
+                       clean_causal=bool(seed % 2))
+    _dense_vs_range(meta, rng)
+
+
 def test_range_form_equals_dense_exhaustive():
     rng = np.random.default_rng(0)
     count = 0
@@ -199,7 +246,7 @@ def test_gradient_invariants():
 
 # ------------------------------------- planted mistakes are caught by the pins
 
-def _mutant_sees_own_clean_block(qr, kr, B):
+def _mutant_sees_own_clean_block(qr, kr, B, *_):
     qs, qc, qp, qci, qb = qr
     ks, kc, kp, kci, _ = kr
     if qs == ks and qc and not kc:
@@ -207,7 +254,7 @@ def _mutant_sees_own_clean_block(qr, kr, B):
     return _ORIG_VISIBLE(qr, kr, B)
 
 
-def _mutant_token_causal(qr, kr, B):
+def _mutant_token_causal(qr, kr, B, *_):
     qs, qc, qp, _, _ = qr
     ks, kc, kp, _, _ = kr
     if qs == ks and not qc and not kc:
@@ -215,7 +262,7 @@ def _mutant_token_causal(qr, kr, B):
     return _ORIG_VISIBLE(qr, kr, B)
 
 
-def _mutant_canvases_see_each_other(qr, kr, B):
+def _mutant_canvases_see_each_other(qr, kr, B, *_):
     qs, qc, _, _, _ = qr
     ks, kc, _, _, _ = kr
     if qs == ks and qc and kc:
@@ -232,6 +279,39 @@ def test_golden_mask_catches_mutants(monkeypatch, mutant):
     gold, _ = read_golden_matrix("mask_b2_two_canvases.txt")
     monkeypatch.setattr(orc, "visible", mutant)
     meta = Meta([4], [0], [[1, 2]], 2, 1, 1, 4)
+    assert not (orc.dense_mask(meta) == gold.astype(bool)).all()
+
+
+def _mutant_ignores_offset(qr, kr, B, o=0, causal=False):
+    return _ORIG_VISIBLE(qr, kr, B, 0, causal)
+
+
+def _mutant_ignores_causal(qr, kr, B, o=0, causal=False):
+    return _ORIG_VISIBLE(qr, kr, B, o, False)
+
+
+def _mutant_offset_wrong_sign(qr, kr, B, o=0, causal=False):
+    qs, qc, qp, qci, qb = qr
+    ks, kc, kp, kci, _ = kr
+    if qs == ks and not kc:             # grid shifted the other way: block (p - o) // B
+        if qc:
+            return (kp - o) // B < qb
+        return (kp - o) // B <= (qp - o) // B
+    return _ORIG_VISIBLE(qr, kr, B, o, causal)
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("mask_b2_offset1_three_canvases.txt", _mutant_ignores_offset),
+    ("mask_b2_offset1_three_canvases.txt", _mutant_offset_wrong_sign),
+    ("mask_b2_commit_folded_token_causal.txt", _mutant_ignores_causal),
+])
+def test_shifted_and_commit_goldens_catch_mutants(monkeypatch, name, mutant):
+    gold, m = read_golden_matrix(name)
+    off = [int(m["block_offset"])] if "block_offset" in m else None
+    meta = Meta([int(m["ctx_len"])], [int(m["ctx_q_begin"])], [[int(x) for x in m["canvases"].split(",")]],
+                int(m["block_size"]), 1, 1, 4, block_offset=off, clean_causal=m.get("clean_causal") == "1")
+    assert (orc.dense_mask(meta) == gold.astype(bool)).all()
+    monkeypatch.setattr(orc, "visible", mutant)
     assert not (orc.dense_mask(meta) == gold.astype(bool)).all()
 
 

@@ -1,10 +1,14 @@
 """Pins of the CPU oracle to things other than itself (CPU only).
 
-* the hand-worked visibility matrix under tests/golden/;
+* the hand-worked visibility matrices under tests/golden/ (the base rule, a
+  shifted block grid, the commit-folded step); a shifted grid equals the
+  aligned grid without its first tokens;
 * special cases that reduce to torch's scaled_dot_product_attention (CPU, fp64):
   one block -> bidirectional attention, block size 1 -> causal attention,
   canvas at the last block index in canvas-only mode -> unmasked attention,
   grouped-query attention -> multi-head attention with repeated K/V;
+  token-causal clean rows -> causal attention; the commit-folded step -> causal
+  rows plus an unmasked canvas; a lone partial first block -> bidirectional;
 * torch SDPA with the oracle's explicit boolean mask (forward and autograd);
 * central finite differences of the forward for the analytic gradients.
 """
@@ -78,7 +82,91 @@ def test_two_documents_block_diagonal():
     assert (mab == np.concatenate([top, bot], 0)).all()
 
 
+def _golden_meta(m):
+    off = [int(m["block_offset"])] if "block_offset" in m else None
+    return Meta([int(m["ctx_len"])], [int(m["ctx_q_begin"])],
+                [[int(x) for x in m["canvases"].split(",")]], int(m["block_size"]), 1, 1, 4,
+                block_offset=off, clean_causal=m.get("clean_causal") == "1")
+
+
+@pytest.mark.parametrize("name", ["mask_b2_offset1_three_canvases.txt",
+                                  "mask_b2_commit_folded_token_causal.txt"])
+def test_golden_masks_offset_and_commit(name):
+    gold, m = read_golden_matrix(name)
+    mask = orc.dense_mask(_golden_meta(m))
+    assert mask.shape == gold.shape
+    assert (mask == gold.astype(bool)).all()
+
+
+def test_commit_folded_block_causal_rows():
+    # Block-causal commit rows see their whole block: the same rows of the
+    # two-canvas golden matrix (queries c2 c3 and canvas Y at block index 2).
+    gold, _ = read_golden_matrix("mask_b2_two_canvases.txt")
+    mask = orc.dense_mask(Meta([4], [2], [[2]], 2, 1, 1, 4))
+    want = gold[[2, 3, 6, 7]][:, [0, 1, 2, 3, 6, 7]]
+    assert (mask == want.astype(bool)).all()
+
+
+@pytest.mark.parametrize("B,n,o", [(2, 3, 1), (4, 3, 3), (3, 4, 2), (5, 2, 4)])
+def test_offset_grid_is_the_aligned_grid_without_its_first_tokens(B, n, o):
+    # A grid offset o is the aligned grid of n whole blocks with its first o
+    # context tokens removed: the mask of (C = nB - o, offset o) is the mask of
+    # (C = nB, offset 0) without the rows and columns of those tokens.
+    cv = [list(range(n + 1))]
+    shifted = Meta([n * B - o], [0], cv, B, 1, 1, 4, block_offset=[o])
+    aligned = Meta([n * B], [0], cv, B, 1, 1, 4)
+    ma = orc.dense_mask(aligned)
+    keep_q = [i for i in range(ma.shape[0]) if i >= o]
+    keep_k = [j for j in range(ma.shape[1]) if j >= o]
+    assert (orc.dense_mask(shifted) == ma[keep_q][:, keep_k]).all()
+    assert orc.visible_pairs(shifted) == int(ma[keep_q][:, keep_k].sum())
+
+
 # ------------------------------------------------------ SDPA special cases
+
+@pytest.mark.parametrize("B,n,o", [(1, 6, 0), (4, 3, 0), (4, 3, 3), (8, 2, 5)])
+def test_token_causal_clean_stream_is_causal(B, n, o):
+    # Token-causal clean rows with no canvases: plain causal attention, whatever
+    # the block size and the grid offset.
+    meta = Meta([n * B - o], [0], [[]], B, 4, 2, 16, block_offset=[o], clean_causal=True)
+    wl = _wl(meta, 40 + B + o)
+    ref = _sdpa(wl.q, wl.k, wl.v, causal=True)
+    o1, _ = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    np.testing.assert_allclose(o1, ref, rtol=0, atol=1e-12)
+    od, _ = orc.attention_fwd_dense(wl.q, wl.k, wl.v, meta)
+    np.testing.assert_allclose(od, ref, rtol=0, atol=1e-12)
+    g = orc.attention_bwd(wl.q, wl.k, wl.v, wl.do, meta)
+    r = _sdpa_grads(wl.q, wl.k, wl.v, wl.do, causal=True)
+    for a, b in zip(g, r):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("B,n", [(2, 3), (4, 4), (3, 2)])
+def test_commit_folded_step_reduces_to_sdpa(B, n):
+    # The commit-folded step with token-causal commit rows: the finished block's
+    # rows are the last B rows of causal attention over the context, the canvas
+    # at the next block index attends to the whole context and itself.
+    C = n * B
+    meta = Meta([C], [C - B], [[n]], B, 2, 1, 8, clean_causal=True)
+    wl = _wl(meta, 70 + B)
+    o, _ = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    full = _wl(Meta([C], [0], [[]], B, 2, 1, 8), 0)
+    qc = np.concatenate([full.q[:C - B], wl.q[:B]], 0)     # any first rows: only the last B are compared
+    ref_clean = _sdpa(qc, wl.k[:C], wl.v[:C], causal=True)[C - B:]
+    np.testing.assert_allclose(o[:B], ref_clean, rtol=0, atol=1e-12)
+    ref_canvas = _sdpa(wl.q[B:], wl.k, wl.v)
+    np.testing.assert_allclose(o[B:], ref_canvas, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,o", [(4, 1), (8, 7)])
+def test_partial_first_block_is_bidirectional(B, o):
+    # A context that is only the partial first block (C = B - o) is one block:
+    # every clean row sees every context key.
+    meta = Meta([B - o], [0], [[]], B, 2, 2, 16, block_offset=[o])
+    wl = _wl(meta, 90 + o)
+    out, _ = orc.attention_fwd(wl.q, wl.k, wl.v, meta)
+    np.testing.assert_allclose(out, _sdpa(wl.q, wl.k, wl.v), rtol=0, atol=1e-12)
+
 
 @pytest.mark.parametrize("B", [1, 3, 8])
 def test_single_block_is_bidirectional(B):
