@@ -40,7 +40,10 @@ WORKLOAD_NAMES = {
     4: "staircase: 4096-token context + 24 canvases at distinct block indices in [1,128], 32q/8kv, D=128, "
        "bf16, fwd+bwd",
     5: "large pack: 4 x (8192-token context + 16 canvases), 32q/8kv, D=128, bf16, fwd+bwd",
+    6: "commit-folded step: 2031-token context in KV (block grid offset 17), the finished 32-token block "
+       "(token-causal) + the next canvas as queries, 32q/8kv, D=128, bf16, fwd",
 }
+FWD_ONLY = (2, 6)     # single-request serving steps: forward only, bandwidth-bound
 
 
 def parse():
@@ -48,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--flags", type=int, default=0, help="plan flags (BD_ATTN_FLAG_*)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -261,7 +264,7 @@ def main():
     k = args.workload
     wl = W.make_config(k, seed=args.seed)
     m = wl.meta
-    backward = wl.do is not None and not args.fwd_only and k != 2
+    backward = wl.do is not None and not args.fwd_only and k not in FWD_ONLY
     t_plan0 = time.perf_counter()
     plan = b.Plan(m, args.flags)
     t_plan = time.perf_counter() - t_plan0
@@ -332,7 +335,7 @@ def main():
         "combine": ("hbm", q_bytes + plan.tq * Hq * 4),
         "transpose_v": ("hbm", 2.0 * kv_bytes),
     }
-    if k == 2:   # the denoising step is bandwidth-bound: its forward is priced in bytes
+    if k in FWD_ONLY:   # the serving steps are bandwidth-bound: their forward is priced in bytes
         algo["fwd"] = ("hbm", float(q_bytes + 2 * kv_bytes))
     algo["dkdv_masked"] = algo["dkdv"]
     dom = max(avg_ms, key=lambda n: avg_ms[n])

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libbdattn.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
 FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD, FLAG_FWD_DIRECT, FLAG_FWD_VT = 1, 2, 4, 8, 16
+FLAG_CLEAN_CAUSAL = 32
 
 
 def flag_split_tiles(n: int) -> int:
@@ -47,6 +48,7 @@ class Desc(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+        ("block_offset", _i32p),
     ]
 
 
@@ -103,8 +105,9 @@ class Plan:
 
     def __init__(self, meta, flags: int = 0):
         self.meta = meta
+        offs = getattr(meta, "block_offset", None)
         self._keep = [_arr(meta.ctx_len), _arr(meta.ctx_q_begin), _arr(meta.canvas_offsets),
-                      _arr(meta.flat_canvas_block_idx)]
+                      _arr(meta.flat_canvas_block_idx), None if offs is None else _arr(offs)]
         d = Desc()
         d.num_segments = len(meta.ctx_len)
         d.ctx_len = ctypes.cast(self._keep[0], _i32p)
@@ -117,7 +120,11 @@ class Plan:
         d.head_dim = meta.head_dim
         d.dtype = BF16 if meta.dtype == "bf16" else FP32
         d.softmax_scale = float(meta.softmax_scale)
+        if getattr(meta, "clean_causal", False):
+            flags |= FLAG_CLEAN_CAUSAL
         d.flags = flags
+        if self._keep[4] is not None:
+            d.block_offset = ctypes.cast(self._keep[4], _i32p)
         h = _vp()
         _check(_lib.bd_attn_plan(ctypes.byref(d), ctypes.byref(h)))
         self.handle = h

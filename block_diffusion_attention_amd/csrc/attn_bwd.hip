@@ -240,7 +240,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
   const bf16* __restrict__ V = static_cast<const bf16*>(a.v);
   const bf16* __restrict__ dO = static_cast<const bf16*>(a.dout);
-  const int G = a.G, B = a.B;
+  const int G = a.G, B = a.B, Bc = a.grain;
 
   const int kidx = wave * 32 + j;
   const bool key_ok = kidx < kt.n_keys;
@@ -286,7 +286,7 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       dma_b32(src, (lds_void*)(wave == 0 ? dL_ : dD_));
     } else if (MASKED && wave == 2) {
       int lim = -1;                                     // padding rows see nothing
-      if (lane < nrows) lim = g.pos0 >= 0 ? ((g.pos0 + lane_tok) / B + 1) * B : g.lim;
+      if (lane < nrows) lim = g.pos0 >= 0 ? ((g.pos0 + lane_tok) / Bc + 1) * Bc : g.lim;
       dM_[lane] = lim;
     }
   };
@@ -324,12 +324,11 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     if (c + 2 < nchunks) issue(c + 2, nQ, nG, nL, nD, nM);
     const ChunkGeom g = chunk_geom(kt, a.canvq, nall - 1 - (c0 + c), nc0, cpc, qct);
     const int nrows = g.ntok * G;
-    // row limits of the two 32-row halves (clean limits grow with the row)
     // row limits of the first and the last valid row (clean limits grow with the row)
     int lim_first, lim_last;
     if (g.pos0 >= 0) {
-      lim_first = (g.pos0 / B + 1) * B;
-      lim_last = ((g.pos0 + (nrows - 1) / G) / B + 1) * B;
+      lim_first = (g.pos0 / Bc + 1) * Bc;
+      lim_last = ((g.pos0 + (nrows - 1) / G) / Bc + 1) * Bc;
     } else {
       lim_first = lim_last = g.lim;
     }
@@ -442,7 +441,7 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   const bool row_ok = row < qt.n_tok * G;
   if (t >= qt.n_tok) t = qt.n_tok - 1;
   const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * G + gh;
-  const int L = row_limit(qt, t, a.B);
+  const int L = row_limit(qt, t, a.grain);
   const int n1 = (qt.lim_max + KT - 1) / KT;
   const int64_t kv_stride = (int64_t)a.hkv * D;
 

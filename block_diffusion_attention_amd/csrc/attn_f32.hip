@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdArgs a) {
   float q[D], acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) { q[d] = Q[qrow * D + d]; acc[d] = 0.f; }
-  const int L = row_limit(qt, t, a.B);
+  const int L = row_limit(qt, t, a.grain);
   const F32Ranges rg(qt);
   float m = -INFINITY, l = 0.f;
   for (int kt = 0; kt < rg.n1 + rg.n2; ++kt) {
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(128) dq_f32_kernel(BwdArgs a) {
 #pragma unroll
   for (int d = 0; d < D; ++d) { q[d] = Q[qrow * D + d]; g[d] = dO[qrow * D + d]; acc[d] = 0.f; }
   const float lse = a.lse[qrow], dl = a.delta[qrow];
-  const int L = row_limit(qt, t, a.B);
+  const int L = row_limit(qt, t, a.grain);
   const F32Ranges rg(qt);
   for (int kt = 0; kt < rg.n1 + rg.n2; ++kt) {
     const bool r1 = kt < rg.n1;
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(128) dkdv_f32_kernel(BwdArgs a) {
         int tok, gh;
         if (r < n_clean_rows) {
           tok = kt.cq_tok + r / G; gh = r % G;
-          lim = ((kt.cq_pos + r / G) / B + 1) * B;
+          lim = ((kt.cq_pos + r / G) / a.grain + 1) * a.grain;
         } else {
           const int rc = r - n_clean_rows, e = rc / (B * G), w = rc - e * B * G;
           const CanvasQ cq = a.canvq[kt.cv_begin + e];

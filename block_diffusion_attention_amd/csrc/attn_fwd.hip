@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   if (t >= qt.n_tok) t = qt.n_tok - 1;          // padding rows mirror the last token
   const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * G + gh;
 
-  const int L = row_limit(qt, t, a.B);
+  const int L = row_limit(qt, t, a.grain);
   const int n1 = (qt.lim_max + KT - 1) / KT;
   const int64_t kv_stride = (int64_t)a.hkv * D;
 

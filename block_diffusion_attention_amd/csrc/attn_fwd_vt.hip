@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   const bool row_ok = row < qt.n_tok * G;
   if (t >= qt.n_tok) t = qt.n_tok - 1;          // padding rows mirror the last token
   const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * G + gh;
-  const int L = row_limit(qt, t, a.B);
+  const int L = row_limit(qt, t, a.grain);
   const int n1 = (qt.lim_max + KT - 1) / KT;
   const int64_t kv_stride = (int64_t)a.hkv * D;
   const float cl2 = a.scale_log2;

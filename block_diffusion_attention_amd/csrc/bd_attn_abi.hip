@@ -156,7 +156,7 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   bdattn::FwdArgs a{};
   a.qtiles = section<int32_t>(meta_dev, p.off_qtiles);
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.B = p.desc.block_size;
+  a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.grain = p.grain;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
   const int D = p.desc.head_dim;
@@ -249,6 +249,7 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.rows_q = p.tq * p.desc.num_q_heads;
   a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.B = p.desc.block_size;
+  a.grain = p.grain;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
   if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;

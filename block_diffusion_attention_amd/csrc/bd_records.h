@@ -8,10 +8,15 @@
 // valid query ranges per key tile).
 //
 // Row limit. Every query row r has a limit L(r) on the context positions of the
-// clean keys it sees (positions p < L(r)):
-//   clean query at context position t : L = (t / B + 1) * B  (block-causal)
-//   query of a canvas at block index b: L = b * B           (blocks before b)
-// and a canvas query additionally sees the B keys of its own canvas.
+// clean keys it sees (positions p < L(r)). With the segment's block-grid offset o
+// (context position t lies at grid position t + o, in block (t + o) / B) and the
+// grain Bc (B for block-causal clean rows, 1 for token-causal ones):
+//   clean query at context position t : L = ((t + o) / Bc + 1) * Bc - o
+//   query of a canvas at block index b: L = max(b * B - o, 0)   (blocks before b)
+// and a canvas query additionally sees the B keys of its own canvas. The query
+// tiles carry context-position limits; the key-side records (KTile, CanvasQ)
+// work in grid positions, where the same rule reads P_key < (P_q / Bc + 1) * Bc
+// and P_key < b * B.
 #pragma once
 #include <stdint.h>
 
@@ -43,9 +48,9 @@ struct QTile {         // 8 x int32
   int32_t q_tok;       // first packed query token
   int32_t n_tok;       // tokens in the tile (>= 1)
   int32_t k_ctx;       // packed index of the segment's first clean key
-  int32_t pos0;        // context position of the first token, or -1 for a canvas tile
+  int32_t pos0;        // grid position of the first token, or -1 for a canvas tile
   int32_t lim_max;     // clean keys [k_ctx, k_ctx + lim_max) may be visible to some row
-  int32_t lim_min;     // every row sees at least the clean keys below lim_min
+  int32_t lim_min;     // limit of the first row: every row sees the clean keys below it
   int32_t k_own;       // packed index of the canvas' own keys (canvas tile)
   int32_t n_own;       // own canvas keys (B for a canvas tile, 0 for a clean tile)
 };
@@ -67,10 +72,10 @@ struct CombItem {      // 4 x int32: merge of the split partial results of one q
 struct KTile {         // 8 x int32
   int32_t k_tok;       // first packed key token
   int32_t n_keys;      // keys in the tile (1..kKBlock)
-  int32_t p0;          // context position of the first key, or -1 for canvas keys
+  int32_t p0;          // grid position of the first key, or -1 for canvas keys
   int32_t cq_tok;      // first packed query token of the clean query range
   int32_t cq_len;      // clean query tokens that may see the tile (0 if none)
-  int32_t cq_pos;      // context position of cq_tok
+  int32_t cq_pos;      // grid position of cq_tok
   int32_t cv_begin;    // first entry of the canvas-query list
   int32_t cv_count;    // canvas-query entries that may see the tile
 };
@@ -78,7 +83,7 @@ struct KTile {         // 8 x int32
 struct CanvasQ {       // 4 x int32
   int32_t q_tok;       // first packed query token of the canvas
   int32_t n_tok;       // B
-  int32_t lim;         // b * B: clean context positions visible to the canvas
+  int32_t lim;         // b * B: grid positions of the clean keys visible to the canvas
   int32_t own;         // 1 for the entry of a canvas key tile (sees all of the tile)
 };
 

@@ -269,9 +269,11 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
 }
 
-// Limit on clean-key context positions visible to query token t of a tile.
-__device__ __forceinline__ int row_limit(const QTile& qt, int t, int B) {
-  return qt.pos0 >= 0 ? ((qt.pos0 + t) / B + 1) * B : qt.lim_min;
+// Limit on clean-key context positions visible to query token t of a tile: the
+// first row's limit, raised by the grain at every multiple of it that the grid
+// position crosses from the first row to row t (constant for a canvas tile).
+__device__ __forceinline__ int row_limit(const QTile& qt, int t, int grain) {
+  return qt.pos0 >= 0 ? qt.lim_min + ((qt.pos0 + t) / grain - qt.pos0 / grain) * grain : qt.lim_min;
 }
 
 // Work-list records are read through the constant address space with a

@@ -20,7 +20,8 @@ struct FwdArgs {
   float* part_lse;           // split mode: partial LSE [slot][kQRows]
   const void* vt;            // V transposed, [Hkv][D][tk_pad] (pipelined kernel)
   int tk_pad;
-  int hq, hkv, G, B;
+  int hq, hkv, G;
+  int grain;                 // step of the clean row limits: block size, or 1 (token-causal)
   float scale_log2;          // softmax scale * log2(e)
   float scale;               // softmax scale
 };
@@ -56,6 +57,7 @@ struct BwdArgs {
   void* dv;
   int64_t rows_q;            // Tq * Hq
   int hq, hkv, G, B;
+  int grain;                 // step of the clean row limits: block size, or 1 (token-causal)
   float scale_log2;
   float scale;
 };

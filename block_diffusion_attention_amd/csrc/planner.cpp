@@ -114,6 +114,7 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   p.desc = *d;
   p.desc.ctx_len = nullptr; p.desc.ctx_q_begin = nullptr;
   p.desc.canvas_offsets = nullptr; p.desc.canvas_block_idx = nullptr;
+  p.desc.block_offset = nullptr;
   p.G = G;
   p.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
   p.ctx.assign(d->ctx_len, d->ctx_len + S);
@@ -121,26 +122,43 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   if (d->ctx_q_begin) p.q0.assign(d->ctx_q_begin, d->ctx_q_begin + S);
   p.coff.assign(d->canvas_offsets, d->canvas_offsets + S + 1);
   p.cb.assign(d->canvas_block_idx, d->canvas_block_idx + ncv);
+  p.off.assign(S, 0);
+  if (d->block_offset) p.off.assign(d->block_offset, d->block_offset + S);
+  // Clean row limits come in steps of the block size (block-causal) or of one
+  // token (token-causal): a clean query at context position t of a segment with
+  // grid offset o sees the clean positions below ((t + o) / Bc + 1) * Bc - o.
+  const bool causal = (d->flags & BD_ATTN_FLAG_CLEAN_CAUSAL) != 0;
+  const int64_t Bc = causal ? 1 : B;
+  p.grain = (int)Bc;
+  auto clean_lim = [Bc](int64_t t, int64_t o) { return ((t + o) / Bc + 1) * Bc - o; };
 
   int64_t tq = 0, tk = 0, pairs = 0;
   const int64_t kMaxTok = (int64_t)INT32_MAX / 2;
   for (int s = 0; s < S; ++s) {
-    const int64_t C = p.ctx[s], q0 = p.q0[s];
-    if (C < 0 || C % B) { *err = "ctx_len[" + std::to_string(s) + "] must be >= 0 and a multiple of block_size"; return BD_ATTN_EINVAL; }
-    if (q0 < 0 || q0 > C) { *err = "ctx_q_begin[" + std::to_string(s) + "] must lie in [0, ctx_len]"; return BD_ATTN_EINVAL; }
-    const int64_t n = C / B;
+    const int64_t C = p.ctx[s], q0 = p.q0[s], o = p.off[s];
+    const std::string ss = "[" + std::to_string(s) + "]";
+    if (o < 0 || o >= B) { *err = "block_offset" + ss + " must lie in [0, block_size)"; return BD_ATTN_EINVAL; }
+    if (C < 0 || (C + o) % B) { *err = "ctx_len" + ss + " must be >= 0 and ctx_len + block_offset a multiple of block_size"; return BD_ATTN_EINVAL; }
+    if (q0 < 0 || q0 > C) { *err = "ctx_q_begin" + ss + " must lie in [0, ctx_len]"; return BD_ATTN_EINVAL; }
+    const int64_t n = (C + o) / B;
     const int64_t m = p.coff[s + 1] - p.coff[s];
     for (int64_t c = p.coff[s]; c < p.coff[s + 1]; ++c)
-      if (p.cb[c] < 0 || p.cb[c] > n) { *err = "canvas_block_idx[" + std::to_string(c) + "] must lie in [0, ctx_len/block_size]"; return BD_ATTN_EINVAL; }
+      if (p.cb[c] < 0 || p.cb[c] > n) { *err = "canvas_block_idx[" + std::to_string(c) + "] must lie in [0, (ctx_len + block_offset)/block_size]"; return BD_ATTN_EINVAL; }
     tq += (C - q0) + m * B;
     tk += C + m * B;
     if (tq > kMaxTok || tk > kMaxTok) { *err = "packed token count too large"; return BD_ATTN_EINVAL; }
-    // visible pairs: clean block j (queries from q0) sees (j+1)B keys; canvas b sees bB + B
-    for (int64_t j = q0 / B; j < n; ++j) {
-      const int64_t lo = std::max(q0, j * B), hi = (j + 1) * B;
-      pairs += (hi - lo) * (j + 1) * B;
+    // visible pairs: a clean query at t sees clean_lim(t) keys (constant over a
+    // block when block-causal); canvas b sees max(bB - o, 0) + B
+    if (causal) {
+      pairs += (C * (C + 1) - q0 * (q0 + 1)) / 2;
+    } else {
+      for (int64_t j = (q0 + o) / B; j < n; ++j) {
+        const int64_t lo = std::max(q0, j * B - o), hi = (j + 1) * B - o;
+        if (hi > lo) pairs += (hi - lo) * hi;
+      }
     }
-    for (int64_t c = p.coff[s]; c < p.coff[s + 1]; ++c) pairs += (int64_t)B * ((int64_t)p.cb[c] * B + B);
+    for (int64_t c = p.coff[s]; c < p.coff[s + 1]; ++c)
+      pairs += (int64_t)B * (std::max<int64_t>((int64_t)p.cb[c] * B - o, 0) + B);
   }
   if (tq == 0) { *err = "the batch has no query tokens"; return BD_ATTN_EINVAL; }
   if (tq * d->num_q_heads > (int64_t)INT32_MAX || tk * d->num_kv_heads > (int64_t)INT32_MAX) {
@@ -158,19 +176,21 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   {
     int64_t qo = 0, ko = 0;
     for (int s = 0; s < S; ++s) {
-      const int64_t C = p.ctx[s], q0 = p.q0[s];
+      const int64_t C = p.ctx[s], q0 = p.q0[s], o = p.off[s];
       const int64_t m = p.coff[s + 1] - p.coff[s];
-      // clean queries, tiles of QT tokens that stay inside one block when B >= QT
+      // clean queries, tiles of QT tokens that stay inside one block when B >= QT.
+      // pos0 is the grid position t + o; the kernels step the first row's limit
+      // by Bc at every multiple of Bc crossed from there.
       for (int64_t t = q0; t < C;) {
         int64_t len = std::min<int64_t>(QT, C - t);
-        if (B >= QT) len = std::min<int64_t>(len, (t / B + 1) * B - t);
+        if (B >= QT) len = std::min<int64_t>(len, ((t + o) / B + 1) * B - o - t);
         QTile q{};
         q.q_tok = (int32_t)(qo + (t - q0));
         q.n_tok = (int32_t)len;
         q.k_ctx = (int32_t)ko;
-        q.pos0 = (int32_t)t;
-        q.lim_min = (int32_t)((t / B + 1) * B);
-        q.lim_max = (int32_t)(((t + len - 1) / B + 1) * B);
+        q.pos0 = (int32_t)(t + o);
+        q.lim_min = (int32_t)clean_lim(t, o);
+        q.lim_max = (int32_t)clean_lim(t + len - 1, o);
         q.k_own = (int32_t)ko; q.n_own = 0;
         p.qtiles.push_back(q); qtile_seg.push_back(s);
         t += len;
@@ -183,7 +203,7 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
           q.n_tok = (int32_t)std::min<int64_t>(QT, B - t);
           q.k_ctx = (int32_t)ko;
           q.pos0 = -1;
-          q.lim_min = q.lim_max = (int32_t)(b * B);
+          q.lim_min = q.lim_max = (int32_t)std::max<int64_t>(b * B - o, 0);
           q.k_own = (int32_t)(ko + C + c * B);
           q.n_own = B;
           p.qtiles.push_back(q); qtile_seg.push_back(s);
@@ -278,10 +298,13 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   {
     int64_t qo = 0, ko = 0;
     for (int s = 0; s < S; ++s) {
-      const int64_t C = p.ctx[s], q0 = p.q0[s];
+      const int64_t C = p.ctx[s], q0 = p.q0[s], o = p.off[s];
       const int64_t m = p.coff[s + 1] - p.coff[s];
+      // Key-side positions are grid positions (context position + o): a clean
+      // key at grid position P is seen by the canvases with b*B > P and by the
+      // clean queries whose grid limit (P_q / Bc + 1) * Bc exceeds P.
       // canvases of the segment sorted by block index, largest first: those
-      // visible to a clean key at position p0 (b*B > p0) form a prefix.
+      // visible to a clean key at grid position p0 (b*B > p0) form a prefix.
       std::vector<int64_t> ord(m);
       std::iota(ord.begin(), ord.end(), 0);
       std::stable_sort(ord.begin(), ord.end(), [&](int64_t a, int64_t b) {
@@ -300,14 +323,16 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
         KTile t{};
         t.k_tok = (int32_t)(ko + k0);
         t.n_keys = (int32_t)std::min<int64_t>(kKBlock, C - k0);
-        t.p0 = (int32_t)k0;
-        const int64_t cpos = std::max<int64_t>(q0, (k0 / B) * B);
-        t.cq_pos = (int32_t)cpos;
+        t.p0 = (int32_t)(k0 + o);
+        // first clean query that can see key k0: the start of its block
+        // (block-causal) or k0 itself (token-causal)
+        const int64_t cpos = std::max<int64_t>(q0, ((k0 + o) / Bc) * Bc - o);
+        t.cq_pos = (int32_t)(cpos + o);
         t.cq_len = (int32_t)std::max<int64_t>(0, C - cpos);
         t.cq_tok = (int32_t)(qo + std::max<int64_t>(0, cpos - q0));
         t.cv_begin = cv_first;
         int32_t cnt = 0;
-        for (int64_t c = 0; c < m; ++c) if (p.canvq[cv_first + c].lim > k0) cnt++;
+        for (int64_t c = 0; c < m; ++c) if (p.canvq[cv_first + c].lim > k0 + o) cnt++;
         t.cv_count = cnt;
         p.ktiles.push_back(t); ktile_seg.push_back(s);
         kcost.push_back((int64_t)t.cq_len + (int64_t)cnt * B);
@@ -439,15 +464,16 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
     off = p.off_ws_lse + nsplit * kQRows * 4;
   }
   p.ws_fwd = (size_t)off;
-  // dK/dV without per-score limits: a wave's 32 keys start at a multiple of 32;
-  // if every row limit is a multiple of 32 (block size a multiple of 32), every
-  // 64-row query chunk lies inside one block (64 / G tokens dividing B, query
-  // ranges starting at block boundaries) and no chunk is partial (B * G a multiple
-  // of 64), each (chunk, wave) pair is seen either whole or not at all.
+  // dK/dV without per-score limits: a wave's 32 keys start at a grid position
+  // that is a multiple of 32 (grid offset a multiple of 32); if every row limit
+  // is a multiple of 32 (block-causal, block size a multiple of 32), every 64-row
+  // query chunk lies inside one block (64 / G tokens dividing B, query ranges
+  // starting at block boundaries) and no chunk is partial (B * G a multiple of
+  // 64), each (chunk, wave) pair is seen either whole or not at all.
   {
     const int qct = 64 / G;
-    bool aligned = B % 32 == 0 && 64 % G == 0 && B % qct == 0;
-    for (int s = 0; s < S && aligned; ++s) aligned = p.q0[s] % B == 0;
+    bool aligned = !causal && B % 32 == 0 && 64 % G == 0 && B % qct == 0;
+    for (int s = 0; s < S && aligned; ++s) aligned = (p.q0[s] + p.off[s]) % B == 0 && p.off[s] % 32 == 0;
     p.dkdv_masked = !aligned;
   }
   p.off_ws_lse2 = ceil_div(tq * Hq * 4, 256) * 256;          // delta [Tq, Hq] fp32, then LSE*log2(e)

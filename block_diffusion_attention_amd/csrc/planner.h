@@ -15,7 +15,8 @@ struct Plan {
   int G = 1;                    // query heads per kv head
   int qt_tokens = 1;            // tokens per query tile
   float scale = 1.f;
-  std::vector<int32_t> ctx, q0, coff, cb;
+  std::vector<int32_t> ctx, q0, coff, cb, off;   // off: block-grid offset per segment
+  int grain = 1;                // step of the clean row limits: B, or 1 (token-causal)
   int64_t tq = 0, tk = 0, pairs = 0;
 
   std::vector<QTile> qtiles;

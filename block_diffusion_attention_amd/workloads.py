@@ -140,11 +140,12 @@ CONFIG_NAMES = {
     3: "packed-replay-16seg-32q8kv-d128",
     4: "staircase-4096ctx-24canvas-32q8kv-d128",
     5: "large-pack-4x8192ctx-16canvas-32q8kv-d128",
+    6: "commit-folded-step-2031ctx-offset17-32q8kv-d128",
 }
 
 
 def config_meta(k: int, rng) -> Meta:
-    """Metadata of named workload ``k`` (1..5), drawn from ``rng``."""
+    """Metadata of named workload ``k`` (1..6), drawn from ``rng``."""
     if k == 1:
         return Meta([64], [0], [[4]], 16, 2, 1, 64, DTYPE_FP32)
     if k == 2:
@@ -158,11 +159,17 @@ def config_meta(k: int, rng) -> Meta:
     if k == 5:
         cv = [[int(x) for x in rng.choice(np.arange(1, 257), size=16, replace=False)] for _ in range(4)]
         return Meta([8192] * 4, [0] * 4, cv, 32, 32, 8, 128, DTYPE_BF16)
+    if k == 6:
+        # commit-folded step of one request: a 2031-token context (a prompt that
+        # leaves the block grid 17 positions short, then whole blocks of 32), the
+        # block just finished (its 32 tokens as token-causal queries) and the next
+        # canvas, in one pass over the KV arena
+        return Meta([2031], [1999], [[64]], 32, 32, 8, 128, DTYPE_BF16, block_offset=[17], clean_causal=True)
     raise ValueError(f"unknown workload {k}")
 
 
 def make_config(k: int, seed: Optional[int] = None, with_do: Optional[bool] = None) -> Workload:
-    """Named workload ``k`` (1..5) with seed (default k)."""
+    """Named workload ``k`` (1..6) with seed (default k)."""
     rng = np.random.default_rng(k if seed is None else seed)
     meta = config_meta(k, rng)
     sigma = 1.0 if k == 1 else 1.0 / math.sqrt(128.0)

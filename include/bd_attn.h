@@ -12,6 +12,20 @@
  *     blocks, other canvases or other segments;
  *   - a clean query sees clean keys block-causally (key block <= query block,
  *     bidirectional inside a block) and never a canvas key.
+ * Two variants of the clean rule, both per plan (ORL section 3.3 "Commit
+ * folding" runs the finished block's commit pass together with the next
+ * canvas; appendix F.1 calls that pass causal; the pages fix neither the
+ * granularity of "causal" nor where a prompt's blocks begin):
+ *   - BD_ATTN_FLAG_CLEAN_CAUSAL: a clean query sees the clean keys at context
+ *     positions up to its own (token-causal) instead of whole blocks;
+ *   - block_offset[s] = o (0 <= o < B): the segment's block grid starts o
+ *     positions before its first context token, i.e. context position p lies
+ *     in block (p + o) / B and the first block holds B - o tokens (a prompt
+ *     whose length is not a multiple of B, followed by whole blocks).
+ *     ctx_len[s] + o must be a multiple of B; a canvas with block index b sees
+ *     the context positions p < b*B - o.
+ * The commit-folded step is ctx_q_begin[s] = ctx_len[s] - B (the finished block's
+ * tokens as queries) with one canvas at the next block index.
  * The forward pass returns O = softmax(scale * Q K^T under that visibility) V and
  * the natural-log LSE of the scaled scores; the backward pass returns dQ, dK,
  * dV of L = <dO, O>. Visible key ranges are derived from per-segment metadata;
@@ -76,6 +90,8 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
 #define BD_ATTN_FLAG_FWD_VT     16u /* bf16 forward through a transposed copy of V (a
                                        pre-pass) when the block size is a multiple of 8;
                                        FWD_DIRECT wins if both are set */
+#define BD_ATTN_FLAG_CLEAN_CAUSAL 32u /* clean queries see clean keys token-causally
+                                         (position <= own) instead of block-causally */
 /* Bits 8..15: key tiles (of 64 keys) per split of the forward split path;
  * 0 selects the library's choice. Ignored unless the plan splits. */
 #define BD_ATTN_FLAG_SPLIT_TILES(n) ((((uint32_t)(n)) & 0xffu) << 8)
@@ -84,10 +100,11 @@ typedef struct bd_attn_plan_s* bd_attn_plan_t;
 
 typedef struct {
   int32_t num_segments;             /* S >= 1 */
-  const int32_t* ctx_len;           /* host [S]: C_s >= 0, multiple of block_size */
+  const int32_t* ctx_len;           /* host [S]: C_s >= 0, C_s + o_s a multiple of block_size */
   const int32_t* ctx_q_begin;       /* host [S] or NULL (= 0 for all): 0 <= q0_s <= C_s */
   const int32_t* canvas_offsets;    /* host [S+1]: prefix sums, canvas_offsets[0] = 0 */
-  const int32_t* canvas_block_idx;  /* host [canvas_offsets[S]]: 0 <= b <= C_s / B, any order */
+  const int32_t* canvas_block_idx;  /* host [canvas_offsets[S]]: 0 <= b <= (C_s + o_s) / B,
+                                       any order */
   int32_t block_size;               /* B >= 1 */
   int32_t num_q_heads;              /* Hq >= 1, multiple of num_kv_heads */
   int32_t num_kv_heads;             /* Hkv >= 1 */
@@ -95,6 +112,8 @@ typedef struct {
   int32_t dtype;                    /* bd_attn_dtype */
   float softmax_scale;              /* <= 0 selects 1/sqrt(head_dim) */
   uint32_t flags;                   /* BD_ATTN_FLAG_* */
+  const int32_t* block_offset;      /* host [S] or NULL (= 0 for all): 0 <= o_s < B, the
+                                       block grid's start before the first context token */
 } bd_attn_desc;
 
 /* Validates the metadata and builds a plan (host only; copies everything it

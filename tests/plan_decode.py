@@ -21,14 +21,22 @@ def decode(blob):
     return out
 
 
+def _grain(meta):
+    """Step of the clean row limits: the block size, or 1 for token-causal clean rows."""
+    return 1 if getattr(meta, "clean_causal", False) else meta.block_size
+
+
 def qtile_visibility(rec, meta, G):
-    """Boolean [Tq, Tk] visibility encoded by the query tiles (each token once per tile)."""
-    B = meta.block_size
+    """Boolean [Tq, Tk] visibility encoded by the query tiles (each token once per tile).
+
+    A clean tile's row limit is the first row's limit raised by the grain at
+    every multiple of the grain its grid position (pos0 + t) crosses."""
+    Bc = _grain(meta)
     vis = np.zeros((meta.tq, meta.tk), dtype=bool)
     cover = np.zeros(meta.tq, dtype=np.int64)
     for q_tok, n_tok, k_ctx, pos0, lim_max, lim_min, k_own, n_own in rec["qtiles"]:
         for t in range(n_tok):
-            L = ((pos0 + t) // B + 1) * B if pos0 >= 0 else lim_min
+            L = lim_min + ((pos0 + t) // Bc - pos0 // Bc) * Bc if pos0 >= 0 else lim_min
             assert L <= lim_max and L >= lim_min
             vis[q_tok + t, k_ctx:k_ctx + L] = True
             vis[q_tok + t, k_own:k_own + n_own] = True
@@ -37,8 +45,9 @@ def qtile_visibility(rec, meta, G):
 
 
 def ktile_visibility(rec, meta, G):
-    """Boolean [Tq, Tk] visibility encoded by the key tiles and canvas-query entries."""
-    B = meta.block_size
+    """Boolean [Tq, Tk] visibility encoded by the key tiles and canvas-query entries
+    (key-side positions are grid positions)."""
+    Bc = _grain(meta)
     vis = np.zeros((meta.tq, meta.tk), dtype=bool)
     cover = np.zeros(meta.tk, dtype=np.int64)
     cv = rec["canvq"]
@@ -47,7 +56,7 @@ def ktile_visibility(rec, meta, G):
         for kk in range(n_keys):
             key = k_tok + kk
             for t in range(cq_len):
-                L = ((cq_pos + t) // B + 1) * B
+                L = ((cq_pos + t) // Bc + 1) * Bc
                 if p0 >= 0 and p0 + kk < L:
                     vis[cq_tok + t, key] = True
             for e in range(cv_begin, cv_begin + cv_count):

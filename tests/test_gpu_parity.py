@@ -192,6 +192,58 @@ def test_random_packs(case, seed, flags):
     _compare(wl, gpu, run_oracle(wl))
 
 
+# ------------------------------------ shifted block grid, token-causal clean rows
+
+SHIFT_CASES = [0, 2, 3, 5, 7, 9, 10, 11]      # indices into CASES
+
+
+@pytest.mark.parametrize("case", SHIFT_CASES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_random_packs_shifted_grid(case, causal):
+    B, hq, hkv, D, dt, sigma = CASES[case]
+    rng = np.random.default_rng(9100 + 31 * case + int(causal))
+    max_blocks = max(2, min(12, 600 // B))
+    meta = W.random_meta(rng, max_segments=3, max_blocks=max_blocks, block_sizes=(B,), max_canvases=4,
+                         hq=hq, hkv=hkv, d=D, dtype=dt, offsets=True, clean_causal=causal)
+    G = hq // hkv
+    wl = W.random_workload(rng, meta, sigma=sigma, do_sigma=min(1.0, (4.0 / G) ** 0.5))
+    _say(f"case shifted B={B} hq={hq} hkv={hkv} D={D} {dt} causal={causal} offsets={meta.block_offset} "
+         f"tq={meta.tq} tk={meta.tk}")
+    gpu, _ = run_gpu(wl)
+    _compare(wl, gpu, run_oracle(wl))
+
+
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT, b.FLAG_NO_SPLIT])
+def test_commit_folded_step(flags):
+    wl = W.make_config(6)
+    _say(f"case {wl.name} flags {flags}")
+    gpu, plan = run_gpu(wl, flags=flags, backward=False)
+    assert ("combine" in plan.kernel_names(False)) == (not flags & b.FLAG_NO_SPLIT)
+    _compare(wl, gpu, run_oracle(wl, backward=False))
+
+
+def test_commit_folded_step_backward():
+    rng = np.random.default_rng(606)
+    meta = W.config_meta(6, rng)
+    wl = W.random_workload(rng, meta, sigma=1 / np.sqrt(128))
+    _say(f"case commit-folded fwd+bwd tq={meta.tq} tk={meta.tk}")
+    gpu, plan = run_gpu(wl)
+    assert plan.kernel_names(True)[1] == "dkdv_masked"
+    _compare(wl, gpu, run_oracle(wl))
+
+
+def test_shifted_grid_unmasked_dkdv():
+    # grid offset 32 with query ranges at shifted block starts: the unmasked dK/dV
+    # program still applies
+    rng = np.random.default_rng(607)
+    meta = W.Meta([224, 96], [32, 96], [[1, 4], [0, 2]], 64, 32, 8, 128, "bf16", block_offset=[32, 32])
+    wl = W.random_workload(rng, meta, sigma=0.3)
+    _say(f"case shifted-unmasked tq={meta.tq} tk={meta.tk}")
+    gpu, plan = run_gpu(wl, flags=b.FLAG_FORCE_SPLIT)
+    assert plan.kernel_names(True)[1] == "dkdv"
+    _compare(wl, gpu, run_oracle(wl))
+
+
 @pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_forced_split_matches_oracle(flags):
     rng = np.random.default_rng(42)

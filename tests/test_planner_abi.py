@@ -42,6 +42,9 @@ def _status(meta, **over):
     desc.num_segments = d["S"]
     desc.ctx_len, desc.ctx_q_begin, desc.canvas_offsets, desc.canvas_block_idx = (
         ctypes.cast(x, b._i32p) for x in keep)
+    if "bo" in d:
+        keep.append(b._arr(d["bo"]))
+        desc.block_offset = ctypes.cast(keep[-1], b._i32p)
     desc.block_size, desc.num_q_heads, desc.num_kv_heads, desc.head_dim = d["B"], d["hq"], d["hkv"], d["D"]
     desc.dtype, desc.softmax_scale, desc.flags = d["dtype"], d["scale"], 0
     h = ctypes.c_void_p()
@@ -73,12 +76,24 @@ GOOD = Meta([64, 32], [0, 32], [[1, 2], [1]], 16, 4, 2, 128, "bf16")
     (dict(dtype=7), b.EINVAL),
     (dict(scale=float("inf")), b.EINVAL),
     (dict(ctx=[0, 0], q0=[0, 0], off=[0, 0, 0], cb=[]), b.EINVAL),   # no query at all
+    (dict(bo=[16, 0]), b.EINVAL),            # grid offset must be below the block size
+    (dict(bo=[-1, 0]), b.EINVAL),
+    (dict(bo=[3, 0]), b.EINVAL),             # ctx_len + offset not a multiple of B
+    (dict(ctx=[61, 32], bo=[3, 0], cb=[1, 5, 1]), b.EINVAL),   # b beyond (ctx_len + o) / B
+    (dict(ctx=[0, 32], q0=[0, 32], bo=[4, 0]), b.EINVAL),      # empty context: offset 0 only
 ])
 def test_validation_errors(over, code):
     st, msg = _status(GOOD, **over)
     assert st == code and msg
     st_ok, _ = _status(GOOD)
     assert st_ok == b.OK
+
+
+def test_shifted_grid_and_causal_metadata_accepted():
+    st, msg = _status(GOOD, ctx=[61, 32], bo=[3, 0], cb=[1, 4, 1])
+    assert st == b.OK, msg
+    st, msg = _status(GOOD, ctx=[61, 29], q0=[0, 29], bo=[3, 3])
+    assert st == b.OK, msg
 
 
 def test_null_and_alignment_checks():
@@ -175,6 +190,46 @@ def test_plan_encodes_oracle_visibility_exhaustive():
     assert n > 100
 
 
+def test_plan_encodes_shifted_grid_and_causal_exhaustive():
+    n = 0
+    for B in (2, 3, 5):
+        for nb in range(1, 4):
+            for o in range(B):
+                C = nb * B - o
+                for causal in (False, True):
+                    for q0 in sorted({0, C, min(C, B - o), max(0, C - B)}):
+                        for cv in [[]] + [[x] for x in range(nb + 1)] + [[nb, 0]]:
+                            if (C - q0) + len(cv) * B == 0:
+                                continue
+                            _check_plan(Meta([C], [q0], [cv], B, 2, 1, 64, "bf16", block_offset=[o],
+                                             clean_causal=causal))
+                            n += 1
+    assert n > 150
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_plan_encodes_shifted_and_causal_random(seed):
+    rng = np.random.default_rng(900 + seed)
+    meta = random_meta(rng, hq=8, hkv=2, d=64, max_segments=4, max_blocks=8,
+                       block_sizes=(2, 4, 16, 32, 48, 64, 160), max_canvases=4, dtype="bf16",
+                       offsets=True, clean_causal=bool(seed % 2))
+    _check_plan(meta)
+    _check_plan(meta, b.FLAG_FORCE_SPLIT)
+
+
+def test_commit_folded_step_plan():
+    # the finished block (queries from C - B, token-causal) and the next canvas
+    # over a 2048-token context, grid offset 17 (a 2031-token prompt + blocks)
+    meta = Meta([2048 - 17], [2048 - 17 - 32], [[64]], 32, 32, 8, 128, "bf16",
+                block_offset=[17], clean_causal=True)
+    p, _rec = _check_plan(meta)
+    assert p.kernel_names(True)[1] == "dkdv_masked"
+    # pairs: the canvas sees the whole context and itself; the block is causal
+    C = 2048 - 17
+    want = 32 * (C + 32) + sum(t + 1 for t in range(C - 32, C))
+    assert p.visible_pairs == want
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_plan_encodes_oracle_visibility_random(seed):
     rng = np.random.default_rng(500 + seed)
@@ -243,11 +298,19 @@ def test_metadata_grows_with_tiles_not_n_squared():
     ([288, 192], [0, 96], 96, 12, 4, "bf16", "dkdv_masked"),   # G = 3 does not divide 64
     ([256, 128], [0, 96], 32, 8, 8, "bf16", "dkdv_masked"),    # 64 tokens per chunk > block
     ([256, 128], [0, 40], 32, 32, 8, "fp32", "dkdv"),          # fp32 has one dK/dV kernel
+    # grid offsets: a multiple of 32 with ranges at (shifted) block starts keeps
+    # the unmasked program; any other offset or token-causal rows need limits
+    ([224, 96], [32, 96], (64, [32, 32]), 32, 8, "bf16", "dkdv"),
+    ([240, 112], [0, 112], (32, [16, 16]), 32, 8, "bf16", "dkdv_masked"),
+    ([256, 128], [0, 128], (32, None, "causal"), 32, 8, "bf16", "dkdv_masked"),
 ])
 def test_dkdv_variant_selection(ctx, q0, B, hq, hkv, dt, want):
     """The unmasked dK/dV program is only chosen when every (64-row query chunk,
     32-key group) pair is either wholly visible or wholly hidden."""
-    meta = Meta(ctx, q0, [[1], [0, 2]], B, hq, hkv, 64, dt)
+    offs, causal = None, False
+    if isinstance(B, tuple):
+        B, offs, causal = B[0], B[1], len(B) > 2
+    meta = Meta(ctx, q0, [[1], [0, 2]], B, hq, hkv, 64, dt, block_offset=offs, clean_causal=causal)
     names = b.Plan(meta).kernel_names(True)
     # bf16: dQ (with the row terms) first, then dK/dV; fp32: row terms, dK/dV, dQ
     assert names[1] == want
