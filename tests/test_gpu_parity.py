@@ -205,8 +205,14 @@ def test_random_packs_shifted_grid(case, causal):
     max_blocks = max(2, min(12, 600 // B))
     meta = W.random_meta(rng, max_segments=3, max_blocks=max_blocks, block_sizes=(B,), max_canvases=4,
                          hq=hq, hkv=hkv, d=D, dtype=dt, offsets=True, clean_causal=causal)
+    # Token-causal rows give the first keys of a context weights near 1/i from
+    # every later row i, so their dV reaches ~G * ln(n) * |dO| (9.0 with unit dO
+    # on the first pack here); bf16 output rounding alone is then 2^-5 at |x| >= 8,
+    # above the 2e-2 bar. Causal packs (block size 1 is causal too) draw dO at a
+    # quarter of the usual scale.
     G = hq // hkv
-    wl = W.random_workload(rng, meta, sigma=sigma, do_sigma=min(1.0, (4.0 / G) ** 0.5))
+    do_sigma = min(1.0, (4.0 / G) ** 0.5) * (0.25 if (causal or B == 1) else 1.0)
+    wl = W.random_workload(rng, meta, sigma=sigma, do_sigma=do_sigma)
     _say(f"case shifted B={B} hq={hq} hkv={hkv} D={D} {dt} causal={causal} offsets={meta.block_offset} "
          f"tq={meta.tq} tk={meta.tk}")
     gpu, _ = run_gpu(wl)
