@@ -64,6 +64,8 @@ def parse():
                     help="summarise rocprofv3 CSV output under the DIRs (no GPU work) and exit")
     ap.add_argument("--summary-out", default=None, help="with --summarize: write the text summary here")
     ap.add_argument("--command", default="", help="with --summarize: the command that produced DIR")
+    ap.add_argument("--pack", action="store_true",
+                    help="time the host packer (replay rows + largest-cost-first groups) instead; CPU only")
     ap.add_argument("--traffic-key", default=None,
                     help="with --summarize: record per-launch HBM bytes of KERNEL@WORKLOAD in "
                          "profiles/traffic.json, e.g. dkdv@3")
@@ -239,10 +241,65 @@ def cpu_baseline(wl, budget_s):
     }
 
 
+def pack_bench(args):
+    """Host packer on a synthetic replay batch: 256 responses, contexts of 8..128
+    blocks of 32 behind a prompt that ends U[0, 32) tokens into a block, 4..16
+    captured denoising steps per block, 1..32 supervised positions and 0..7
+    resident pages per state, cost weights (1, 1, 4), 8 data-parallel groups."""
+    import numpy as np
+
+    from block_diffusion_attention_amd import binding as b
+
+    rng = np.random.default_rng(args.seed if args.seed is not None else 11)
+    B, R, G = 32, 256, 8
+    nb = rng.integers(8, 129, size=R)
+    off = rng.integers(0, B, size=R)
+    clean = nb * B - off
+    steps = rng.integers(4, 17, size=int(nb.sum()))
+    resp = np.repeat(np.repeat(np.arange(R), nb), steps)
+    block = np.repeat(np.concatenate([np.arange(1, n + 1) for n in nb]), steps)
+    step = np.concatenate([np.arange(k) for k in steps])
+    N = len(resp)
+    sup = rng.integers(1, B + 1, size=N)
+    pages = rng.integers(0, 8, size=N)
+    args_ = (clean, resp, block, step, B, G)
+    kw = dict(block_offset=off, state_supervised=sup, state_pages=pages, w_tokens=1, w_supervised=1, w_pages=4)
+    times = []
+    for _ in range(args.warmup + args.steps):
+        t0 = time.perf_counter()
+        p = b.pack(*args_, **kw)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times[args.warmup:]))
+    loads = p["group_cost"].astype(np.float64)
+    out = {
+        "metric": "host packer: captured states packed into replay rows and assigned per second",
+        "value": round(N / t, 1), "unit": "states/s", "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_call": round(t * 1e3, 3),
+        "data": "synthetic",
+        "config": {"workload": " ".join(pack_bench.__doc__.split(":", 1)[1].split()),
+                   "states": N, "rows": int(p["n_rows"]), "groups": G,
+                   "note": "wall time includes the Python argument marshalling of the binding"},
+        "balance": {"max_over_mean_group_cost": round(float(loads.max() / loads.mean()), 5)},
+    }
+    if not args.no_cpu:
+        from oracle import bd_pack_oracle as po
+        states = [{"resp": int(r), "block": int(bl), "step": int(k), "supervised": int(su), "pages": int(pg)}
+                  for r, bl, k, su, pg in zip(resp, block, step, sup, pages)]
+        t0 = time.perf_counter()
+        po.pack(clean.tolist(), off.tolist(), states, B, G, 1, 1, 4)
+        to = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(N / to, 1), "unit": "states/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole batch ({N} states), pure Python, {to:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args)
+        return
+    if args.pack:
+        pack_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",

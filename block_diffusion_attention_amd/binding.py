@@ -75,9 +75,53 @@ for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_a
            "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_destroy"):
     getattr(_lib, _f).restype = ctypes.c_int
 
+
+class PackDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_responses", ctypes.c_int32),
+        ("clean_len", _i32p),
+        ("block_offset", _i32p),
+        ("num_states", ctypes.c_int32),
+        ("state_resp", _i32p),
+        ("state_block", _i32p),
+        ("state_step", _i32p),
+        ("state_supervised", _i32p),
+        ("state_pages", _i32p),
+        ("block_size", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("w_tokens", ctypes.c_int32),
+        ("w_supervised", ctypes.c_int32),
+        ("w_pages", ctypes.c_int32),
+    ]
+
+
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+class PackOut(ctypes.Structure):
+    _fields_ = [
+        ("state_row", _i32p),
+        ("row_resp", _i32p),
+        ("row_step", _i32p),
+        ("row_ctx_len", _i32p),
+        ("row_group", _i32p),
+        ("row_cost", _i64p),
+        ("row_state_offsets", _i32p),
+        ("row_states", _i32p),
+        ("group_row_offsets", _i32p),
+        ("group_rows", _i32p),
+        ("group_cost", _i64p),
+        ("n_rows", ctypes.c_int32),
+    ]
+
+
+_lib.bd_attn_pack.argtypes = [ctypes.POINTER(PackDesc), ctypes.POINTER(PackOut)]
+_lib.bd_attn_pack.restype = ctypes.c_int
+
 EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
             "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
-            "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version")
+            "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version",
+            "bd_attn_pack")
 
 
 class BdAttnError(RuntimeError):
@@ -98,6 +142,42 @@ def version() -> str:
 def _arr(vals):
     a = (ctypes.c_int32 * max(1, len(vals)))(*[int(x) for x in vals])
     return a
+
+
+def pack(clean_len, state_resp, state_block, state_step, block_size, num_groups, *, block_offset=None,
+         state_supervised=None, state_pages=None, w_tokens=1, w_supervised=0, w_pages=0):
+    """Replay rows and their largest-cost-first assignment to data-parallel groups
+    (bd_attn_pack). Returns a dict of numpy arrays trimmed to the row count."""
+    import numpy as np
+    R, N, G = len(clean_len), len(state_resp), int(num_groups)
+    d = PackDesc()
+    d.num_responses, d.num_states, d.block_size, d.num_groups = R, N, int(block_size), G
+    d.w_tokens, d.w_supervised, d.w_pages = int(w_tokens), int(w_supervised), int(w_pages)
+    keep = {}
+    for n, v in (("clean_len", clean_len), ("state_resp", state_resp), ("state_block", state_block),
+                 ("state_step", state_step), ("block_offset", block_offset),
+                 ("state_supervised", state_supervised), ("state_pages", state_pages)):
+        if v is not None:
+            keep[n] = np.ascontiguousarray(np.asarray(v, dtype=np.int64).astype(np.int32))
+            setattr(d, n, keep[n].ctypes.data_as(_i32p))
+    n1 = max(1, N)
+    bufs = {n: np.zeros(n1, np.int32) for n in ("state_row", "row_resp", "row_step", "row_ctx_len", "row_group",
+                                                "row_states", "group_rows")}
+    bufs["row_cost"] = np.zeros(n1, np.int64)
+    bufs["row_state_offsets"] = np.zeros(n1 + 1, np.int32)
+    bufs["group_row_offsets"] = np.zeros(G + 1, np.int32)
+    bufs["group_cost"] = np.zeros(max(1, G), np.int64)
+    o = PackOut()
+    for n, a in bufs.items():
+        setattr(o, n, a.ctypes.data_as(_i64p if a.dtype == np.int64 else _i32p))
+    _check(_lib.bd_attn_pack(ctypes.byref(d), ctypes.byref(o)))
+    nr = o.n_rows
+    res = {"n_rows": nr, "state_row": bufs["state_row"][:N], "row_states": bufs["row_states"][:N],
+           "row_state_offsets": bufs["row_state_offsets"][:nr + 1], "group_rows": bufs["group_rows"][:nr],
+           "group_row_offsets": bufs["group_row_offsets"], "group_cost": bufs["group_cost"][:G]}
+    for n in ("row_resp", "row_step", "row_ctx_len", "row_group", "row_cost"):
+        res[n] = bufs[n][:nr]
+    return res
 
 
 class Plan:

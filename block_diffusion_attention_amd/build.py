@@ -14,7 +14,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_vt.hip", "attn_bwd.hip", "attn_f32.hip", "bd_attn_abi.hip"]
-CXX_SOURCES = ["planner.cpp"]
+CXX_SOURCES = ["planner.cpp", "packer.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # packed fp32 VALU instructions stay disabled for all device code
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -8,6 +8,7 @@
 
 #include "../../include/bd_attn.h"
 #include "kernels.h"
+#include "packer.h"
 #include "planner.h"
 
 using bdattn::Plan;
@@ -303,6 +304,17 @@ const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int3
 
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan) {
   delete plan;
+  return BD_ATTN_OK;
+}
+
+bd_attn_status bd_attn_pack(const bd_pack_desc* desc, bd_pack_out* out) {
+  std::string err;
+  try {
+    const bd_attn_status st = bdattn::build_pack(desc, out, &err);
+    if (st != BD_ATTN_OK) return fail(st, err);
+  } catch (const std::bad_alloc&) {
+    return fail(BD_ATTN_EINVAL, "out of host memory while packing");
+  }
   return BD_ATTN_OK;
 }
 

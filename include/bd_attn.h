@@ -201,6 +201,65 @@ int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward);
  * is static. */
 const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int32_t i);
 
+/* ---------------------------------------------------------------------------
+ * Host packer (ORL section 3.2 "Packed and cost-balanced state training",
+ * appendix D.3): builds replay rows from captured denoising states and assigns
+ * them to data-parallel groups. A row holds one response's clean tokens once,
+ * followed by the states of its blocks captured at the same denoising step k
+ * (each state a canvas at its block index), so every state reuses the clean
+ * context before it. A row keeps the clean tokens its states can see: up to
+ * max_b (b*B - o) of its states (at most the response's clean length). Rows are
+ * ordered by (response, step); each state, and so each of its supervised labels,
+ * belongs to exactly one row.
+ * Cost proxy of a row (integer): w_tokens * (clean tokens + states * B)
+ *   + w_supervised * (sum of supervised positions) + w_pages * (sum of pages).
+ * Assignment: rows in decreasing cost (ties: lower row number first), each to
+ * the group with the smallest total cost so far (ties: lowest group index) --
+ * deterministic largest-cost-first. A group's rows, in that order, are the
+ * segments of one bd_attn_desc (ctx_len = row_ctx_len, ctx_q_begin = 0,
+ * canvas_block_idx = the blocks of the row's states, block_offset = the
+ * response's offset, or 0 for a row that holds no clean token).
+ * Host-only; touches no device memory.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t num_responses;            /* R >= 1 */
+  const int32_t* clean_len;         /* host [R]: clean tokens C_r of each response */
+  const int32_t* block_offset;      /* host [R] or NULL (= 0): grid offset o_r, 0 <= o_r < B,
+                                       C_r + o_r a multiple of B (as in bd_attn_desc) */
+  int32_t num_states;               /* N >= 0 */
+  const int32_t* state_resp;        /* host [N]: response of each state, 0..R-1 */
+  const int32_t* state_block;       /* host [N]: block index b, 0 <= b <= (C_r + o_r) / B */
+  const int32_t* state_step;        /* host [N]: denoising step k >= 0 */
+  const int32_t* state_supervised;  /* host [N] or NULL (= B): supervised positions, 0..B */
+  const int32_t* state_pages;       /* host [N] or NULL (= 0): resident residual pages >= 0 */
+  int32_t block_size;               /* B >= 1 */
+  int32_t num_groups;               /* data-parallel groups G >= 1 */
+  int32_t w_tokens;                 /* cost weights >= 0 */
+  int32_t w_supervised;
+  int32_t w_pages;
+} bd_pack_desc;
+
+/* Outputs, every array host memory owned by the caller; sizes in brackets
+ * (rows never outnumber states, so N bounds every row array). */
+typedef struct {
+  int32_t* state_row;           /* [N]   row of each state */
+  int32_t* row_resp;            /* [N]   response of row i (i < n_rows) */
+  int32_t* row_step;            /* [N]   its step k */
+  int32_t* row_ctx_len;         /* [N]   clean tokens it holds */
+  int32_t* row_group;           /* [N]   the group it is assigned to */
+  int64_t* row_cost;            /* [N]   its cost proxy */
+  int32_t* row_state_offsets;   /* [N+1] states of row i: row_states[off[i] .. off[i+1]) */
+  int32_t* row_states;          /* [N]   state indices, input order within a row */
+  int32_t* group_row_offsets;   /* [G+1] rows of group g: group_rows[off[g] .. off[g+1]) */
+  int32_t* group_rows;          /* [N]   in assignment order */
+  int64_t* group_cost;          /* [G]   total cost per group */
+  int32_t n_rows;               /* written: number of rows */
+} bd_pack_out;
+
+/* Builds the rows and the assignment. Errors: EINVAL on bad input (message in
+ * bd_attn_last_error), outputs then unspecified. */
+bd_attn_status bd_attn_pack(const bd_pack_desc* desc, bd_pack_out* out);
+
 /* Frees a plan (NULL is accepted). */
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan);
 

@@ -250,6 +250,29 @@ def test_shifted_grid_unmasked_dkdv():
     _compare(wl, gpu, run_oracle(wl))
 
 
+def test_packed_group_from_the_packer():
+    # captured states of 12 responses -> replay rows -> largest-cost-first groups;
+    # the attention of one group's pack against the oracle
+    from pack_common import group_meta
+    rng = np.random.default_rng(608)
+    B, R = 32, 12
+    nb = rng.integers(2, 12, size=R)
+    off = [int(x) for x in rng.integers(0, B, size=R)]
+    clean = [int(n) * B - o for n, o in zip(nb, off)]
+    resp, block, step = [], [], []
+    for r in range(R):
+        for bl in range(1, int(nb[r]) + 1):
+            for k in range(int(rng.integers(1, 4))):
+                resp.append(r); block.append(bl); step.append(k)
+    p = b.pack(clean, resp, block, step, B, 4, block_offset=off)
+    g = int(np.argmax(p["group_cost"]))
+    meta = group_meta(p, g, clean, off, block, B, 8, 2, 128, "bf16")
+    wl = W.random_workload(rng, meta, sigma=0.3)
+    _say(f"case packer group {g}: {meta.num_segments} rows tq={meta.tq} tk={meta.tk}")
+    gpu, _ = run_gpu(wl)
+    _compare(wl, gpu, run_oracle(wl))
+
+
 @pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_forced_split_matches_oracle(flags):
     rng = np.random.default_rng(42)
