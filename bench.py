@@ -64,6 +64,8 @@ def parse():
                     help="summarise rocprofv3 CSV output under the DIRs (no GPU work) and exit")
     ap.add_argument("--summary-out", default=None, help="with --summarize: write the text summary here")
     ap.add_argument("--command", default="", help="with --summarize: the command that produced DIR")
+    ap.add_argument("--aec", action="store_true",
+                    help="time the normalized-entropy / AEC reduction over vocabulary logits instead")
     ap.add_argument("--pack", action="store_true",
                     help="time the host packer (replay rows + largest-cost-first groups) instead; CPU only")
     ap.add_argument("--traffic-key", default=None,
@@ -88,6 +90,7 @@ KERNEL_SOURCES = {
     "dq": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "bwd_pre": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "combine": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "aec_entropy": ["aec.hip", "aec.h"],
 }
 
 
@@ -106,7 +109,8 @@ def traffic_from_profiles(kernel, workload):
 
 
 KERNEL_SYMBOLS = {"fwd": "fwd_", "combine": "combine_kernel", "bwd_pre": "bwd_pre_kernel",
-                  "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel", "transpose_v": "transpose_v_kernel"}
+                  "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel", "transpose_v": "transpose_v_kernel",
+                  "aec_entropy": "aec_entropy_kernel"}
 COPY_SYMBOL = "MulFunctor"
 
 
@@ -293,6 +297,79 @@ def pack_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def aec_bench(args):
+    """Normalized entropy + AEC loss over the logits of the canvas positions of a
+    replay batch: 16 states of 32 positions, a 151,936-entry vocabulary, bf16
+    logits N(0, tau^2) with tau ~ U[0.5, 6] per row, seed 7."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_attention_amd import binding as b
+    from block_diffusion_attention_amd import workloads as W
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.aec_workload(7 if args.seed is None else args.seed)
+    N, V = wl.logits.shape[0], wl.vocab
+    logits = torch.from_numpy(wl.logits).to(dev).to(torch.bfloat16).contiguous()
+    t = lambda x, ty: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(ty)
+    kw = dict(unresolved=t(wl.unresolved, torch.uint8), state_rows=t(wl.state_rows, torch.int32),
+              pair_next=t(wl.pair_next, torch.int32), pair_h_source=t(wl.pair_h_source, torch.float32),
+              pair_weight=t(wl.pair_weight, torch.float32), rho=wl.rho, gate_max=wl.gate_max)
+    d = b.aec_desc(N, V, logits.shape[1], "bf16", len(wl.state_rows) - 1, len(wl.pair_next), wl.rho, wl.gate_max)
+    nk = b.aec_kernels(d)
+    names = ["aec_entropy"] + (["aec_merge"] if nk == 3 else []) + ["aec_reduce"]
+    ws = torch.empty(max(16, b.aec_workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        b.aec_fwd(logits, V, ws=ws, **kw)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    for e in [x for row in ev for x in row]:
+        e.record()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        b.aec_fwd(logits, V, events=ev[i], ws=ws, **kw)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    avg = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)])) for j, n in enumerate(names)}
+    logit_bytes = float(N) * V * 2
+    work = logit_bytes + 8.0 * N + N           # logits in; unresolved flags in; lse and hbar out
+    dom = "aec_entropy"
+    achieved = work / (avg[dom] * 1e-3) / 1e9
+    out = {
+        "metric": "normalized-entropy + AEC reduction over vocabulary logits: logit bytes per second",
+        "value": round(logit_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": " ".join(aec_bench.__doc__.split()), "rows": N, "vocab": V,
+                   "states": len(wl.state_rows) - 1, "pairs": len(wl.pair_next)},
+        "kernels_ms": {n: round(x, 4) for n, x in avg.items()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "kernel": dom, "work_per_launch": work,
+                     "avg_launch_ms": round(avg[dom], 4), "traffic": None},
+    }
+    if not args.no_cpu:
+        from oracle import bd_aec_oracle as ao
+        rows = 64
+        t0 = time.perf_counter()
+        ao.lse_and_entropy(wl.logits[:rows, :V])
+        to = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(rows * V * 2 / to / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{rows} of {N} rows (entropy and normalizer), "
+                                                           f"fp64 numpy, {to:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -300,6 +377,9 @@ def main():
         return
     if args.pack:
         pack_bench(args)
+        return
+    if args.aec:
+        aec_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",

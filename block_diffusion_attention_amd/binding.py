@@ -118,10 +118,32 @@ class PackOut(ctypes.Structure):
 _lib.bd_attn_pack.argtypes = [ctypes.POINTER(PackDesc), ctypes.POINTER(PackOut)]
 _lib.bd_attn_pack.restype = ctypes.c_int
 
+class AecDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_rows", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("row_stride", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("num_states", ctypes.c_int32),
+        ("num_pairs", ctypes.c_int32),
+        ("rho", ctypes.c_float),
+        ("gate_max", ctypes.c_float),
+    ]
+
+
+_lib.bd_aec_workspace.argtypes = [ctypes.POINTER(AecDesc), ctypes.POINTER(_sz)]
+_lib.bd_aec_workspace.restype = ctypes.c_int
+_lib.bd_aec_fwd.argtypes = [ctypes.POINTER(AecDesc)] + [_vp] * 12
+_lib.bd_aec_fwd.restype = ctypes.c_int
+_lib.bd_aec_fwd_timed.argtypes = [ctypes.POINTER(AecDesc)] + [_vp] * 13 + [ctypes.c_int]
+_lib.bd_aec_fwd_timed.restype = ctypes.c_int
+_lib.bd_aec_kernels.argtypes = [ctypes.POINTER(AecDesc)]
+_lib.bd_aec_kernels.restype = ctypes.c_int32
+
 EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
             "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
             "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version",
-            "bd_attn_pack")
+            "bd_attn_pack", "bd_aec_workspace", "bd_aec_fwd", "bd_aec_fwd_timed", "bd_aec_kernels")
 
 
 class BdAttnError(RuntimeError):
@@ -337,3 +359,55 @@ class BdAttnFunction(torch.autograd.Function):
 
 def attention(q, k, v, plan: Plan):
     return BdAttnFunction.apply(q, k, v, plan)
+
+
+# ------------------------------------------------ normalized entropy / AEC loss
+
+def aec_desc(num_rows, vocab, row_stride, dtype, num_states, num_pairs, rho, gate_max) -> AecDesc:
+    d = AecDesc()
+    d.num_rows, d.vocab, d.row_stride = int(num_rows), int(vocab), int(row_stride)
+    d.dtype = BF16 if dtype in ("bf16", torch.bfloat16, BF16) else FP32
+    d.num_states, d.num_pairs = int(num_states), int(num_pairs)
+    d.rho, d.gate_max = float(rho), float(gate_max)
+    return d
+
+
+def aec_kernels(d: AecDesc) -> int:
+    return int(_lib.bd_aec_kernels(ctypes.byref(d)))
+
+
+def aec_workspace_bytes(d: AecDesc) -> int:
+    n = _sz()
+    _check(_lib.bd_aec_workspace(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def aec_fwd(logits, vocab, unresolved, state_rows, pair_next, pair_h_source, pair_weight, rho, gate_max,
+            events=None, ws=None):
+    """Per-row log-normalizer and normalized entropy, per-state means over the
+    unresolved rows and the AEC loss (bd_aec_fwd). logits: [N, row_stride] bf16 or
+    fp32 device tensor whose first ``vocab`` columns are the vocabulary; the other
+    arguments are device tensors (uint8, int32, int32, float32, float32).
+    Returns (lse [N], hbar [N], h_state [S], loss [1]), all float32."""
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [N, row_stride] tensor")
+    N, stride = logits.shape
+    S = state_rows.numel() - 1 if state_rows is not None else 0
+    P = pair_next.numel() if pair_next is not None else 0
+    d = aec_desc(N, vocab, stride, logits.dtype, S, P, rho, gate_max)
+    dev = logits.device
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    hbar = torch.empty(N, dtype=torch.float32, device=dev)
+    h_state = torch.empty(max(S, 1), dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    nbytes = aec_workspace_bytes(d)
+    if nbytes and ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    args = [ctypes.byref(d), _ptr(logits), _ptr(unresolved), _ptr(state_rows), _ptr(pair_next), _ptr(pair_h_source),
+            _ptr(pair_weight), _ptr(lse), _ptr(hbar), _ptr(h_state), _ptr(loss), _ptr(ws), _stream(dev)]
+    if events is None:
+        _check(_lib.bd_aec_fwd(*args))
+    else:
+        ev, n = _events_arg(events)
+        _check(_lib.bd_aec_fwd_timed(*args, ev, n))
+    return lse, hbar, h_state[:S], loss

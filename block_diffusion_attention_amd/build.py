@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libbdattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_vt.hip", "attn_bwd.hip", "attn_f32.hip", "bd_attn_abi.hip"]
+HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_vt.hip", "attn_bwd.hip", "attn_f32.hip", "aec.hip", "bd_attn_abi.hip"]
 CXX_SOURCES = ["planner.cpp", "packer.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # packed fp32 VALU instructions stay disabled for all device code

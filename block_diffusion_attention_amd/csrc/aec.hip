@@ -1,0 +1,232 @@
+// Normalized entropy of vocabulary distributions and the adjacent-entropy-
+// contraction (AEC) loss, for gfx950.
+//
+// ORL paper, paragraph "Learning how fast to refine": the normalized token
+// entropy -sum_v p_v log p_v / log|V| of a softmax over the vocabulary, its mean
+// over the unresolved positions of a state, and the hinge
+// max(0, H_next - (1 - rho) H_source)^2 of an adjacent pair of states; the
+// appendix paragraph on valid AEC pairs gives the pair weights w, fixed before
+// the gate g, and the normalizer D = sum w g (loss 0 when D = 0). The natural-log
+// normalizer of every row is written as well (appendix F.1 "Kernels": a later
+// softmax over the same logits reuses it).
+//
+// The logits are read once. Each workgroup streams a contiguous part of one
+// row with 16-byte loads, four in flight per thread, and keeps per thread a
+// running (max m, S = sum 2^d, U = sum 2^d d) over d = x log2(e) - m, so that
+// log2 Z = m + log2 S and the entropy in bits is log2 S - U / S. Partial
+// triples of several workgroups (short batches split each row) merge exactly:
+// moving a triple to a larger max M scales S by 2^(m-M) and U to
+// 2^(m-M) (U + (m-M) S). Every sum runs in a fixed order: no atomics.
+#include "aec.h"
+
+namespace bdattn {
+
+namespace {
+
+constexpr float kL2E = 1.4426950408889634f;
+constexpr float kLN2 = 0.6931471805599453f;
+constexpr int kThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct Acc {
+  float m, s, u;
+};
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void merge(Acc& a, const Acc& b) {
+  if (b.s == 0.f) return;
+  if (a.s == 0.f) { a = b; return; }
+  const float m = fmaxf(a.m, b.m);
+  const float da = a.m - m, db = b.m - m;
+  const float fa = ex2(da), fb = ex2(db);
+  a.u = fa * fmaf(da, a.s, a.u) + fb * fmaf(db, b.s, b.u);
+  a.s = fa * a.s + fb * b.s;
+  a.m = m;
+}
+
+// Adds K logits (natural units); the running max only moves up.
+template <int K>
+__device__ __forceinline__ void add(Acc& a, const float (&x)[K]) {
+  float mx = x[0];
+#pragma unroll
+  for (int j = 1; j < K; ++j) mx = fmaxf(mx, x[j]);
+  const float mv = mx * kL2E;
+  if (mv > a.m) {
+    if (a.s > 0.f) {
+      const float d = a.m - mv, f = ex2(d);
+      a.u = f * fmaf(d, a.s, a.u);
+      a.s *= f;
+    }
+    a.m = mv;
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const float d = fmaf(x[j], kL2E, -a.m);
+    const float e = ex2(d);
+    a.s += e;
+    a.u = fmaf(e, d, a.u);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack(const u32x4& w, float (&x)[BF16 ? 8 : 4]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+      x[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+    }
+  } else {
+    // whole-vector reinterpretation: a bit cast of one element of a vector
+    // value is compiled here as a cast of element 0
+    const f32x4 f = __builtin_bit_cast(f32x4, w);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = f[k];
+  }
+}
+
+__device__ __forceinline__ void finish(const Acc& a, int vocab, float* lse, float* hbar) {
+  const float l2s = log2f(a.s);
+  *lse = (a.m + l2s) * kLN2;
+  *hbar = (l2s - a.u / a.s) / log2f((float)vocab);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) aec_entropy_kernel(AecArgs a) {
+  constexpr int EPV = BF16 ? 8 : 4;                   // elements per 16-byte load
+  const int row = blockIdx.x / a.nsplit, split = blockIdx.x - row * a.nsplit;
+  const int64_t c0 = (int64_t)split * a.chunk;
+  const int64_t c1 = min((int64_t)a.vocab, c0 + a.chunk);
+  const int64_t nvec = (c1 - c0) / EPV;               // whole vectors; c0 is a multiple of EPV
+  const int tail = (int)((c1 - c0) - nvec * EPV);     // only the last split has one
+  const char* rowp = static_cast<const char*>(a.logits) + (row * a.row_stride + c0) * (BF16 ? 2 : 4);
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
+
+  Acc acc{-INFINITY, 0.f, 0.f};
+  int64_t i = threadIdx.x;
+  for (; i + 3 * kThreads < nvec; i += 4 * kThreads) {
+    u32x4 w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = __builtin_nontemporal_load(vp + i + k * kThreads);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float x[EPV];
+      unpack<BF16>(w[k], x);
+      add<EPV>(acc, x);
+    }
+  }
+  for (; i < nvec; i += kThreads) {
+    float x[EPV];
+    unpack<BF16>(__builtin_nontemporal_load(vp + i), x);
+    add<EPV>(acc, x);
+  }
+  if (threadIdx.x < tail) {
+    float x[1];
+    if constexpr (BF16) {
+      const uint16_t b = reinterpret_cast<const uint16_t*>(rowp)[nvec * EPV + threadIdx.x];
+      x[0] = __builtin_bit_cast(float, (uint32_t)b << 16);
+    } else {
+      x[0] = reinterpret_cast<const float*>(rowp)[nvec * EPV + threadIdx.x];
+    }
+    add<1>(acc, x);
+  }
+
+  // workgroup reduction in a fixed order: lanes, then the four waves
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    Acc o{__shfl_xor(acc.m, off), __shfl_xor(acc.s, off), __shfl_xor(acc.u, off)};
+    merge(acc, o);
+  }
+  __shared__ float red[3][kThreads / 64];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][wave] = acc.m; red[1][wave] = acc.s; red[2][wave] = acc.u; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Acc t{red[0][0], red[1][0], red[2][0]};
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) merge(t, Acc{red[0][w], red[1][w], red[2][w]});
+    if (a.nsplit == 1) {
+      finish(t, a.vocab, a.lse + row, a.hbar + row);
+    } else {
+      float* p = a.part + (int64_t)blockIdx.x * 3;
+      p[0] = t.m; p[1] = t.s; p[2] = t.u;
+    }
+  }
+}
+
+// One thread per row: the row's partial triples in split order.
+__global__ void __launch_bounds__(kThreads) aec_merge_kernel(AecArgs a) {
+  const int row = blockIdx.x * kThreads + threadIdx.x;
+  if (row >= a.n_rows) return;
+  const float* p = a.part + (int64_t)row * a.nsplit * 3;
+  Acc t{p[0], p[1], p[2]};
+  for (int k = 1; k < a.nsplit; ++k) merge(t, Acc{p[3 * k], p[3 * k + 1], p[3 * k + 2]});
+  finish(t, a.vocab, a.lse + row, a.hbar + row);
+}
+
+// Mean normalized entropy over the unresolved rows of state s (row order), or
+// NaN when it has none. Row ranges are clamped to [0, N].
+__device__ float state_mean(const AecArgs& a, int s) {
+  const int lo = min(max(a.state_rows[s], 0), a.n_rows);
+  const int hi = min(max(a.state_rows[s + 1], lo), a.n_rows);
+  float sum = 0.f;
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i)
+    if (a.unresolved[i]) { sum += a.hbar[i]; ++cnt; }
+  return cnt ? sum / (float)cnt : __builtin_nanf("");
+}
+
+// One workgroup: per-state means, then the gated, weighted hinge of every pair.
+// A pair is valid when its next state index lies in [0, S), that state has an
+// unresolved row and the source mean is finite.
+__global__ void __launch_bounds__(kThreads) aec_reduce_kernel(AecArgs a) {
+  for (int s = threadIdx.x; s < a.n_states; s += kThreads) a.h_state[s] = state_mean(a, s);
+  float num = 0.f, den = 0.f;
+  for (int p = threadIdx.x; p < a.n_pairs; p += kThreads) {
+    const int n = a.pair_next[p];
+    const float hs = a.pair_h_source[p];
+    if (n < 0 || n >= a.n_states || !__builtin_isfinite(hs)) continue;
+    const float hn = state_mean(a, n);
+    if (!__builtin_isfinite(hn) || !(hs <= a.gate_max)) continue;
+    const float w = a.pair_weight[p];
+    const float h = fmaxf(0.f, hn - (1.f - a.rho) * hs);
+    num = fmaf(w * h, h, num);
+    den += w;
+  }
+  __shared__ float rn[kThreads], rd[kThreads];
+  rn[threadIdx.x] = num;
+  rd[threadIdx.x] = den;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      rn[threadIdx.x] += rn[threadIdx.x + off];
+      rd[threadIdx.x] += rd[threadIdx.x + off];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.loss[0] = rd[0] > 0.f ? rn[0] / rd[0] : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_aec_entropy(const AecArgs& a, bool bf16, hipStream_t s) {
+  const int grid = a.n_rows * a.nsplit;
+  if (bf16) hipLaunchKernelGGL(aec_entropy_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(aec_entropy_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_aec_merge(const AecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(aec_merge_kernel, dim3((a.n_rows + kThreads - 1) / kThreads), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_aec_reduce(const AecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(aec_reduce_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bdattn

@@ -2,11 +2,14 @@
 // Every entry point returns a status; no exception crosses the boundary.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cstring>
 #include <new>
 #include <string>
 
 #include "../../include/bd_attn.h"
+#include "aec.h"
 #include "kernels.h"
 #include "packer.h"
 #include "planner.h"
@@ -305,6 +308,111 @@ const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int3
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan) {
   delete plan;
   return BD_ATTN_OK;
+}
+
+namespace {
+
+// Validated AEC launch geometry: workgroups per row and entries per split.
+struct AecGeom {
+  int nsplit = 1;
+  int64_t chunk = 0;
+  size_t ws = 0;
+};
+
+bd_attn_status aec_geom(const bd_aec_desc* d, AecGeom* g) {
+  if (!d) return fail(BD_ATTN_EINVAL, "desc is NULL");
+  if (d->num_rows < 1) return fail(BD_ATTN_EINVAL, "num_rows must be >= 1");
+  if (d->vocab < 2) return fail(BD_ATTN_EINVAL, "vocab must be >= 2");
+  if (d->dtype != BD_ATTN_BF16 && d->dtype != BD_ATTN_FP32) return fail(BD_ATTN_EINVAL, "unknown dtype");
+  const int epv = d->dtype == BD_ATTN_BF16 ? 8 : 4;
+  if (d->row_stride < d->vocab || d->row_stride % epv)
+    return fail(BD_ATTN_EINVAL, "row_stride must be >= vocab and a multiple of 8 (bf16) or 4 (fp32)");
+  if (d->num_states < 0 || d->num_pairs < 0) return fail(BD_ATTN_EINVAL, "num_states and num_pairs must be >= 0");
+  if (!(d->rho >= 0.f && d->rho <= 1.f)) return fail(BD_ATTN_EINVAL, "rho must lie in [0, 1]");
+  if (d->gate_max != d->gate_max) return fail(BD_ATTN_EINVAL, "gate_max must not be NaN");
+  // about 2048 workgroups in all, each split at least kAecMinChunk entries
+  const int64_t V = d->vocab, N = d->num_rows;
+  const int64_t max_split = std::max<int64_t>(1, V / bdattn::kAecMinChunk);
+  const int64_t want = std::min<int64_t>(max_split, std::max<int64_t>(1, (2048 + N - 1) / N));
+  int64_t chunk = (V + want - 1) / want;
+  chunk = (chunk + epv - 1) / epv * epv;
+  const int64_t nsplit = (V + chunk - 1) / chunk;
+  if (N * nsplit > INT32_MAX) return fail(BD_ATTN_EINVAL, "num_rows too large");
+  g->nsplit = (int)nsplit;
+  g->chunk = chunk;
+  g->ws = nsplit > 1 ? (size_t)(N * nsplit * 3 * sizeof(float)) : 0;
+  return BD_ATTN_OK;
+}
+
+bd_attn_status aec_impl(const bd_aec_desc* d, const void* logits, const uint8_t* unresolved,
+                        const int32_t* state_rows, const int32_t* pair_next, const float* pair_h_source,
+                        const float* pair_weight, float* lse, float* hbar, float* h_state, float* loss,
+                        void* ws, bd_attn_stream_t stream, void* const* events, int n_events) {
+  AecGeom g;
+  bd_attn_status st;
+  if ((st = aec_geom(d, &g))) return st;
+  const int nk = g.nsplit > 1 ? 3 : 2;
+  if (events && n_events < nk + 1) return fail(BD_ATTN_EINVAL, "n_events must be at least the number of kernels + 1");
+  if ((st = check_ptr(logits, "logits"))) return st;
+  if (!lse || !hbar || !loss) return fail(BD_ATTN_EINVAL, "lse, hbar and loss must not be NULL");
+  if (d->num_states > 0 && (!unresolved || !state_rows || !h_state))
+    return fail(BD_ATTN_EINVAL, "unresolved, state_rows and h_state must not be NULL when num_states > 0");
+  if (d->num_pairs > 0 && (!pair_next || !pair_h_source || !pair_weight))
+    return fail(BD_ATTN_EINVAL, "the pair arrays must not be NULL when num_pairs > 0");
+  if (g.ws > 0 && !ws) return fail(BD_ATTN_EWORKSPACE, "this call needs a workspace (bd_aec_workspace)");
+  if (ws && !aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
+  bdattn::AecArgs a{};
+  a.logits = logits; a.row_stride = d->row_stride; a.n_rows = d->num_rows; a.vocab = d->vocab;
+  a.nsplit = g.nsplit; a.chunk = g.chunk; a.part = static_cast<float*>(ws);
+  a.lse = lse; a.hbar = hbar; a.unresolved = unresolved; a.state_rows = state_rows;
+  a.n_states = d->num_states; a.pair_next = pair_next; a.pair_h_source = pair_h_source;
+  a.pair_weight = pair_weight; a.n_pairs = d->num_pairs; a.rho = d->rho; a.gate_max = d->gate_max;
+  a.h_state = h_state; a.loss = loss;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const EventMarks ev{events, events ? n_events : 0, s};
+  int mark = 0;
+  if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
+  if ((st = hip_status(bdattn::launch_aec_entropy(a, d->dtype == BD_ATTN_BF16, s), "aec_entropy launch"))) return st;
+  if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
+  if (g.nsplit > 1) {
+    if ((st = hip_status(bdattn::launch_aec_merge(a, s), "aec_merge launch"))) return st;
+    if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
+  }
+  if ((st = hip_status(bdattn::launch_aec_reduce(a, s), "aec_reduce launch"))) return st;
+  return hip_status(ev.mark(mark), "hipEventRecord");
+}
+
+}  // namespace
+
+bd_attn_status bd_aec_workspace(const bd_aec_desc* desc, size_t* ws_bytes) {
+  AecGeom g;
+  bd_attn_status st;
+  if ((st = aec_geom(desc, &g))) return st;
+  if (ws_bytes) *ws_bytes = g.ws;
+  return BD_ATTN_OK;
+}
+
+bd_attn_status bd_aec_fwd(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                          const int32_t* state_rows, const int32_t* pair_next, const float* pair_h_source,
+                          const float* pair_weight, float* lse, float* hbar, float* h_state, float* loss,
+                          void* ws, bd_attn_stream_t stream) {
+  return aec_impl(desc, logits, unresolved, state_rows, pair_next, pair_h_source, pair_weight, lse, hbar,
+                  h_state, loss, ws, stream, nullptr, 0);
+}
+
+bd_attn_status bd_aec_fwd_timed(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                                const int32_t* state_rows, const int32_t* pair_next, const float* pair_h_source,
+                                const float* pair_weight, float* lse, float* hbar, float* h_state, float* loss,
+                                void* ws, bd_attn_stream_t stream, void* const* events, int n_events) {
+  return aec_impl(desc, logits, unresolved, state_rows, pair_next, pair_h_source, pair_weight, lse, hbar,
+                  h_state, loss, ws, stream, events, n_events);
+}
+
+int32_t bd_aec_kernels(const bd_aec_desc* desc) {
+  AecGeom g;
+  const std::string keep = g_last_error;
+  if (aec_geom(desc, &g) != BD_ATTN_OK) { g_last_error = keep; return 0; }
+  return g.nsplit > 1 ? 3 : 2;
 }
 
 bd_attn_status bd_attn_pack(const bd_pack_desc* desc, bd_pack_out* out) {

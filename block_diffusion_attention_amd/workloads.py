@@ -239,3 +239,69 @@ def kv_group_slice(wl: Workload, g: int) -> Workload:
     hs = slice(g * G, (g + 1) * G)
     return Workload(f"{wl.name}[kv{g}]", sub, wl.q[:, hs], wl.k[:, g:g + 1], wl.v[:, g:g + 1],
                     None if wl.do is None else wl.do[:, hs], wl.passes)
+
+
+# ---------------------------------------------------------------- vocabulary logits
+
+AEC_VOCAB = 151936          # a 152k-entry vocabulary (the pages give no size)
+
+
+@dataclasses.dataclass
+class AecWorkload:
+    """Logits of the canvas positions of a replay batch, their unresolved
+    masks, and adjacent state pairs with captured source entropies."""
+    name: str
+    logits: np.ndarray         # [N, row_stride] float32 (exact bf16 values for bf16)
+    vocab: int
+    unresolved: np.ndarray     # [N] uint8
+    state_rows: np.ndarray     # [S+1] int32
+    pair_next: np.ndarray      # [P] int32
+    pair_h_source: np.ndarray  # [P] float32
+    pair_weight: np.ndarray    # [P] float32
+    rho: float
+    gate_max: float
+    dtype: str
+
+
+def aec_workload(seed: int, n_states: int = 16, block: int = 32, vocab: int = AEC_VOCAB,
+                 row_stride: Optional[int] = None, dtype: str = DTYPE_BF16, rho: float = 0.1,
+                 gate_max: float = math.inf, states_per_response: int = 4) -> AecWorkload:
+    """Seeded synthetic logits for ``n_states`` states of ``block`` positions.
+
+    Draw order: per-row temperature tau ~ U[0.5, 6]; logits N(0, 1) * tau; for
+    about one row in ten, one entry raised by U[10, 30]; unresolved flags
+    (probability 0.6; the fourth state fully resolved); captured source means
+    U[0.05, 1] for the pairs (s, s+1) inside each response of
+    ``states_per_response`` consecutive states, weighted 1 / (pairs of the
+    response). Columns past the vocabulary hold 30000, which a kernel that read
+    them would notice.
+    """
+    rng = np.random.default_rng(seed)
+    N = n_states * block
+    width = 8 if dtype == DTYPE_BF16 else 4
+    stride = row_stride or -(-vocab // width) * width
+    tau = rng.uniform(0.5, 6.0, size=N).astype(np.float32)
+    z = rng.standard_normal((N, vocab), dtype=np.float32)
+    z *= tau[:, None]
+    peaky = np.nonzero(rng.random(N) < 0.1)[0]
+    for i in peaky:
+        z[i, int(rng.integers(vocab))] += np.float32(rng.uniform(10.0, 30.0))
+    logits = np.full((N, stride), 30000.0, dtype=np.float32)
+    logits[:, :vocab] = z
+    if dtype == DTYPE_BF16:
+        logits = round_bf16(logits)
+    unresolved = (rng.random(N) < 0.6).astype(np.uint8)
+    if n_states > 3:
+        unresolved[3 * block:4 * block] = 0
+    state_rows = (np.arange(n_states + 1) * block).astype(np.int32)
+    nxt, hs, w = [], [], []
+    for r0 in range(0, n_states, states_per_response):
+        members = list(range(r0, min(n_states, r0 + states_per_response)))
+        pairs = list(zip(members, members[1:]))
+        for _src, dst in pairs:
+            nxt.append(dst)
+            hs.append(rng.uniform(0.05, 1.0))
+            w.append(1.0 / len(pairs))
+    return AecWorkload(f"aec-{n_states}x{block}-V{vocab}-{dtype}", logits, vocab, unresolved, state_rows,
+                       np.array(nxt, np.int32), np.array(hs, np.float32), np.array(w, np.float32),
+                       float(rho), float(gate_max), dtype)

@@ -260,6 +260,65 @@ typedef struct {
  * bd_attn_last_error), outputs then unspecified. */
 bd_attn_status bd_attn_pack(const bd_pack_desc* desc, bd_pack_out* out);
 
+/* ---------------------------------------------------------------------------
+ * Normalized entropy and the adjacent-entropy-contraction (AEC) loss over
+ * vocabulary logits (ORL paper, paragraph "Learning how fast to refine"; the
+ * appendix paragraph on valid AEC pairs, their weights and the gate):
+ *   per row i (a position):  lse_i = log sum_v exp(x_iv)           (natural log)
+ *                            hbar_i = -sum_v p_iv log p_iv / log V, p_i = softmax(x_i)
+ *   per state s:             h_state_s = mean of hbar over its unresolved rows,
+ *                            NaN when it has none
+ *   per pair p (source -> next state):
+ *                            hinge_p = max(0, h_state[next_p] - (1 - rho) h_source_p)^2
+ *   loss = sum_p w_p g_p hinge_p / D, D = sum_p w_p g_p, over valid pairs; 0 if D = 0
+ * A pair is valid when next_p lies in [0, S), that state has an unresolved row
+ * and h_source_p (the captured mean of the source state) is finite; the gate
+ * g_p = 1 if h_source_p <= gate_max (+inf keeps every pair). The combination of
+ * the pairs is a reading: its equation is lost from the pages' text, which fixes
+ * the weights before the gate, D as their gated sum and a zero loss for D = 0.
+ * Logits must be finite. Results are deterministic (no atomics).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t num_rows;                 /* N >= 1 */
+  int32_t vocab;                    /* V >= 2 */
+  int64_t row_stride;               /* elements from one row to the next, >= V; a multiple
+                                       of 8 (bf16) or 4 (fp32) */
+  int32_t dtype;                    /* logits: BD_ATTN_BF16 or BD_ATTN_FP32 */
+  int32_t num_states;               /* S >= 0 */
+  int32_t num_pairs;                /* P >= 0 */
+  float rho;                        /* target contraction rate, 0 <= rho <= 1 */
+  float gate_max;                   /* not NaN */
+} bd_aec_desc;
+
+/* Bytes of device workspace bd_aec_fwd needs (0 when none; then ws may be NULL). */
+bd_attn_status bd_aec_workspace(const bd_aec_desc* desc, size_t* ws_bytes);
+
+/* Enqueues the reduction on stream. Device pointers: logits [N][row_stride]
+ * (16-byte aligned), unresolved [N] (uint8, nonzero = unresolved), state_rows
+ * [S+1] (state s owns rows state_rows[s] .. state_rows[s+1]-1, ranges clamped to
+ * [0, N]), pair_next / pair_h_source / pair_weight [P]; outputs lse [N], hbar
+ * [N], h_state [S], loss [1] (float32). unresolved and state_rows may be NULL
+ * only when S = 0, the pair arrays only when P = 0. Errors: EINVAL (bad sizes,
+ * NULL or misaligned pointer), EWORKSPACE (ws NULL while needed), EHIP. */
+bd_attn_status bd_aec_fwd(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                          const int32_t* state_rows, const int32_t* pair_next,
+                          const float* pair_h_source, const float* pair_weight, float* lse,
+                          float* hbar, float* h_state, float* loss, void* ws,
+                          bd_attn_stream_t stream);
+
+/* Same, recording caller-created hipEvent_t handles (as void*) around the
+ * kernels: events[0] before the first, events[i] after the i-th; the kernels are
+ * "aec_entropy", then "aec_merge" when rows are split over several workgroups,
+ * then "aec_reduce" (bd_aec_kernels gives the count). n_events >= kernels + 1. */
+bd_attn_status bd_aec_fwd_timed(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                                const int32_t* state_rows, const int32_t* pair_next,
+                                const float* pair_h_source, const float* pair_weight, float* lse,
+                                float* hbar, float* h_state, float* loss, void* ws,
+                                bd_attn_stream_t stream, void* const* events, int n_events);
+
+/* Number of kernels bd_aec_fwd launches for desc (0 if desc is invalid). */
+int32_t bd_aec_kernels(const bd_aec_desc* desc);
+
 /* Frees a plan (NULL is accepted). */
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan);
 

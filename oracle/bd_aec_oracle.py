@@ -25,9 +25,9 @@ Readings of points the pages leave open:
     reading of the surrounding text (weights w given before gating, D the
     weighted count of retained pairs, zero loss for D = 0) is the weighted mean
     above;
-  * a pair is valid when its next state has at least one unresolved position
-    and its source mean is a finite number (the caller marks a source without
-    unresolved positions with NaN);
+  * a pair is valid when its next state exists (index in [0, S)), has at least
+    one unresolved position, and its source mean is a finite number (the caller
+    marks a source without unresolved positions with NaN);
   * the gate keeps a pair when H_source <= gate_max (gate_max = +inf keeps
     every pair, the LLaDA setting; 0.20 is the QwenDLM setting);
   * a state with no unresolved position has mean NaN.
@@ -74,6 +74,8 @@ def aec_loss(h_state, pair_next, h_source, weight, rho, gate_max):
     """Weighted mean of the gated hinge over valid pairs (0 when nothing is kept)."""
     num = den = 0.0
     for n, hs, w in zip(pair_next, h_source, weight):
+        if not 0 <= int(n) < len(h_state):      # no such state: not a valid pair
+            continue
         hn = h_state[int(n)]
         if not (math.isfinite(hs) and math.isfinite(hn)):
             continue

@@ -85,6 +85,8 @@ def test_hinge_gate_and_empty_cases():
     assert ao.aec_loss(hs, [0], [0.9], [1.0], 0.1, math.inf) == 0.0
     # a next state without unresolved positions or a NaN source: the pair is not valid
     assert ao.aec_loss(hs, [1, 0], [0.1, float("nan")], [1.0, 1.0], 0.0, math.inf) == 0.0
+    # a next-state index outside [0, S) names no state: not a valid pair
+    assert ao.aec_loss(hs, [-1, 3, 0], [0.1, 0.1, 0.9], [1.0, 1.0, 1.0], 0.1, math.inf) == 0.0
     # every pair gated off: D = 0, loss 0
     assert ao.aec_loss(hs, [2], [0.5], [1.0], 0.0, 0.2) == 0.0
     # rho = 1: the hinge is H_next^2

@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_exports_every_declared_function():
     hdr = open(os.path.join(ROOT, "include", "bd_attn.h")).read()
-    names = set(re.findall(r"^\s*(?:bd_attn_status|const char\*|int32_t)\s+(bd_attn_\w+)\s*\(", hdr, re.M))
+    names = set(re.findall(r"^\s*(?:bd_attn_status|const char\*|int32_t)\s+(bd_\w+)\s*\(", hdr, re.M))
     assert {"bd_attn_plan", "bd_attn_fwd", "bd_attn_bwd"} <= names
     lib = ctypes.CDLL(b.LIB_PATH)
     for n in sorted(names):
