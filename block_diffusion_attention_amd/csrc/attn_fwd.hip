@@ -39,6 +39,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
   const int idx = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
+  if (idx < 0) return;                              // empty slot of the split launch order
   const int4 itv = reinterpret_cast<const int4*>(a.items)[idx];
   if (itv.x < 0) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;

@@ -80,6 +80,7 @@ __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   const int kbase = pad_base<D / 8>(lane);        // K operand rows
   const int vbase = pad_base<KT / 8>(lane);       // VT operand dimensions
   const int idx = a.order ? __builtin_amdgcn_readfirstlane(a.order[blockIdx.x]) : (int)blockIdx.x;
+  if (idx < 0) return;                              // empty slot of the split launch order
   const int4 itv = ld_rec4(a.items, idx);
   if (itv.x < 0) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;

@@ -250,6 +250,16 @@ def test_shifted_grid_unmasked_dkdv():
     _compare(wl, gpu, run_oracle(wl))
 
 
+def test_split_order_with_empty_slots():
+    # regression: empty slots (-1) of the split launch order must be skipped
+    from test_planner_abi import SPLIT_WITH_EMPTY_SLOTS as meta
+    wl = W.random_workload(np.random.default_rng(609), meta, sigma=0.3)
+    _say(f"case split order with empty slots tq={meta.tq} tk={meta.tk}")
+    gpu, plan = run_gpu(wl, backward=False)
+    assert "combine" in plan.kernel_names(False)
+    _compare(wl, gpu, run_oracle(wl, backward=False))
+
+
 def test_packed_group_from_the_packer():
     # captured states of 12 responses -> replay rows -> largest-cost-first groups;
     # the attention of one group's pack against the oracle

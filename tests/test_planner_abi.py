@@ -350,3 +350,18 @@ def test_dkdv_split_of_long_key_tiles():
     _check_plan(small, b.FLAG_NO_SPLIT)
     f32 = Meta([96, 64], [0, 64], [[2, 0, 3], [4]], 16, 8, 2, 64, "fp32")
     _check_plan(f32, b.FLAG_FORCE_SPLIT)
+
+
+# Nine segments over two kv heads with a short query stream: the forward takes
+# the split path and its XCD-grouped launch order has empty slots (-1), which
+# the forward kernels must skip.
+SPLIT_WITH_EMPTY_SLOTS = Meta(
+    [352, 264, 312, 264, 262, 223, 155, 102, 155], [0] * 9,
+    [[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11], [1, 2, 3, 4, 5, 6, 7, 8, 9], [1, 3, 4, 5, 8, 10],
+     [1, 2, 3, 4, 7, 9], [1, 4, 5, 8, 9], [2, 4, 7], [3, 4, 5], [1, 2, 3, 4], [3, 5]],
+    32, 8, 2, 128, "bf16", block_offset=[0, 24, 8, 24, 26, 1, 5, 26, 5])
+
+
+def test_split_launch_order_has_empty_slots():
+    p, rec = _check_plan(SPLIT_WITH_EMPTY_SLOTS)
+    assert len(rec["comb"]) > 0 and (rec["fwd_order"] < 0).any()
