@@ -324,7 +324,7 @@ def aec_bench(args):
               pair_weight=t(wl.pair_weight, torch.float32), rho=wl.rho, gate_max=wl.gate_max)
     d = b.aec_desc(N, V, logits.shape[1], "bf16", len(wl.state_rows) - 1, len(wl.pair_next), wl.rho, wl.gate_max)
     nk = b.aec_kernels(d)
-    names = ["aec_entropy"] + (["aec_merge"] if nk == 3 else []) + ["aec_reduce"]
+    names = ["aec_entropy", "aec_reduce"][:nk]
     ws = torch.empty(max(16, b.aec_workspace_bytes(d)), dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
         b.aec_fwd(logits, V, ws=ws, **kw)

@@ -34,7 +34,6 @@ struct AecArgs {
 constexpr int kAecMinChunk = 8192;
 
 hipError_t launch_aec_entropy(const AecArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_aec_merge(const AecArgs& a, hipStream_t s);
 hipError_t launch_aec_reduce(const AecArgs& a, hipStream_t s);
 
 }  // namespace bdattn

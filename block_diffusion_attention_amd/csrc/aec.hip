@@ -14,7 +14,8 @@
 // row with 16-byte loads, four in flight per thread, and keeps per thread a
 // running (max m, S = sum 2^d, U = sum 2^d d) over d = x log2(e) - m, so that
 // log2 Z = m + log2 S and the entropy in bits is log2 S - U / S. Partial
-// triples of several workgroups (short batches split each row) merge exactly:
+// triples of several workgroups (short batches split each row; a single
+// workgroup merges them before the state means) merge exactly:
 // moving a triple to a larger max M scales S by 2^(m-M) and U to
 // 2^(m-M) (U + (m-M) S). Every sum runs in a fixed order: no atomics.
 #include "aec.h"
@@ -157,40 +158,55 @@ __global__ void __launch_bounds__(kThreads) aec_entropy_kernel(AecArgs a) {
   }
 }
 
-// One thread per row: the row's partial triples in split order.
-__global__ void __launch_bounds__(kThreads) aec_merge_kernel(AecArgs a) {
-  const int row = blockIdx.x * kThreads + threadIdx.x;
-  if (row >= a.n_rows) return;
-  const float* p = a.part + (int64_t)row * a.nsplit * 3;
-  Acc t{p[0], p[1], p[2]};
-  for (int k = 1; k < a.nsplit; ++k) merge(t, Acc{p[3 * k], p[3 * k + 1], p[3 * k + 2]});
-  finish(t, a.vocab, a.lse + row, a.hbar + row);
-}
-
-// Mean normalized entropy over the unresolved rows of state s (row order), or
-// NaN when it has none. Row ranges are clamped to [0, N].
-__device__ float state_mean(const AecArgs& a, int s) {
+// Mean normalized entropy over the unresolved rows [lo, hi) of one state, by one
+// wave: lanes take rows lo + lane, lo + lane + 64, ...; the sums meet in a fixed
+// butterfly. NaN when the state has no unresolved row.
+__device__ float wave_state_mean(const AecArgs& a, int s, int lane) {
   const int lo = min(max(a.state_rows[s], 0), a.n_rows);
   const int hi = min(max(a.state_rows[s + 1], lo), a.n_rows);
-  float sum = 0.f;
-  int cnt = 0;
-  for (int i = lo; i < hi; ++i)
-    if (a.unresolved[i]) { sum += a.hbar[i]; ++cnt; }
-  return cnt ? sum / (float)cnt : __builtin_nanf("");
+  float sum = 0.f, cnt = 0.f;
+  for (int i = lo + lane; i < hi; i += 64)
+    if (a.unresolved[i]) { sum += a.hbar[i]; cnt += 1.f; }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sum += __shfl_xor(sum, off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  return cnt > 0.f ? sum / cnt : __builtin_nanf("");
 }
 
-// One workgroup: per-state means, then the gated, weighted hinge of every pair.
-// A pair is valid when its next state index lies in [0, S), that state has an
-// unresolved row and the source mean is finite.
+// One workgroup, three phases separated by barriers (global writes of a phase
+// are visible to the whole workgroup after the barrier):
+//   1. split rows: merge each row's partial triples in split order -> lse, hbar;
+//   2. per state, one wave: the mean over its unresolved rows -> h_state;
+//   3. per pair, one thread: the gated, weighted hinge; a fixed-shape tree sums
+//      numerators and weights. A pair is valid when its next state index lies
+//      in [0, S), that state has an unresolved row and the source mean is finite.
 __global__ void __launch_bounds__(kThreads) aec_reduce_kernel(AecArgs a) {
-  for (int s = threadIdx.x; s < a.n_states; s += kThreads) a.h_state[s] = state_mean(a, s);
+  if (a.nsplit > 1) {
+    for (int row = threadIdx.x; row < a.n_rows; row += kThreads) {
+      const float* p = a.part + (int64_t)row * a.nsplit * 3;
+      Acc t{p[0], p[1], p[2]};
+      for (int k = 1; k < a.nsplit; ++k) merge(t, Acc{p[3 * k], p[3 * k + 1], p[3 * k + 2]});
+      finish(t, a.vocab, a.lse + row, a.hbar + row);
+    }
+    __threadfence_block();
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int s = wave; s < a.n_states; s += kThreads / 64) {
+    const float m = wave_state_mean(a, s, lane);
+    if (lane == 0) a.h_state[s] = m;
+  }
+  __threadfence_block();
+  __syncthreads();
   float num = 0.f, den = 0.f;
   for (int p = threadIdx.x; p < a.n_pairs; p += kThreads) {
     const int n = a.pair_next[p];
     const float hs = a.pair_h_source[p];
-    if (n < 0 || n >= a.n_states || !__builtin_isfinite(hs)) continue;
-    const float hn = state_mean(a, n);
-    if (!__builtin_isfinite(hn) || !(hs <= a.gate_max)) continue;
+    if (n < 0 || n >= a.n_states || !__builtin_isfinite(hs) || !(hs <= a.gate_max)) continue;
+    const float hn = a.h_state[n];
+    if (!__builtin_isfinite(hn)) continue;
     const float w = a.pair_weight[p];
     const float h = fmaxf(0.f, hn - (1.f - a.rho) * hs);
     num = fmaf(w * h, h, num);
@@ -216,11 +232,6 @@ hipError_t launch_aec_entropy(const AecArgs& a, bool bf16, hipStream_t s) {
   const int grid = a.n_rows * a.nsplit;
   if (bf16) hipLaunchKernelGGL(aec_entropy_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(aec_entropy_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_aec_merge(const AecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(aec_merge_kernel, dim3((a.n_rows + kThreads - 1) / kThreads), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -351,7 +351,7 @@ bd_attn_status aec_impl(const bd_aec_desc* d, const void* logits, const uint8_t*
   AecGeom g;
   bd_attn_status st;
   if ((st = aec_geom(d, &g))) return st;
-  const int nk = g.nsplit > 1 ? 3 : 2;
+  const int nk = 2;
   if (events && n_events < nk + 1) return fail(BD_ATTN_EINVAL, "n_events must be at least the number of kernels + 1");
   if ((st = check_ptr(logits, "logits"))) return st;
   if (!lse || !hbar || !loss) return fail(BD_ATTN_EINVAL, "lse, hbar and loss must not be NULL");
@@ -374,10 +374,6 @@ bd_attn_status aec_impl(const bd_aec_desc* d, const void* logits, const uint8_t*
   if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
   if ((st = hip_status(bdattn::launch_aec_entropy(a, d->dtype == BD_ATTN_BF16, s), "aec_entropy launch"))) return st;
   if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
-  if (g.nsplit > 1) {
-    if ((st = hip_status(bdattn::launch_aec_merge(a, s), "aec_merge launch"))) return st;
-    if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
-  }
   if ((st = hip_status(bdattn::launch_aec_reduce(a, s), "aec_reduce launch"))) return st;
   return hip_status(ev.mark(mark), "hipEventRecord");
 }
@@ -412,7 +408,7 @@ int32_t bd_aec_kernels(const bd_aec_desc* desc) {
   AecGeom g;
   const std::string keep = g_last_error;
   if (aec_geom(desc, &g) != BD_ATTN_OK) { g_last_error = keep; return 0; }
-  return g.nsplit > 1 ? 3 : 2;
+  return 2;
 }
 
 bd_attn_status bd_attn_pack(const bd_pack_desc* desc, bd_pack_out* out) {

@@ -308,8 +308,10 @@ bd_attn_status bd_aec_fwd(const bd_aec_desc* desc, const void* logits, const uin
 
 /* Same, recording caller-created hipEvent_t handles (as void*) around the
  * kernels: events[0] before the first, events[i] after the i-th; the kernels are
- * "aec_entropy", then "aec_merge" when rows are split over several workgroups,
- * then "aec_reduce" (bd_aec_kernels gives the count). n_events >= kernels + 1. */
+ * "aec_entropy" (one pass over the logits; short batches split each row over
+ * several workgroups and leave partial results in ws) and "aec_reduce" (one
+ * workgroup: the merge of split rows, the state means, the loss).
+ * n_events >= kernels + 1 (bd_aec_kernels gives the count). */
 bd_attn_status bd_aec_fwd_timed(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
                                 const int32_t* state_rows, const int32_t* pair_next,
                                 const float* pair_h_source, const float* pair_weight, float* lse,

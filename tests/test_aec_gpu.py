@@ -88,7 +88,7 @@ def test_short_batch_splits_rows(dtype):
     wl = W.aec_workload(8, n_states=2, block=4, dtype=dtype, states_per_response=2)
     _say(f"case {wl.name}")
     dt = b.aec_desc(len(wl.unresolved), wl.vocab, wl.logits.shape[1], dtype, 2, len(wl.pair_next), 0.1, math.inf)
-    assert b.aec_kernels(dt) == 3
+    assert b.aec_workspace_bytes(dt) > 0, "rows split over several workgroups"
     _check(wl, _run(wl), _ref(wl))
 
 
