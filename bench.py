@@ -356,8 +356,15 @@ def aec_bench(args):
         "kernels_ms": {n: round(x, 4) for n, x in avg.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "kernel": dom, "work_per_launch": work,
-                     "avg_launch_ms": round(avg[dom], 4), "traffic": None},
+                     "avg_launch_ms": round(avg[dom], 4), "traffic": traffic_from_profiles(dom, "aec")},
     }
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         from oracle import bd_aec_oracle as ao
         rows = 64
