@@ -42,7 +42,7 @@ import math
 
 import numpy as np
 
-__all__ = ["lse_and_entropy", "state_means", "aec_loss", "aec_forward"]
+__all__ = ["lse_and_entropy", "state_means", "aec_loss", "aec_forward", "aec_backward"]
 
 
 def lse_and_entropy(logits):
@@ -91,3 +91,45 @@ def aec_forward(logits, unresolved, state_rows, pair_next, h_source, weight, rho
     lse, hbar = lse_and_entropy(logits)
     hs = state_means(hbar, unresolved, state_rows)
     return lse, hbar, hs, aec_loss(hs, pair_next, h_source, weight, rho, gate_max)
+
+
+def aec_backward(logits, unresolved, state_rows, pair_next, h_source, weight, rho, gate_max, grad_loss=1.0):
+    """Gradient of grad_loss * loss with respect to the logits (float64, [N, V]).
+
+    By the chain rule through the definitions above:
+      dL/dH_next(n) = sum over kept valid pairs p with next n of 2 w_p hinge_p / D
+                      (hinge_p taken before squaring; 0 where the hinge is 0);
+      dH_state/dHbar_i = 1 / (unresolved rows of the state) for its unresolved rows;
+      dHbar_i/dx_iv = -p_iv (log p_iv + H_i) / log|V|, H_i the entropy in nats.
+    The captured source means are constants (detached).
+    """
+    x = np.asarray(logits, np.float64)
+    N, V = x.shape
+    lse, hbar = lse_and_entropy(x)
+    hs = state_means(hbar, unresolved, state_rows)
+    den = 0.0
+    kept = []
+    for n, h_src, w in zip(pair_next, h_source, weight):
+        n = int(n)
+        if not 0 <= n < len(hs):
+            continue
+        if not (math.isfinite(h_src) and math.isfinite(hs[n])):
+            continue
+        if not h_src <= gate_max:
+            continue
+        den += w
+        kept.append((n, h_src, w))
+    g_state = np.zeros(len(hs))
+    if den > 0:
+        for n, h_src, w in kept:
+            hinge = max(0.0, hs[n] - (1.0 - rho) * h_src)
+            g_state[n] += 2.0 * w * hinge / den
+    g_row = np.zeros(N)
+    for s in range(len(state_rows) - 1):
+        rows = [i for i in range(int(state_rows[s]), int(state_rows[s + 1])) if unresolved[i]]
+        for i in rows:
+            g_row[i] += g_state[s] / len(rows)
+    logp = x - lse[:, None]
+    p = np.exp(logp)
+    H = hbar * math.log(V)
+    return grad_loss * g_row[:, None] * (-p * (logp + H[:, None])) / math.log(V)

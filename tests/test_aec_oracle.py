@@ -115,3 +115,84 @@ def test_planted_mistakes_are_caught(monkeypatch):
         _, hbar = ao.lse_and_entropy(logits)
         assert np.abs(hbar[:3] - g["hbar_rows012"]).max() > 1e-3
     monkeypatch.setattr(ao, "lse_and_entropy", orig)
+
+
+# ------------------------------------------------------------- the gradient
+
+def _tiny(seed, V=7):
+    rng = np.random.default_rng(seed)
+    N = 10
+    x = rng.standard_normal((N, V)) * rng.uniform(0.5, 3.0, size=(N, 1))
+    unres = [int(u) for u in rng.random(N) < 0.7]
+    rows = [0, 3, 6, 8, 10]
+    nxt = [1, 2, 3, 0, 7]                 # the last names no state
+    hs = list(rng.uniform(0.0, 1.0, size=5))
+    hs[3] = float("nan")                  # no captured source mean
+    w = list(rng.uniform(0.2, 1.0, size=5))
+    return x, unres, rows, nxt, hs, w
+
+
+def _fd(x, args, eps=1e-6):
+    g = np.zeros_like(x)
+    for i in range(x.shape[0]):
+        for v in range(x.shape[1]):
+            xp, xm = x.copy(), x.copy()
+            xp[i, v] += eps
+            xm[i, v] -= eps
+            g[i, v] = (ao.aec_forward(xp, *args)[3] - ao.aec_forward(xm, *args)[3]) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("seed,rho,gate", [(0, 0.1, math.inf), (1, 0.0, math.inf), (2, 0.3, 0.6), (3, 0.9, 0.8)])
+def test_gradient_by_central_differences(seed, rho, gate):
+    x, unres, rows, nxt, hs, w = _tiny(seed)
+    args = (unres, rows, nxt, hs, w, rho, gate)
+    g = ao.aec_backward(x, *args)
+    fd = _fd(x, args)
+    assert np.abs(g - fd).max() <= 1e-6 * max(1.0, np.abs(fd).max())
+    assert ao.aec_backward(x, *args, grad_loss=2.5) == pytest.approx(2.5 * g, abs=1e-15)
+
+
+def test_gradient_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    x, unres, rows, nxt, hs, w = _tiny(5, V=11)
+    rho = 0.2
+    t = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    logp = torch.log_softmax(t, dim=1)
+    hbar = -(logp.exp() * logp).sum(1) / math.log(x.shape[1])
+    means = []
+    for s in range(len(rows) - 1):
+        sel = [i for i in range(rows[s], rows[s + 1]) if unres[i]]
+        means.append(hbar[sel].mean() if sel else None)
+    num = torch.zeros((), dtype=torch.float64)
+    den = 0.0
+    for n, h_src, wt in zip(nxt, hs, w):
+        if not (0 <= n < len(means)) or means[n] is None or not math.isfinite(h_src):
+            continue
+        num = num + wt * torch.clamp(means[n] - (1 - rho) * h_src, min=0.0) ** 2
+        den += wt
+    (num / den).backward()
+    g = ao.aec_backward(x, unres, rows, nxt, hs, w, rho, math.inf)
+    np.testing.assert_allclose(g, t.grad.numpy(), rtol=0, atol=1e-13)
+
+
+def test_gradient_is_zero_without_kept_pairs():
+    x, unres, rows, nxt, hs, w = _tiny(4)
+    assert not ao.aec_backward(x, unres, rows, nxt, hs, w, 0.1, -1.0).any()      # every pair gated off
+    # every hinge closed (H_next <= 1 = (1 - 0) * H_source): no gradient either
+    assert not ao.aec_backward(x, unres, rows, nxt, [1.0] * 5, w, 0.0, math.inf).any()
+
+
+def test_planted_gradient_mistake_is_caught():
+    x, unres, rows, nxt, hs, w = _tiny(0)
+    args = (unres, rows, nxt, hs, w, 0.1, math.inf)
+    good = ao.aec_backward(x, *args)
+    V = x.shape[1]
+    lse = np.log(np.exp(x).sum(1, keepdims=True))
+    p = np.exp(x - lse)
+    # dropping the entropy term of dHbar/dx (only -p log p / log V)
+    scale = np.divide(good, -p * ((x - lse) + (-(p * (x - lse)).sum(1, keepdims=True))) / math.log(V),
+                      out=np.zeros_like(good), where=good != 0)
+    bad = scale * (-p * (x - lse)) / math.log(V)
+    fd = _fd(x, args)
+    assert np.abs(good - fd).max() < 1e-6 < np.abs(bad - fd).max()
