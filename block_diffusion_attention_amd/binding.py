@@ -137,13 +137,18 @@ _lib.bd_aec_fwd.argtypes = [ctypes.POINTER(AecDesc)] + [_vp] * 12
 _lib.bd_aec_fwd.restype = ctypes.c_int
 _lib.bd_aec_fwd_timed.argtypes = [ctypes.POINTER(AecDesc)] + [_vp] * 13 + [ctypes.c_int]
 _lib.bd_aec_fwd_timed.restype = ctypes.c_int
+_lib.bd_aec_bwd.argtypes = [ctypes.POINTER(AecDesc)] + [_vp] * 13
+_lib.bd_aec_bwd.restype = ctypes.c_int
+_lib.bd_aec_bwd_timed.argtypes = [ctypes.POINTER(AecDesc)] + [_vp] * 14 + [ctypes.c_int]
+_lib.bd_aec_bwd_timed.restype = ctypes.c_int
 _lib.bd_aec_kernels.argtypes = [ctypes.POINTER(AecDesc)]
 _lib.bd_aec_kernels.restype = ctypes.c_int32
 
 EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
             "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
             "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version",
-            "bd_attn_pack", "bd_aec_workspace", "bd_aec_fwd", "bd_aec_fwd_timed", "bd_aec_kernels")
+            "bd_attn_pack", "bd_aec_workspace", "bd_aec_fwd", "bd_aec_fwd_timed", "bd_aec_kernels",
+            "bd_aec_bwd", "bd_aec_bwd_timed")
 
 
 class BdAttnError(RuntimeError):
@@ -411,3 +416,27 @@ def aec_fwd(logits, vocab, unresolved, state_rows, pair_next, pair_h_source, pai
         ev, n = _events_arg(events)
         _check(_lib.bd_aec_fwd_timed(*args, ev, n))
     return lse, hbar, h_state[:S], loss
+
+
+def aec_bwd(logits, vocab, unresolved, state_rows, pair_next, pair_h_source, pair_weight, rho, gate_max,
+            lse, hbar, h_state, grad_loss, events=None, ws=None):
+    """Gradient of grad_loss * loss with respect to the logits (bd_aec_bwd); lse,
+    hbar and h_state are aec_fwd's outputs, grad_loss a one-element float32 device
+    tensor. Returns dlogits shaped like logits (columns past ``vocab`` are zero)."""
+    N, stride = logits.shape
+    S = state_rows.numel() - 1 if state_rows is not None else 0
+    P = pair_next.numel() if pair_next is not None else 0
+    d = aec_desc(N, vocab, stride, logits.dtype, S, P, rho, gate_max)
+    dev = logits.device
+    dlogits = torch.zeros_like(logits) if stride != vocab else torch.empty_like(logits)
+    if ws is None:
+        ws = torch.empty(max(16, aec_workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    args = [ctypes.byref(d), _ptr(logits), _ptr(unresolved), _ptr(state_rows), _ptr(pair_next), _ptr(pair_h_source),
+            _ptr(pair_weight), _ptr(lse), _ptr(hbar), _ptr(h_state if S else None), _ptr(grad_loss), _ptr(dlogits),
+            _ptr(ws), _stream(dev)]
+    if events is None:
+        _check(_lib.bd_aec_bwd(*args))
+    else:
+        ev, n = _events_arg(events)
+        _check(_lib.bd_aec_bwd_timed(*args, ev, n))
+    return dlogits

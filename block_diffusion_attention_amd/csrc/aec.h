@@ -27,6 +27,11 @@ struct AecArgs {
   float gate_max;
   float* h_state;              // [S]
   float* loss;                 // [1]
+  // backward
+  const float* grad_loss;      // [1] upstream gradient of the loss
+  float* state_grad;           // [S] workspace: dL/dH_state
+  float* row_coef;             // [N] workspace: dL/dHbar_i / ln V (0 for rows outside the pairs)
+  void* dlogits;               // [N][row_stride], the logits' type
 };
 
 // Workgroups per row: enough for ~2048 workgroups in all, each split at least
@@ -35,5 +40,7 @@ constexpr int kAecMinChunk = 8192;
 
 hipError_t launch_aec_entropy(const AecArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_aec_reduce(const AecArgs& a, hipStream_t s);
+hipError_t launch_aec_grad_coef(const AecArgs& a, hipStream_t s);
+hipError_t launch_aec_grad(const AecArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace bdattn

@@ -226,6 +226,147 @@ __global__ void __launch_bounds__(kThreads) aec_reduce_kernel(AecArgs a) {
   if (threadIdx.x == 0) a.loss[0] = rd[0] > 0.f ? rn[0] / rd[0] : 0.f;
 }
 
+// ------------------------------------------------------------------ backward
+//
+// dL/dx_iv = -c_i p_iv (log p_iv + H_i), with H_i = hbar_i ln V (nats),
+// log p = x - lse and c_i = (dL/dHbar_i) / ln V. For an unresolved row of state
+// s, dL/dHbar_i = dL/dH_s / |U_s|, and dL/dH_s is the sum over the kept valid
+// pairs naming s as next state of 2 w_p hinge_p / D (times the upstream
+// gradient). The captured source means are constants.
+
+constexpr int kPairTile = 2048;
+
+__device__ __forceinline__ bool pair_kept(const AecArgs& a, int p, float* w, float* hinge) {
+  const int n = a.pair_next[p];
+  const float hs = a.pair_h_source[p];
+  if (n < 0 || n >= a.n_states || !__builtin_isfinite(hs) || !(hs <= a.gate_max)) return false;
+  const float hn = a.h_state[n];
+  if (!__builtin_isfinite(hn)) return false;
+  *w = a.pair_weight[p];
+  *hinge = fmaxf(0.f, hn - (1.f - a.rho) * hs);
+  return true;
+}
+
+// One workgroup, four phases separated by barriers:
+//   1. D = sum of the kept pairs' weights (fixed-shape tree); every row
+//      coefficient and every state gradient set to 0 (state s by thread s % 256);
+//   2. pairs staged through LDS in tiles; thread s % 256 adds, in pair order, the
+//      contributions of the pairs naming state s;
+//   3. one wave per state: its unresolved rows get dL/dH_s / (|U_s| ln V).
+// Row ranges of the states must not overlap (state_rows non-decreasing) for the
+// row coefficients to be well defined.
+__global__ void __launch_bounds__(kThreads) aec_grad_coef_kernel(AecArgs a) {
+  __shared__ float red[kThreads];
+  __shared__ int tnext[kPairTile];
+  __shared__ float tcontrib[kPairTile];
+  float den = 0.f;
+  for (int p = threadIdx.x; p < a.n_pairs; p += kThreads) {
+    float w, h;
+    if (pair_kept(a, p, &w, &h)) den += w;
+  }
+  red[threadIdx.x] = den;
+  for (int i = threadIdx.x; i < a.n_rows; i += kThreads) a.row_coef[i] = 0.f;
+  for (int s = threadIdx.x; s < a.n_states; s += kThreads) a.state_grad[s] = 0.f;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  const float D = red[0];
+  const float scale = D > 0.f ? 2.f * a.grad_loss[0] / D : 0.f;
+  for (int p0 = 0; p0 < a.n_pairs; p0 += kPairTile) {
+    const int np = min(kPairTile, a.n_pairs - p0);
+    __syncthreads();                                  // the previous tile is consumed
+    for (int q = threadIdx.x; q < np; q += kThreads) {
+      float w = 0.f, h = 0.f;
+      const bool kept = pair_kept(a, p0 + q, &w, &h);
+      tnext[q] = kept ? a.pair_next[p0 + q] : -1;
+      tcontrib[q] = scale * w * h;
+    }
+    __syncthreads();
+    for (int q = 0; q < np; ++q) {
+      const int n = tnext[q];
+      if (n >= 0 && n % kThreads == (int)threadIdx.x) a.state_grad[n] += tcontrib[q];
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float inv_lnv = 1.f / logf((float)a.vocab);
+  for (int s = wave; s < a.n_states; s += kThreads / 64) {
+    const int lo = min(max(a.state_rows[s], 0), a.n_rows);
+    const int hi = min(max(a.state_rows[s + 1], lo), a.n_rows);
+    float cnt = 0.f;
+    for (int i = lo + lane; i < hi; i += 64) cnt += a.unresolved[i] ? 1.f : 0.f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    const float c = cnt > 0.f ? a.state_grad[s] / cnt * inv_lnv : 0.f;
+    for (int i = lo + lane; i < hi; i += 64)
+      if (a.unresolved[i]) a.row_coef[i] = c;
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)x;
+  v[1] = (__bf16)y;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// dlogits of one row (or one part of it, as in the forward geometry); rows with
+// a zero coefficient get zeros without reading their logits.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) aec_grad_kernel(AecArgs a) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  const int row = blockIdx.x / a.nsplit, split = blockIdx.x - row * a.nsplit;
+  const int64_t c0 = (int64_t)split * a.chunk;
+  const int64_t c1 = min((int64_t)a.vocab, c0 + a.chunk);
+  const int64_t nvec = (c1 - c0) / EPV;
+  const int tail = (int)((c1 - c0) - nvec * EPV);
+  const int64_t off = (row * a.row_stride + c0) * (BF16 ? 2 : 4);
+  const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.logits) + off);
+  u32x4* op = reinterpret_cast<u32x4*>(static_cast<char*>(a.dlogits) + off);
+  const float c = a.row_coef[row];
+  if (c == 0.f) {
+    for (int64_t i = threadIdx.x; i < nvec; i += kThreads) op[i] = u32x4{0u, 0u, 0u, 0u};
+    if (threadIdx.x < tail) {
+      if constexpr (BF16) reinterpret_cast<uint16_t*>(op)[nvec * EPV + threadIdx.x] = 0;
+      else reinterpret_cast<float*>(op)[nvec * EPV + threadIdx.x] = 0.f;
+    }
+    return;
+  }
+  const float lse = a.lse[row];
+  const float H = a.hbar[row] * logf((float)a.vocab);
+  auto grad = [&](float x) {
+    const float lp = x - lse;
+    return -c * ex2(lp * kL2E) * (lp + H);
+  };
+  for (int64_t i = threadIdx.x; i < nvec; i += kThreads) {
+    float x[EPV];
+    unpack<BF16>(__builtin_nontemporal_load(vp + i), x);
+    u32x4 o;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(grad(x[2 * k]), grad(x[2 * k + 1]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = __builtin_bit_cast(uint32_t, grad(x[k]));
+    }
+    op[i] = o;
+  }
+  if (threadIdx.x < tail) {
+    const int64_t e = nvec * EPV + threadIdx.x;
+    if constexpr (BF16) {
+      const uint16_t b = reinterpret_cast<const uint16_t*>(vp)[e];
+      const __bf16 r = (__bf16)grad(__builtin_bit_cast(float, (uint32_t)b << 16));
+      reinterpret_cast<uint16_t*>(op)[e] = __builtin_bit_cast(uint16_t, r);
+    } else {
+      reinterpret_cast<float*>(op)[e] = grad(reinterpret_cast<const float*>(vp)[e]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_aec_entropy(const AecArgs& a, bool bf16, hipStream_t s) {
@@ -237,6 +378,18 @@ hipError_t launch_aec_entropy(const AecArgs& a, bool bf16, hipStream_t s) {
 
 hipError_t launch_aec_reduce(const AecArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(aec_reduce_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_aec_grad_coef(const AecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(aec_grad_coef_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_aec_grad(const AecArgs& a, bool bf16, hipStream_t s) {
+  const int grid = a.n_rows * a.nsplit;
+  if (bf16) hipLaunchKernelGGL(aec_grad_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(aec_grad_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

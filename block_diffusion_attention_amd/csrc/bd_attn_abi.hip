@@ -316,7 +316,8 @@ namespace {
 struct AecGeom {
   int nsplit = 1;
   int64_t chunk = 0;
-  size_t ws = 0;
+  size_t ws = 0;          // workspace of the forward (partials) or the backward, the larger
+  size_t ws_rows = 0;     // backward: byte offset of the row coefficients (after the state gradients)
 };
 
 bd_attn_status aec_geom(const bd_aec_desc* d, AecGeom* g) {
@@ -340,7 +341,10 @@ bd_attn_status aec_geom(const bd_aec_desc* d, AecGeom* g) {
   if (N * nsplit > INT32_MAX) return fail(BD_ATTN_EINVAL, "num_rows too large");
   g->nsplit = (int)nsplit;
   g->chunk = chunk;
-  g->ws = nsplit > 1 ? (size_t)(N * nsplit * 3 * sizeof(float)) : 0;
+  const size_t ws_fwd = nsplit > 1 ? (size_t)(N * nsplit * 3 * sizeof(float)) : 0;
+  g->ws_rows = ((size_t)std::max(d->num_states, 1) * sizeof(float) + 255) / 256 * 256;
+  const size_t ws_bwd = g->ws_rows + (size_t)N * sizeof(float);
+  g->ws = std::max(ws_fwd, ws_bwd);
   return BD_ATTN_OK;
 }
 
@@ -359,7 +363,7 @@ bd_attn_status aec_impl(const bd_aec_desc* d, const void* logits, const uint8_t*
     return fail(BD_ATTN_EINVAL, "unresolved, state_rows and h_state must not be NULL when num_states > 0");
   if (d->num_pairs > 0 && (!pair_next || !pair_h_source || !pair_weight))
     return fail(BD_ATTN_EINVAL, "the pair arrays must not be NULL when num_pairs > 0");
-  if (g.ws > 0 && !ws) return fail(BD_ATTN_EWORKSPACE, "this call needs a workspace (bd_aec_workspace)");
+  if (g.nsplit > 1 && !ws) return fail(BD_ATTN_EWORKSPACE, "this call needs a workspace (bd_aec_workspace)");
   if (ws && !aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
   bdattn::AecArgs a{};
   a.logits = logits; a.row_stride = d->row_stride; a.n_rows = d->num_rows; a.vocab = d->vocab;
@@ -378,7 +382,61 @@ bd_attn_status aec_impl(const bd_aec_desc* d, const void* logits, const uint8_t*
   return hip_status(ev.mark(mark), "hipEventRecord");
 }
 
+bd_attn_status aec_bwd_impl(const bd_aec_desc* d, const void* logits, const uint8_t* unresolved,
+                            const int32_t* state_rows, const int32_t* pair_next, const float* pair_h_source,
+                            const float* pair_weight, const float* lse, const float* hbar, const float* h_state,
+                            const float* grad_loss, void* dlogits, void* ws, bd_attn_stream_t stream,
+                            void* const* events, int n_events) {
+  AecGeom g;
+  bd_attn_status st;
+  if ((st = aec_geom(d, &g))) return st;
+  if (events && n_events < 3) return fail(BD_ATTN_EINVAL, "n_events must be at least the number of kernels + 1");
+  if ((st = check_ptr(logits, "logits")) || (st = check_ptr(dlogits, "dlogits"))) return st;
+  if (!lse || !hbar || !grad_loss) return fail(BD_ATTN_EINVAL, "lse, hbar and grad_loss must not be NULL");
+  if (d->num_states > 0 && (!unresolved || !state_rows || !h_state))
+    return fail(BD_ATTN_EINVAL, "unresolved, state_rows and h_state must not be NULL when num_states > 0");
+  if (d->num_pairs > 0 && (!pair_next || !pair_h_source || !pair_weight))
+    return fail(BD_ATTN_EINVAL, "the pair arrays must not be NULL when num_pairs > 0");
+  if (!ws) return fail(BD_ATTN_EWORKSPACE, "the backward needs a workspace (bd_aec_workspace)");
+  if (!aligned16(ws)) return fail(BD_ATTN_EINVAL, "ws is not 16-byte aligned");
+  bdattn::AecArgs a{};
+  a.logits = logits; a.row_stride = d->row_stride; a.n_rows = d->num_rows; a.vocab = d->vocab;
+  a.nsplit = g.nsplit; a.chunk = g.chunk;
+  a.lse = const_cast<float*>(lse); a.hbar = const_cast<float*>(hbar);
+  a.unresolved = unresolved; a.state_rows = state_rows; a.n_states = d->num_states;
+  a.pair_next = pair_next; a.pair_h_source = pair_h_source; a.pair_weight = pair_weight;
+  a.n_pairs = d->num_pairs; a.rho = d->rho; a.gate_max = d->gate_max;
+  a.h_state = const_cast<float*>(h_state); a.grad_loss = grad_loss;
+  a.state_grad = static_cast<float*>(ws);
+  a.row_coef = reinterpret_cast<float*>(static_cast<char*>(ws) + g.ws_rows);
+  a.dlogits = dlogits;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const EventMarks ev{events, events ? n_events : 0, s};
+  if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
+  if ((st = hip_status(bdattn::launch_aec_grad_coef(a, s), "aec_grad_coef launch"))) return st;
+  if ((st = hip_status(ev.mark(1), "hipEventRecord"))) return st;
+  if ((st = hip_status(bdattn::launch_aec_grad(a, d->dtype == BD_ATTN_BF16, s), "aec_grad launch"))) return st;
+  return hip_status(ev.mark(2), "hipEventRecord");
+}
+
 }  // namespace
+
+bd_attn_status bd_aec_bwd(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                          const int32_t* state_rows, const int32_t* pair_next, const float* pair_h_source,
+                          const float* pair_weight, const float* lse, const float* hbar, const float* h_state,
+                          const float* grad_loss, void* dlogits, void* ws, bd_attn_stream_t stream) {
+  return aec_bwd_impl(desc, logits, unresolved, state_rows, pair_next, pair_h_source, pair_weight, lse, hbar,
+                      h_state, grad_loss, dlogits, ws, stream, nullptr, 0);
+}
+
+bd_attn_status bd_aec_bwd_timed(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                                const int32_t* state_rows, const int32_t* pair_next, const float* pair_h_source,
+                                const float* pair_weight, const float* lse, const float* hbar,
+                                const float* h_state, const float* grad_loss, void* dlogits, void* ws,
+                                bd_attn_stream_t stream, void* const* events, int n_events) {
+  return aec_bwd_impl(desc, logits, unresolved, state_rows, pair_next, pair_h_source, pair_weight, lse, hbar,
+                      h_state, grad_loss, dlogits, ws, stream, events, n_events);
+}
 
 bd_attn_status bd_aec_workspace(const bd_aec_desc* desc, size_t* ws_bytes) {
   AecGeom g;

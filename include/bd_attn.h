@@ -290,7 +290,8 @@ typedef struct {
   float gate_max;                   /* not NaN */
 } bd_aec_desc;
 
-/* Bytes of device workspace bd_aec_fwd needs (0 when none; then ws may be NULL). */
+/* Bytes of device workspace for bd_aec_fwd and bd_aec_bwd (one buffer serves
+ * both; bd_aec_fwd also accepts NULL when the rows are not split). */
 bd_attn_status bd_aec_workspace(const bd_aec_desc* desc, size_t* ws_bytes);
 
 /* Enqueues the reduction on stream. Device pointers: logits [N][row_stride]
@@ -320,6 +321,29 @@ bd_attn_status bd_aec_fwd_timed(const bd_aec_desc* desc, const void* logits, con
 
 /* Number of kernels bd_aec_fwd launches for desc (0 if desc is invalid). */
 int32_t bd_aec_kernels(const bd_aec_desc* desc);
+
+/* Gradient of grad_loss[0] * loss with respect to the logits, written to dlogits
+ * [N][row_stride] (the logits' type; only the first V columns are written):
+ *   dL/dx_iv = -c_i p_iv (log p_iv + H_i),  H_i = hbar_i ln V,
+ *   c_i = (1 / (|U_s| ln V)) sum over kept valid pairs p with next state s of
+ *         2 w_p hinge_p / D, for an unresolved row i of state s; 0 otherwise.
+ * The captured source means are constants. lse, hbar and h_state are the outputs
+ * of bd_aec_fwd on the same inputs; grad_loss is a device scalar. state_rows must
+ * be non-decreasing (states own disjoint row ranges). Launches "aec_grad_coef" (one
+ * workgroup) and "aec_grad" (one pass over the logits). ws: bd_aec_workspace
+ * bytes (required). Errors as bd_aec_fwd. */
+bd_attn_status bd_aec_bwd(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                          const int32_t* state_rows, const int32_t* pair_next,
+                          const float* pair_h_source, const float* pair_weight, const float* lse,
+                          const float* hbar, const float* h_state, const float* grad_loss,
+                          void* dlogits, void* ws, bd_attn_stream_t stream);
+/* Same, with events[0..2] recorded before, between and after the two kernels. */
+bd_attn_status bd_aec_bwd_timed(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
+                                const int32_t* state_rows, const int32_t* pair_next,
+                                const float* pair_h_source, const float* pair_weight, const float* lse,
+                                const float* hbar, const float* h_state, const float* grad_loss,
+                                void* dlogits, void* ws, bd_attn_stream_t stream, void* const* events,
+                                int n_events);
 
 /* Frees a plan (NULL is accepted). */
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan);

@@ -31,13 +31,27 @@ def test_validation(over, msg):
     assert b.aec_kernels(_d(**over)) == 0
 
 
-def test_geometry():
-    # a long batch reads each row in one workgroup: no partials
-    assert b.aec_workspace_bytes(_d(num_rows=4096)) == 0 and b.aec_kernels(_d(num_rows=4096)) == 2
-    # short batches split each row; partial triples need a workspace
+def test_geometry_and_workspace():
+    # a long batch: the backward's state gradients (256-byte aligned) and row coefficients
+    assert b.aec_workspace_bytes(_d(num_rows=4096)) == 256 + 4096 * 4 and b.aec_kernels(_d(num_rows=4096)) == 2
+    # a short batch splits each row over several workgroups of >= 8192 logits:
+    # the forward's partial triples dominate the workspace
     d = _d(num_rows=8)
     assert b.aec_kernels(d) == 2
     nsplit = b.aec_workspace_bytes(d) // (8 * 3 * 4)
-    assert nsplit >= 2 and 151936 / nsplit >= 8192 - 8
+    assert 2 <= nsplit <= 151936 // 8192
     # fp32 rows may have a stride that is a multiple of 4
-    assert b.aec_workspace_bytes(_d(vocab=1002, row_stride=1004, dtype="fp32", num_rows=2)) == 0
+    assert b.aec_workspace_bytes(_d(vocab=1002, row_stride=1004, dtype="fp32", num_rows=2)) > 0
+
+
+def test_split_forward_requires_workspace_and_backward_always():
+    import ctypes
+    vp = ctypes.c_void_p
+    d = _d(num_rows=8)
+    st = b._lib.bd_aec_fwd(ctypes.byref(d), vp(16), vp(16), vp(16), vp(16), vp(16), vp(16),
+                           vp(16), vp(16), vp(16), vp(16), vp(0), vp(0))
+    assert st == b.EWORKSPACE
+    d = _d(num_rows=4096)
+    st = b._lib.bd_aec_bwd(ctypes.byref(d), vp(16), vp(16), vp(16), vp(16), vp(16), vp(16),
+                           vp(16), vp(16), vp(16), vp(16), vp(16), vp(0), vp(0))
+    assert st == b.EWORKSPACE
