@@ -91,6 +91,7 @@ KERNEL_SOURCES = {
     "bwd_pre": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "combine": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "aec_entropy": ["aec.hip", "aec.h"],
+    "aec_grad": ["aec.hip", "aec.h"],
 }
 
 
@@ -110,7 +111,7 @@ def traffic_from_profiles(kernel, workload):
 
 KERNEL_SYMBOLS = {"fwd": "fwd_", "combine": "combine_kernel", "bwd_pre": "bwd_pre_kernel",
                   "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel", "transpose_v": "transpose_v_kernel",
-                  "aec_entropy": "aec_entropy_kernel"}
+                  "aec_entropy": "aec_entropy_kernel", "aec_grad": "aec_grad_kernel"}
 COPY_SYMBOL = "MulFunctor"
 
 
@@ -300,7 +301,10 @@ def pack_bench(args):
 def aec_bench(args):
     """Normalized entropy + AEC loss over the logits of the canvas positions of a
     replay batch: 16 states of 32 positions, a 151,936-entry vocabulary, bf16
-    logits N(0, tau^2) with tau ~ U[0.5, 6] per row, seed 7."""
+    logits N(0, tau^2) with tau ~ U[0.5, 6] per row, seed 7; forward and the
+    gradient with respect to the logits."""
+    import ctypes
+
     import numpy as np
     import torch
 
@@ -326,29 +330,54 @@ def aec_bench(args):
     nk = b.aec_kernels(d)
     names = ["aec_entropy", "aec_reduce"][:nk]
     ws = torch.empty(max(16, b.aec_workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    backward = not args.fwd_only
+    grad = torch.ones(1, dtype=torch.float32, device=dev)
+    dlogits = torch.empty_like(logits)
+
+    def step(evf=None, evb=None):
+        lse, hbar, hs, _loss = b.aec_fwd(logits, V, events=evf, ws=ws, **kw)
+        if backward:
+            args_b = [ctypes.byref(d), b._ptr(logits), b._ptr(kw["unresolved"]), b._ptr(kw["state_rows"]),
+                      b._ptr(kw["pair_next"]), b._ptr(kw["pair_h_source"]), b._ptr(kw["pair_weight"]),
+                      b._ptr(lse), b._ptr(hbar), b._ptr(hs), b._ptr(grad), b._ptr(dlogits), b._ptr(ws),
+                      b._stream(dev)]
+            if evb is None:
+                b._check(b._lib.bd_aec_bwd(*args_b))
+            else:
+                arr, n = b._events_arg(evb)
+                b._check(b._lib.bd_aec_bwd_timed(*args_b, arr, n))
+
     for _ in range(args.warmup):
-        b.aec_fwd(logits, V, ws=ws, **kw)
+        step()
     torch.cuda.synchronize()
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
-    for e in [x for row in ev for x in row]:
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)] if backward else [None] * K
+    for e in [x for row in ev for x in row] + [x for row in evb if row for x in row]:
         e.record()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(K):
-        b.aec_fwd(logits, V, events=ev[i], ws=ws, **kw)
+        step(ev[i], evb[i])
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
     avg = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)])) for j, n in enumerate(names)}
+    if backward:
+        for j, n in enumerate(["aec_grad_coef", "aec_grad"]):
+            avg[n] = float(np.mean([evb[i][j].elapsed_time(evb[i][j + 1]) for i in range(K)]))
     logit_bytes = float(N) * V * 2
-    work = logit_bytes + 8.0 * N + N           # logits in; unresolved flags in; lse and hbar out
-    dom = "aec_entropy"
+    algo = {"aec_entropy": logit_bytes + 8.0 * N + N,     # logits, flags in; lse, hbar out
+            "aec_grad": 2.0 * logit_bytes + 12.0 * N}     # logits in, dlogits out; coefficients, lse, hbar in
+    dom = max((n for n in avg if n in algo), key=lambda n: avg[n])
+    work = algo[dom]
     achieved = work / (avg[dom] * 1e-3) / 1e9
     out = {
-        "metric": "normalized-entropy + AEC reduction over vocabulary logits: logit bytes per second",
+        "metric": "normalized-entropy + AEC loss (forward and gradient) over vocabulary logits: logit bytes "
+                  "per second",
         "value": round(logit_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "passes": "fwd+bwd" if backward else "fwd",
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": " ".join(aec_bench.__doc__.split()), "rows": N, "vocab": V,
@@ -370,6 +399,9 @@ def aec_bench(args):
         rows = 64
         t0 = time.perf_counter()
         ao.lse_and_entropy(wl.logits[:rows, :V])
+        if backward:      # the gradient's per-row work: softmax, log-probabilities, one product
+            ao.aec_backward(wl.logits[:rows, :V], wl.unresolved[:rows], wl.state_rows[:rows // 32 + 1],
+                            [], [], [], wl.rho, wl.gate_max)
         to = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": round(rows * V * 2 / to / 1e9, 3), "unit": "GB/s", "cores": 1,
                                "kind": "oracle", "sample": f"{rows} of {N} rows (entropy and normalizer), "

@@ -173,7 +173,7 @@ def test_backward_replay_batch():
     (151936, 151936, "fp32", 2, 4),        # rows split over several workgroups
     (50257, 50264, "bf16", 6, 8),
     (1000, 1000, "fp32", 6, 8),
-    (7, 8, "bf16", 4, 4),
+    (7, 8, "bf16", 6, 4),
 ])
 def test_backward_shapes(vocab, stride, dtype, n_states, block):
     wl = W.aec_workload(12, n_states=n_states, block=block, vocab=vocab, row_stride=stride, dtype=dtype,
