@@ -404,7 +404,8 @@ def aec_bench(args):
                             [], [], [], wl.rho, wl.gate_max)
         to = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": round(rows * V * 2 / to / 1e9, 3), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle", "sample": f"{rows} of {N} rows (entropy and normalizer), "
+                               "kind": "oracle", "sample": f"{rows} of {N} rows (normalizer and entropy"
+                                                           f"{', then the gradient' if backward else ''}), "
                                                            f"fp64 numpy, {to:.2f} s"}
     print(json.dumps(out), flush=True)
 
