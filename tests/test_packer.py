@@ -203,3 +203,24 @@ def test_group_rows_form_a_valid_attention_plan():
         meta = group_meta(p, g, clean, off, block, B, 4, 2, 64, "bf16")
         plan = b.Plan(meta)
         assert plan.visible_pairs == orc.visible_pairs(meta)
+
+
+def test_empty_batch_and_more_groups_than_rows():
+    p = b.pack([64, 32], [], [], [], 32, 4)
+    assert p["n_rows"] == 0 and list(p["group_row_offsets"]) == [0] * 5 and not p["group_cost"].any()
+    # three rows over five groups: one row each in the first three groups, largest first
+    p = b.pack([64, 96, 32], [0, 1, 2], [2, 3, 1], [0, 0, 0], 32, 5)
+    assert p["n_rows"] == 3
+    assert list(p["group_row_offsets"]) == [0, 1, 2, 3, 3, 3]
+    assert list(p["group_rows"]) == [1, 0, 2]          # costs 128, 96, 64
+    assert list(p["group_cost"]) == [128, 96, 64, 0, 0]
+
+
+def test_row_with_only_block_zero_states_holds_no_clean_token():
+    # states at block 0 see no clean token; with a grid offset the row still
+    # needs none, and its attention plan takes offset 0
+    p = b.pack([29], [0, 0], [0, 0], [3, 3], 32, 1, block_offset=[3])
+    assert p["n_rows"] == 1 and p["row_ctx_len"][0] == 0 and p["row_cost"][0] == 64
+    meta = group_meta(p, 0, [29], [3], [0, 0], 32, 4, 2, 64, "bf16")
+    assert meta.block_offset == [0]
+    assert b.Plan(meta).visible_pairs == orc.visible_pairs(meta)
