@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (no per-launch host cost); "
+                         "value and ms_per_step then come from the replays")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (fp32 read + write), "
                          "the reference for scaling HBM byte counters")
@@ -494,6 +497,28 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / K
+    ms_eager = ms_step
+    if args.graph:
+        # the same step captured once and replayed (stream-ordered, no host launches)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()                          # warm the side stream before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(K):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_step = g0.elapsed_time(g1) / K
 
     per_kernel = {}
     for i in range(K):
@@ -575,7 +600,9 @@ def main():
             "passes": "fwd+bwd" if backward else "fwd",
             "useful_flop_per_step": useful,
             "parallelism": "single GPU",
+            "launch": "hip graph replay" if args.graph else "eager stream launches",
         },
+        "eager_ms_per_step": round(ms_eager, 4),
         "kernels_ms": {n: round(t, 4) for n, t in avg_ms.items()},
         "plan_ms": round(t_plan * 1e3, 3),
         "wall_s": round(wall, 3),

@@ -95,6 +95,43 @@ def test_denoise_step_split(seed, flags):
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
+@pytest.mark.parametrize("k", [2, 6])
+def test_graph_replay_of_the_serving_steps(k):
+    # The serving steps captured once in a HIP graph and replayed: every replay,
+    # with eager work of another plan in between, reproduces the eager result
+    # bit for bit (the kernels are deterministic and the graph holds no memset).
+    wl = W.make_config(k, with_do=False)
+    _say(f"case graph replay {wl.name}")
+    plan = b.Plan(wl.meta).upload("cuda")
+    dt = plan.dtype
+    q, kk, v = (torch.from_numpy(x).cuda().to(dt).contiguous() for x in (wl.q, wl.k, wl.v))
+    o = torch.empty_like(q)
+    lse = torch.empty((plan.tq, wl.meta.num_q_heads), dtype=torch.float32, device="cuda")
+    b.fwd(plan, q, kk, v, o, lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = o.clone(), lse.clone()
+    other = W.make_config(4, with_do=False)
+    oplan = b.Plan(other.meta).upload("cuda")
+    oq, ok_, ov = (torch.from_numpy(x).cuda().to(torch.bfloat16).contiguous() for x in (other.q, other.k, other.v))
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b.fwd(plan, q, kk, v, o, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        b.fwd(plan, q, kk, v, o, lse)
+    for _ in range(3):
+        o.zero_()
+        lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+        b.fwd(oplan, oq, ok_, ov)             # eager work of another plan between replays
+        torch.cuda.synchronize()
+
+
 def test_denoise_step_no_split_matches_split():
     wl = W.make_config(2, with_do=False)
     g1, _ = run_gpu(wl, backward=False)
