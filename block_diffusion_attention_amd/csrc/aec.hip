@@ -11,7 +11,7 @@
 // softmax over the same logits reuses it).
 //
 // The logits are read once. Each workgroup streams a contiguous part of one
-// row with 16-byte loads, four in flight per thread, and keeps per thread a
+// row with 16-byte loads, eight in flight per thread, and keeps per thread a
 // running (max m, S = sum 2^d, U = sum 2^d d) over d = x log2(e) - m, so that
 // log2 Z = m + log2 S and the entropy in bits is log2 S - U / S. Partial
 // triples of several workgroups (short batches split each row; a single
@@ -108,12 +108,12 @@ __global__ void __launch_bounds__(kThreads) aec_entropy_kernel(AecArgs a) {
 
   Acc acc{-INFINITY, 0.f, 0.f};
   int64_t i = threadIdx.x;
-  for (; i + 3 * kThreads < nvec; i += 4 * kThreads) {
-    u32x4 w[4];
+  for (; i + 7 * kThreads < nvec; i += 8 * kThreads) {
+    u32x4 w[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = __builtin_nontemporal_load(vp + i + k * kThreads);
+    for (int k = 0; k < 8; ++k) w[k] = __builtin_nontemporal_load(vp + i + k * kThreads);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       float x[EPV];
       unpack<BF16>(w[k], x);
       add<EPV>(acc, x);

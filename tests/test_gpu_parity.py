@@ -256,6 +256,22 @@ def test_random_packs_shifted_grid(case, causal):
     _compare(wl, gpu, run_oracle(wl))
 
 
+@pytest.mark.parametrize("case,causal", [(0, True), (2, False), (7, True), (9, False)])
+def test_shifted_grid_forced_split(case, causal):
+    # forward key-range splits and dK/dV chunk splits on shifted grids and
+    # token-causal rows
+    B, hq, hkv, D, dt, sigma = CASES[case]
+    rng = np.random.default_rng(9500 + 31 * case + int(causal))
+    meta = W.random_meta(rng, max_segments=3, max_blocks=max(2, min(12, 600 // B)), block_sizes=(B,),
+                         max_canvases=4, hq=hq, hkv=hkv, d=D, dtype=dt, offsets=True, clean_causal=causal)
+    G = hq // hkv
+    do_sigma = min(1.0, (4.0 / G) ** 0.5) * (0.25 if (causal or B == 1) else 1.0)
+    wl = W.random_workload(rng, meta, sigma=sigma, do_sigma=do_sigma)
+    _say(f"case shifted forced-split B={B} G={G} causal={causal} tq={meta.tq}")
+    gpu, plan = run_gpu(wl, flags=b.FLAG_FORCE_SPLIT)
+    _compare(wl, gpu, run_oracle(wl))
+
+
 @pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT, b.FLAG_NO_SPLIT])
 def test_commit_folded_step(flags):
     wl = W.make_config(6)
