@@ -435,7 +435,7 @@ def main():
         aec_bench(args)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on exactly one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
