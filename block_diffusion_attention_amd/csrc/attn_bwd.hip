@@ -425,7 +425,7 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
-  const int4 itv = reinterpret_cast<const int4*>(a.dq_items)[blockIdx.x];
+  const int4 itv = ld_rec4(a.dq_items, blockIdx.x);
   if (itv.x < 0) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
   const QTile qt = load_qtile(a.qtiles, itv.x);

@@ -38,9 +38,9 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
-  const int idx = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
+  const int idx = a.order ? ld_rec1(a.order, blockIdx.x) : (int)blockIdx.x;
   if (idx < 0) return;                              // empty slot of the split launch order
-  const int4 itv = reinterpret_cast<const int4*>(a.items)[idx];
+  const int4 itv = ld_rec4(a.items, idx);
   if (itv.x < 0) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
   const QTile qt = load_qtile(a.qtiles, itv.x);
@@ -194,6 +194,8 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
 // Merges the split partial results of one query tile: lse = log sum_i exp(lse_i),
 // O = sum_i exp(lse_i - lse) O_i. Workgroup: kCombRows rows of one merge item,
 // one thread per (row, 4 columns); blockIdx.x = item * (kQRows / rows) + group.
+constexpr int kCombFast = 16;   // splits merged from registers in one round trip
+
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   constexpr int C4 = D / 4;
@@ -202,22 +204,50 @@ __global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
   const int item = blockIdx.x / GROUPS;
   const int row = (blockIdx.x - item * GROUPS) * RPW + threadIdx.x / C4;
   const int c = threadIdx.x % C4;
-  const int4 it = reinterpret_cast<const int4*>(a.items)[item];
+  const int4 it = ld_rec4(a.items, item);
   const QTile qt = load_qtile(a.qtiles, it.x);
   const int kvh = it.y, first = it.z, count = it.w;
   if (row >= qt.n_tok * a.G) return;
   const float* pl = a.part_lse + (int64_t)first * kQRows + row;
+  const float* po = a.part_o + ((int64_t)first * kQRows + row) * D + c * 4;
   float mx = -INFINITY;
-  for (int i = 0; i < count; ++i) mx = fmaxf(mx, pl[(int64_t)i * kQRows]);
   float wsum = 0.f;
   f32x4 accv = f32x4{};
-  if (mx != -INFINITY) {
-    const float* po = a.part_o + ((int64_t)first * kQRows + row) * D + c * 4;
+  if (count <= kCombFast) {
+    // every partial LSE and O of the row is requested before the first is used:
+    // one memory round trip instead of one per loop iteration
+    float lv[kCombFast];
+    f32x4 ov[kCombFast];
+#pragma unroll
+    for (int i = 0; i < kCombFast; ++i) {
+      lv[i] = -INFINITY;
+      ov[i] = f32x4{};
+      if (i < count) {
+        lv[i] = pl[(int64_t)i * kQRows];
+        ov[i] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * kQRows * D);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kCombFast; ++i) mx = fmaxf(mx, lv[i]);
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < kCombFast; ++i) {
+        if (i < count) {
+          const float w = __expf(lv[i] - mx);
+          wsum += w;
+          accv += w * ov[i];
+        }
+      }
+    }
+  } else {
+    for (int i = 0; i < count; ++i) mx = fmaxf(mx, pl[(int64_t)i * kQRows]);
+    if (mx != -INFINITY) {
 #pragma unroll 4
-    for (int i = 0; i < count; ++i) {
-      const float w = __expf(pl[(int64_t)i * kQRows] - mx);
-      wsum += w;
-      accv += w * *reinterpret_cast<const f32x4*>(po + (int64_t)i * kQRows * D);
+      for (int i = 0; i < count; ++i) {
+        const float w = __expf(pl[(int64_t)i * kQRows] - mx);
+        wsum += w;
+        accv += w * *reinterpret_cast<const f32x4*>(po + (int64_t)i * kQRows * D);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -288,6 +288,11 @@ __device__ __forceinline__ int4 ld_rec4(const void* base, int i) {
   return make_int4(v[0], v[1], v[2], v[3]);
 }
 
+__device__ __forceinline__ int ld_rec1(const void* base, int i) {
+  const int u = __builtin_amdgcn_readfirstlane(i);
+  return reinterpret_cast<__attribute__((address_space(4))) const int*>(reinterpret_cast<uintptr_t>(base))[u];
+}
+
 __device__ __forceinline__ QTile load_qtile(const int32_t* base, int i) {
   int4 a = ld_rec4(base, 2 * i), b = ld_rec4(base, 2 * i + 1);
   QTile q;
