@@ -89,6 +89,17 @@ def test_validation_errors(over, code):
     assert st_ok == b.OK
 
 
+@pytest.mark.parametrize("over,needle", [
+    # 2^30 packed query tokens: beyond the planner's token limit (INT32_MAX / 2)
+    (dict(S=1, ctx=[1 << 30], q0=[0], off=[0, 0], cb=[], B=1 << 20, hq=4, hkv=2), "token count"),
+    # 2^26 tokens x 32 query heads = 2^31 rows: beyond int32 rows per tensor
+    (dict(S=1, ctx=[1 << 26], q0=[0], off=[0, 0], cb=[], B=1 << 16, hq=32, hkv=1), "fit in int32"),
+])
+def test_size_limits(over, needle):
+    st, msg = _status(GOOD, **over)
+    assert st == b.EINVAL and needle in msg, msg
+
+
 def test_shifted_grid_and_causal_metadata_accepted():
     st, msg = _status(GOOD, ctx=[61, 32], bo=[3, 0], cb=[1, 4, 1])
     assert st == b.OK, msg
