@@ -141,6 +141,19 @@ def test_denoise_step_no_split_matches_split():
     assert st["max_abs"] <= 4e-3, st
 
 
+@pytest.mark.parametrize("tiles", [1, 3, 4, 5, 8])
+@pytest.mark.parametrize("k", [2, 6])
+def test_serving_steps_split_sizes(k, tiles):
+    """Serving steps split into ranges of 1 to 8 key tiles (the caller's split
+    size) all match the oracle, including single-tile splits and ragged last
+    splits."""
+    wl = W.make_config(k, with_do=False)
+    _say(f"case {wl.name} tiles per split {tiles}")
+    gpu, plan = run_gpu(wl, flags=tiles << 8, backward=False)
+    assert "combine" in plan.kernel_names(False)
+    _compare(wl, gpu, run_oracle(wl, backward=False))
+
+
 @pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_staircase_full_kv_group_samples(flags):
     wl = W.make_config(4)
