@@ -161,6 +161,8 @@ def summarize(args):
                          f"{float(r['Percentage']):.1f} |")
         lines.append("")
     pmc = _read_csvs(roots, "counter_collection.csv")
+    lines += _summarize_sq(pmc)
+    pmc = [r for r in pmc if r["Counter_Name"] in ("FETCH_SIZE", "WRITE_SIZE")]
     traffic = {}
     if pmc:
         per = collections.defaultdict(list)     # (kernel, counter) -> values per dispatch
@@ -205,6 +207,66 @@ def summarize(args):
         with open(path, "w") as f:
             json.dump(rec, f, indent=1, sort_keys=True)
         print(f"traffic {args.traffic_key}: {traffic[kern] / 1e6:.2f} MB per launch -> {path}")
+
+
+SIMDS = 256 * 4                # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8
+
+
+def _summarize_sq(rows):
+    """MFMA utilisation and LDS counters per kernel from rocprofv3 --pmc rows.
+
+    MFMA busy fraction = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles x SIMDs),
+    with the GPU cycles of one XCD (GRBM_GUI_ACTIVE summed over the 8 XCDs / 8); executed
+    MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; the clock is those cycles over the
+    dispatch's own start/end timestamps."""
+    import collections
+    per = collections.defaultdict(dict)          # (kernel, dispatch) -> counter -> value
+    for r in rows:
+        if r["Counter_Name"] in ("FETCH_SIZE", "WRITE_SIZE") or "bdattn" not in r["Kernel_Name"]:
+            continue
+        d = per[(_short(r["Kernel_Name"]), r["Dispatch_Id"])]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if not per:
+        return []
+    by_kernel = collections.defaultdict(list)
+    for (kn, _), d in per.items():
+        by_kernel[kn].append(d)
+    out = []
+    mfma = {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16"}
+    if any(mfma <= set(d) for ds in by_kernel.values() for d in ds):
+        out += ["## MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
+                "| kernel | dispatches | mean us | clock GHz | MFMA busy % | executed TFLOP | executed TFLOP/s | % of 2.5 PFLOP/s |",
+                "|---|---|---|---|---|---|---|---|"]
+        for kn, ds in sorted(by_kernel.items()):
+            ds = [d for d in ds if mfma <= set(d) and d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] > 0]
+            if not ds:
+                continue
+            dur = sum(d["dur_s"] for d in ds) / len(ds)
+            cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / len(ds) / XCDS
+            busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / len(ds)
+            flop = sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds) / len(ds) * 512.0
+            out.append(f"| {kn} | {len(ds)} | {dur * 1e6:.1f} | {cyc / dur / 1e9:.2f} | {100 * busy / (cyc * SIMDS):.1f} | "
+                       f"{flop / 1e12:.4f} | {flop / dur / 1e12:.0f} | {100 * flop / dur / 1e12 / PEAK_BF16_TFLOPS:.1f} |")
+        out.append("")
+    lds = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU",
+           "SQ_INSTS_VALU", "SQ_WAVE_CYCLES"]
+    if any(set(lds) <= set(d) for ds in by_kernel.values() for d in ds):
+        out += ["## LDS and VALU counters (SQ_WAVE_CYCLES, SQ_WAIT_INST_LDS, SQ_ACTIVE_INST_VALU in quad-cycles)", "",
+                "| kernel | LDS bank-conflict cycles | LDS instructions | waiting for LDS issue, % of wave time | "
+                "VALU active, % of wave time | VALU instructions |", "|---|---|---|---|---|---|"]
+        for kn, ds in sorted(by_kernel.items()):
+            ds = [d for d in ds if set(lds) <= set(d)]
+            if not ds:
+                continue
+            m = {c: sum(d[c] for d in ds) / len(ds) for c in lds}
+            wc = max(m["SQ_WAVE_CYCLES"], 1.0)
+            out.append(f"| {kn} | {m['SQ_LDS_BANK_CONFLICT']:.0f} | {m['SQ_INSTS_LDS']:.3e} | "
+                       f"{100 * m['SQ_WAIT_INST_LDS'] / wc:.1f} | {100 * m['SQ_ACTIVE_INST_VALU'] / wc:.1f} | "
+                       f"{m['SQ_INSTS_VALU']:.3e} |")
+        out.append("")
+    return out
 
 
 def cpu_baseline(wl, budget_s):
