@@ -22,6 +22,9 @@ namespace bdattn {
 
 namespace {
 
+// LDS operand reads run this many products ahead of the MFMA that consumes them.
+constexpr int kFwdAhead = 4;
+
 template <int D>
 __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   constexpr int KT = kKTile;
@@ -35,7 +38,8 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 sK1[TE];
   __shared__ __attribute__((aligned(1024))) bf16 sV1[TE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: copy targets in SGPRs
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
   const int idx = a.order ? ld_rec1(a.order, blockIdx.x) : (int)blockIdx.x;
@@ -94,15 +98,24 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
     const int lim = r1 ? L : qt.n_own;
     const bool need_mask = kpos0 + KT > (r1 ? qt.lim_min : qt.n_own);
 
-    // S^T = K Q^T : two 32-key blocks, each lane one query row
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NKS; ++kk)
-        s[kb] = mfma32(sw_row8<D>(sK, lo, kb * 32, kk), qf[kk], s[kb]);
-    }
+    // S^T = K Q^T : two 32-key blocks, each lane one query row. Fixed program of
+    // 2 NKS products (the two blocks alternate) whose K operands are read from LDS
+    // kFwdAhead products ahead; the reads of the first V^T operands are issued
+    // under the last products, so they land during the softmax.
+    constexpr int NSS = 2 * NKS, NPV = 4 * NDB;
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    bf16x8 opk[NSS], opv[NPV];
+    auto fetch_k = [&](int i) { return sw_row8<D>(sK, lo, (i & 1) * 32, i >> 1); };
+    auto fetch_v = [&](int i) { return sw_tr8<D>(sV, lo, (i / NDB) * 16, (i % NDB) * 32); };
+    static_for<kFwdAhead>([&](auto ic) { opk[ic.value] = fetch_k(ic.value); });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NSS>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      s[i & 1] = mfma32(opk[i], qf[i >> 1], s[i & 1]);
+      if constexpr (i + kFwdAhead < NSS) opk[i + kFwdAhead] = fetch_k(i + kFwdAhead);
+      else opv[i + kFwdAhead - NSS] = fetch_v(i + kFwdAhead - NSS);
+      __builtin_amdgcn_sched_barrier(0);
+    });
 
     // masking only on tiles that cross a row limit or the end of a range
     if (need_mask) {
@@ -149,12 +162,15 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
       for (int e = 0; e < 8; ++e) tmp[e] = s[kq >> 1][(kq & 1) * 8 + e];
       pb[kq] = pack8(tmp);
     }
-    // O^T += V^T P^T, V^T read transposed out of the natural V tile
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-        acc[db] = mfma32(sw_tr8<D>(sV, lo, kq * 16, db * 32), pb[kq], acc[db]);
+    // O^T += V^T P^T, V^T read transposed out of the natural V tile; product
+    // i = kq NDB + db, so consecutive products accumulate into different blocks
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NPV>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      acc[i % NDB] = mfma32(opv[i], pb[i / NDB], acc[i % NDB]);
+      if constexpr (i + kFwdAhead < NPV) opv[i + kFwdAhead] = fetch_v(i + kFwdAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
     step(kt, sK0, sV0, sK1, sV1);
