@@ -412,6 +412,9 @@ __global__ void __launch_bounds__(256) dkdv_merge_kernel(BwdArgs a) {
 // LSE * log2(e)) that the dK/dV kernel reads, so it runs first. Per wave 32 rows; scores transposed as in the
 // forward pass. K and V tiles go straight into LDS (two stages); K^T for
 // dQ^T = K^T dS^T is read with the LDS transpose read.
+// dQ: LDS operand reads run this many products ahead of the MFMA that consumes them.
+constexpr int kDqAhead = 4;
+
 template <int D>
 __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   constexpr int KT = kKTile;
@@ -422,7 +425,8 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 sK1[TE];
   __shared__ __attribute__((aligned(1024))) bf16 sV1[TE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: copy targets in SGPRs
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
   const int4 itv = ld_rec4(a.dq_items, blockIdx.x);
@@ -501,16 +505,26 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
     const int lim = r1 ? L : qt.n_own;
     const bool need_mask = kpos0 + KT > (r1 ? qt.lim_min : qt.n_own);
 
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
-#pragma unroll
-    for (int kk = 0; kk < NKS; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32(sw_row8<D>(sK, lo, kb * 32, kk), qf[kk], s[kb]);
-        dp[kb] = mfma32(sw_row8<D>(sV, lo, kb * 32, kk), df[kk], dp[kb]);
-      }
+    // S^T = K Q^T and dP^T = V dO^T as one fixed program of 4 NKS products
+    // (product i: dimension step i / 4, key block i % 2, K/Q for even i % 4 / 2,
+    // V/dO for odd), four accumulators in rotation, operands read from LDS
+    // kDqAhead products ahead; the first K^T operands of dQ are requested under
+    // the last products.
+    constexpr int NSD = 4 * NKS, NQ = 4 * NDB;
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    bf16x8 opa[NSD], opq[NQ];
+    auto fetch_a = [&](int i) { return sw_row8<D>((i & 2) ? sV : sK, lo, (i & 1) * 32, i >> 2); };
+    auto fetch_q = [&](int i) { return sw_tr8<D>(sK, lo, (i / NDB) * 16, (i % NDB) * 32); };
+    static_for<kDqAhead>([&](auto ic) { opa[ic.value] = fetch_a(ic.value); });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NSD>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i & 2) dp[i & 1] = mfma32(opa[i], df[i >> 2], dp[i & 1]);
+      else s[i & 1] = mfma32(opa[i], qf[i >> 2], s[i & 1]);
+      if constexpr (i + kDqAhead < NSD) opa[i + kDqAhead] = fetch_a(i + kDqAhead);
+      else opq[i + kDqAhead - NSD] = fetch_q(i + kDqAhead - NSD);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -533,11 +547,14 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) tmp[e] = dp[kq >> 1][(kq & 1) * 8 + e];
       sb[kq] = pack8(tmp);
     }
-#pragma unroll
-    for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = mfma32(sw_tr8<D>(sK, lo, kq * 16, db * 32), sb[kq], acc[db]);
+    // dQ^T += K^T dS^T: product i = kq NDB + db, reads kDqAhead products ahead
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NQ>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      acc[i % NDB] = mfma32(opq[i], sb[i / NDB], acc[i % NDB]);
+      if constexpr (i + kDqAhead < NQ) opq[i + kDqAhead] = fetch_q(i + kDqAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   for (int kt = kt_begin; kt < kt_end; kt += 2) {
     step(kt, sK0, sV0, sK1, sV1);
