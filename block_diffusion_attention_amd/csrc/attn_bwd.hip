@@ -278,8 +278,8 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
     const int64_t row0 = (int64_t)g.tok0 * a.hq + kvh * G;
     const int last = ((nrows - 1) / G) * a.hq + (nrows - 1) % G;   // uniform
-    fetch.issue(dQ_, Q + row0 * D, nrows, last * D, wave);
-    fetch.issue(dG_, dO + row0 * D, nrows, last * D, wave);
+    fetch.template issue<false>(dQ_, Q + row0 * D, nrows, last * D, wave);
+    fetch.template issue<false>(dG_, dO + row0 * D, nrows, last * D, wave);
     if (wave < 2) {                                     // 64 rows x 4 bytes each
       const int64_t qr = row0 + (lane < nrows ? lane_row : last);
       const float* src = wave == 0 ? a.lse2 + qr : a.delta + qr;
@@ -457,8 +457,8 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
     else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
     const int64_t off0 = (int64_t)base * kv_stride + kvh * D;
     const int last = (nvalid - 1) * (int)kv_stride;
-    fetch.issue(dK, K + off0, nvalid, last, wave);
-    fetch.issue(dV, V + off0, nvalid, last, wave);
+    fetch.template issue<false>(dK, K + off0, nvalid, last, wave);
+    fetch.template issue<false>(dV, V + off0, nvalid, last, wave);
   };
   if (kt_begin < kt_end) issue(kt_begin, sK0, sV0);
 

@@ -87,6 +87,13 @@ __device__ __forceinline__ void dma_b32(const void* src, lds_void* dst) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m) : "memory");
 }
+// The same copy with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (the instruction's scalar-base form): no per-lane 64-bit
+// address arithmetic when the offsets are fixed.
+__device__ __forceinline__ void dma_b128_sv(const void* sbase, uint32_t voff, lds_void* dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m) : "memory");
+}
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16. Within each group of 16 lanes, lane s supplies the address
@@ -178,13 +185,30 @@ struct SwFetch {
       off[n] = row_off(r) + col[n];
     }
   }
-  // last_off: element offset of row nvalid - 1 (any valid row works for the rows
-  // past the end: their values are never used)
+  // base: wave-uniform (it goes into scalar registers); offsets are byte offsets
+  // from it, below 2^32. last_off: element offset of row nvalid - 1 (any valid row
+  // works for the rows past the end: their values are never used). A whole tile
+  // takes the fixed offsets as they are.
+  // SCALAR_BASE = false keeps 64-bit per-lane addresses (fewer scalar registers,
+  // for kernels at their register limit).
+  template <bool SCALAR_BASE = true>
   __device__ __forceinline__ void issue(bf16* tile, const bf16* base, int nvalid, int last_off, int wave) const {
+    if constexpr (!SCALAR_BASE) {
 #pragma unroll
-    for (int n = 0; n < PER_WAVE; ++n) {
-      const int o = row[n] < nvalid ? off[n] : last_off + col[n];
-      dma_b128(base + o, (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+      for (int n = 0; n < PER_WAVE; ++n) {
+        const int o = row[n] < nvalid ? off[n] : last_off + col[n];
+        dma_b128(base + o, (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+      }
+    } else if (nvalid >= 64) {
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n)
+        dma_b128_sv(base, 2u * (uint32_t)off[n], (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+    } else {
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n) {
+        const int o = row[n] < nvalid ? off[n] : last_off + col[n];
+        dma_b128_sv(base, 2u * (uint32_t)o, (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+      }
     }
   }
 };
