@@ -250,6 +250,20 @@ def _summarize_sq(rows):
             out.append(f"| {kn} | {len(ds)} | {dur * 1e6:.1f} | {cyc / dur / 1e9:.2f} | {100 * busy / (cyc * SIMDS):.1f} | "
                        f"{flop / 1e12:.4f} | {flop / dur / 1e12:.0f} | {100 * flop / dur / 1e12 / PEAK_BF16_TFLOPS:.1f} |")
         out.append("")
+    stall = ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+             "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_VMEM"]
+    if any(set(stall) <= set(d) for ds in by_kernel.values() for d in ds):
+        out += ["## Where the waves' time goes (% of SQ_WAVE_CYCLES; quad-cycle counters, per wave)", "",
+                "| kernel | waiting for anything | waiting to issue | active (any) | active VALU/MFMA | active LDS | "
+                "active scalar | active vector memory |", "|---|---|---|---|---|---|---|---|"]
+        for kn, ds in sorted(by_kernel.items()):
+            ds = [d for d in ds if set(stall) <= set(d)]
+            if not ds:
+                continue
+            m = {c: sum(d[c] for d in ds) / len(ds) for c in stall}
+            wc = max(m["SQ_WAVE_CYCLES"], 1.0)
+            out.append(f"| {kn} | " + " | ".join(f"{100 * m[c] / wc:.1f}" for c in stall[1:]) + " |")
+        out.append("")
     lds = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU",
            "SQ_INSTS_VALU", "SQ_WAVE_CYCLES"]
     if any(set(lds) <= set(d) for ds in by_kernel.values() for d in ds):
