@@ -249,7 +249,10 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const bool canvas_keys = kt.p0 < 0;
   const int kpos = canvas_keys ? 0 : kt.p0 + kidx;
   const int wpos_lo = kt.p0 + wave * 32;
-  const int wpos_hi = kt.p0 + min(wave * 32 + 31, kt.n_keys - 1);
+  // a clean query row at grid position x sees the wave's first key iff
+  // wpos_lo < (x / Bc + 1) Bc, i.e. iff x >= (wpos_lo / Bc) Bc: one division per
+  // kernel instead of two per chunk
+  const int wpos_floor = canvas_keys ? 0 : (wpos_lo / Bc) * Bc;
 
   const int qct = QC / G;                               // tokens per chunk
   const int nc0 = (kt.cq_len + qct - 1) / qct;
@@ -277,13 +280,13 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const ChunkGeom g = chunk_geom(kt, a.canvq, nall - 1 - (c0 + c), nc0, cpc, qct);
     const int nrows = g.ntok * G;                       // valid rows (<= qct*G <= 64)
     const int64_t row0 = (int64_t)g.tok0 * a.hq + kvh * G;
-    const int last = ((nrows - 1) / G) * a.hq + (nrows - 1) % G;   // uniform
+    const int last = (g.ntok - 1) * a.hq + (G - 1);     // row nrows - 1 (nrows = ntok G); uniform
     fetch.template issue<false>(dQ_, Q + row0 * D, nrows, last * D, wave);
     fetch.template issue<false>(dG_, dO + row0 * D, nrows, last * D, wave);
     if (wave < 2) {                                     // 64 rows x 4 bytes each
       const int64_t qr = row0 + (lane < nrows ? lane_row : last);
       const float* src = wave == 0 ? a.lse2 + qr : a.delta + qr;
-      dma_b32(src, (lds_void*)(wave == 0 ? dL_ : dD_));
+      dma_b32(src, wave == 0 ? dL_ : dD_);
     } else if (MASKED && wave == 2) {
       int lim = -1;                                     // padding rows see nothing
       if (lane < nrows) lim = g.pos0 >= 0 ? ((g.pos0 + lane_tok) / Bc + 1) * Bc : g.lim;
@@ -325,15 +328,10 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const ChunkGeom g = chunk_geom(kt, a.canvq, nall - 1 - (c0 + c), nc0, cpc, qct);
     const int nrows = g.ntok * G;
     // row limits of the first and the last valid row (clean limits grow with the row)
-    int lim_first, lim_last;
-    if (g.pos0 >= 0) {
-      lim_first = (g.pos0 / Bc + 1) * Bc;
-      lim_last = ((g.pos0 + (nrows - 1) / G) / Bc + 1) * Bc;
-    } else {
-      lim_first = lim_last = g.lim;
-    }
-    // skip when no valid row sees any of the wave's keys
-    if (!wave_live || (!canvas_keys && wpos_lo >= lim_last)) return;
+    // skip when no valid row sees any of the wave's keys: for a clean chunk its last
+    // row (grid position pos0 + ntok - 1) has the largest limit
+    const bool unseen = g.pos0 >= 0 ? g.pos0 + g.ntok - 1 < wpos_floor : wpos_lo >= g.lim;
+    if (!wave_live || (!canvas_keys && unseen)) return;
     dkdv_chunk<D, MASKED>(kf, vf, dkt, dvt, cQ, cG, cL, cD, cM, lo, h, kpos, a.scale_log2);
   };
   for (int c = 0; c < nchunks; c += kBwdStages) {

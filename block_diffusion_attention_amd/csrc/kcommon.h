@@ -79,19 +79,24 @@ typedef __attribute__((address_space(3))) void lds_void;
 // The hardware tracks these copies with the vector memory counter only; callers
 // wait for them with explicit vmcnt waits (or a barrier that waits vmcnt(0))
 // before reading the destination.
-__device__ __forceinline__ void dma_b128(const void* src, lds_void* dst) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+// dst is a generic pointer into LDS: the low 32 bits of a flat LDS address are its
+// LDS offset, so no address-space conversion (and its null check) is needed.
+__device__ __forceinline__ uint32_t lds_offset(const void* dst) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+}
+__device__ __forceinline__ void dma_b128(const void* src, void* dst) {
+  const uint32_t m = lds_offset(dst);
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m) : "memory");
 }
-__device__ __forceinline__ void dma_b32(const void* src, lds_void* dst) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+__device__ __forceinline__ void dma_b32(const void* src, void* dst) {
+  const uint32_t m = lds_offset(dst);
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m) : "memory");
 }
 // The same copy with a wave-uniform 64-bit base in scalar registers and a 32-bit
 // per-lane byte offset (the instruction's scalar-base form): no per-lane 64-bit
 // address arithmetic when the offsets are fixed.
-__device__ __forceinline__ void dma_b128_sv(const void* sbase, uint32_t voff, lds_void* dst) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+__device__ __forceinline__ void dma_b128_sv(const void* sbase, uint32_t voff, void* dst) {
+  const uint32_t m = lds_offset(dst);
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m) : "memory");
 }
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -197,17 +202,17 @@ struct SwFetch {
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n) {
         const int o = row[n] < nvalid ? off[n] : last_off + col[n];
-        dma_b128(base + o, (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+        dma_b128(base + o, tile + (wave * PER_WAVE + n) * 64 * 8);
       }
     } else if (nvalid >= 64) {
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n)
-        dma_b128_sv(base, 2u * (uint32_t)off[n], (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+        dma_b128_sv(base, 2u * (uint32_t)off[n], tile + (wave * PER_WAVE + n) * 64 * 8);
     } else {
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n) {
         const int o = row[n] < nvalid ? off[n] : last_off + col[n];
-        dma_b128_sv(base, 2u * (uint32_t)o, (lds_void*)(tile + (wave * PER_WAVE + n) * 64 * 8));
+        dma_b128_sv(base, 2u * (uint32_t)o, tile + (wave * PER_WAVE + n) * 64 * 8);
       }
     }
   }
