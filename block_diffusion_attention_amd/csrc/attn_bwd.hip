@@ -455,8 +455,8 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
     else { const int k2 = kt - n1; base = qt.k_own + k2 * KT; nvalid = min(KT, qt.n_own - k2 * KT); }
     const int64_t off0 = (int64_t)base * kv_stride + kvh * D;
     const int last = (nvalid - 1) * (int)kv_stride;
-    fetch.template issue<false>(dK, K + off0, nvalid, last, wave);
-    fetch.template issue<false>(dV, V + off0, nvalid, last, wave);
+    fetch.issue(dK, K + off0, nvalid, last, wave);
+    fetch.issue(dV, V + off0, nvalid, last, wave);
   };
   if (kt_begin < kt_end) issue(kt_begin, sK0, sV0);
 
