@@ -124,6 +124,11 @@ struct DkdvGeom {
 // plans whose chunks are all either seen whole by a wave's keys or skipped use
 // the program without it (a separate kernel, chosen by the planner).
 constexpr int kPrefetch = 4;
+// Slots between a half's last S/dP product and the first use of its scores (at
+// most 2 NDB: the packed P/dS of score elements 8..15 of a half are complete in
+// slot kPointShift - 1 of its dV/dK phase, which first reads them in slot 2 NDB).
+// 4 measured best for D = 128 (2 and 6 slower; 8 slower still).
+constexpr int kPointShift = 4;
 
 template <int D, bool MASKED>
 __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
@@ -134,6 +139,8 @@ __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf1
   constexpr int NS = 2 * NKS;                 // MFMA slots per phase
   constexpr int NSLOT = 4 * NS;
   constexpr int EPS = 16 / NS;                // score elements per slot in the vector phases
+  constexpr int SH = kPointShift;
+  static_assert(SH <= 2 * NDB, "P/dS of a half must be packed before its dV/dK products read them");
   f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
   bf16x8 pb[2][2], sb[2][2];
   f32x4 lv[2][4], dl[2][4];
@@ -200,11 +207,14 @@ __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf1
     if constexpr (i + kPrefetch < NSLOT) op[i + kPrefetch] = fetch(i + kPrefetch);
     if constexpr (i == NS - 3) rowterms(0);
     if constexpr (i == 2 * NS - 3) rowterms(1);
-    if constexpr (i >= NS && i < 2 * NS) {
-      static_for<EPS>([&](auto uc) { pointwise(0, (i - NS) * EPS + uc.value); });
+    // a half's vector work starts SH slots after its last S/dP product,
+    // so that product has finished by the time its scores are read
+    constexpr int P0 = NS + SH, P1 = 2 * NS + SH;
+    if constexpr (i >= P0 && i < P0 + NS) {
+      static_for<EPS>([&](auto uc) { pointwise(0, (i - P0) * EPS + uc.value); });
     }
-    if constexpr (i >= 2 * NS && i < 3 * NS) {
-      static_for<EPS>([&](auto uc) { pointwise(1, (i - 2 * NS) * EPS + uc.value); });
+    if constexpr (i >= P1 && i < P1 + NS) {
+      static_for<EPS>([&](auto uc) { pointwise(1, (i - P1) * EPS + uc.value); });
     }
     __builtin_amdgcn_sched_barrier(0);
   });
