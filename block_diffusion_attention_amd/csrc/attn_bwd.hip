@@ -113,10 +113,11 @@ struct DkdvGeom {
 // One 64-row query chunk for the 32 keys of a wave, as a fixed program of
 // 4 * NS MFMA slots (NS = 2 * D / 16):
 //   slots [0, NS)      S = Q K^T, dP = dO V^T for rows 0..31 (alternating)
-//   slots [NS, 2NS)    the same for rows 32..63; vector work of rows 0..31
-//   slots [2NS, 3NS)   dV^T += dO^T P, dK^T += Q^T dS for rows 0..31; vector work
-//                      of rows 32..63
+//   slots [NS, 2NS)    the same for rows 32..63
+//   slots [2NS, 3NS)   dV^T += dO^T P, dK^T += Q^T dS for rows 0..31
 //   slots [3NS, 4NS)   dV^T, dK^T for rows 32..63
+// with the vector work of rows 0..31 in slots [NS, 2NS) and that of rows 32..63
+// in [2NS, 3NS), each shifted kPointShift slots later (below).
 // Each slot issues one MFMA, the LDS reads of the operand kPrefetch slots ahead
 // and its share of the per-score vector work; scheduling barriers between slots
 // keep that order, so the vector ALU and the LDS run in the shadow of the MFMAs.
