@@ -508,7 +508,6 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   auto step = [&](int kt, const bf16* sK, const bf16* sV, bf16* nK, bf16* nV) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
-    if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
     const bool r1 = kt < n1;
     const int kpos0 = r1 ? kt * KT : (kt - n1) * KT;
     const int lim = r1 ? L : qt.n_own;
@@ -534,6 +533,8 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
       else opq[i + kDqAhead - NSD] = fetch_q(i + kDqAhead - NSD);
       __builtin_amdgcn_sched_barrier(0);
     });
+    // the next tile's copies go out after the S and dP products (as in the forward)
+    if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)

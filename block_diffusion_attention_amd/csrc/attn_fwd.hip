@@ -92,7 +92,6 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   auto step = [&](int kt, const bf16* sK, const bf16* sV, bf16* nK, bf16* nV) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();                  // tile kt is in LDS; the other stage is free again
-    if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
     const bool r1 = kt < n1;
     const int kpos0 = r1 ? kt * KT : (kt - n1) * KT;
     const int lim = r1 ? L : qt.n_own;
@@ -116,6 +115,10 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
       else opv[i + kFwdAhead - NSS] = fetch_v(i + kFwdAhead - NSS);
       __builtin_amdgcn_sched_barrier(0);
     });
+    // the next tile's copies go out after the S products, so their LDS writes do
+    // not compete with this tile's K operand reads (the other stage is free since
+    // the barrier)
+    if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
 
     // masking only on tiles that cross a row limit or the end of a range
     if (need_mask) {
