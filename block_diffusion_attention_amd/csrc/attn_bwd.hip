@@ -335,15 +335,17 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     lds_barrier();                                      // chunk c visible; stage of c-1 free
-    if (c + 2 < nchunks) issue(c + 2, nQ, nG, nL, nD, nM);
     const ChunkGeom g = chunk_geom(kt, a.canvq, nall - 1 - (c0 + c), nc0, cpc, qct);
     const int nrows = g.ntok * G;
     // row limits of the first and the last valid row (clean limits grow with the row)
     // skip when no valid row sees any of the wave's keys: for a clean chunk its last
     // row (grid position pos0 + ntok - 1) has the largest limit
     const bool unseen = g.pos0 >= 0 ? g.pos0 + g.ntok - 1 < wpos_floor : wpos_lo >= g.lim;
-    if (!wave_live || (!canvas_keys && unseen)) return;
-    dkdv_chunk<D, MASKED>(kf, vf, dkt, dvt, cQ, cG, cL, cD, cM, lo, h, kpos, a.scale_log2);
+    if (wave_live && (canvas_keys || !unseen))
+      dkdv_chunk<D, MASKED>(kf, vf, dkt, dvt, cQ, cG, cL, cD, cM, lo, h, kpos, a.scale_log2);
+    // the copies of chunk c+2 (into the stage of c-1, free since the barrier) go out
+    // after this chunk's products
+    if (c + 2 < nchunks) issue(c + 2, nQ, nG, nL, nD, nM);
   };
   for (int c = 0; c < nchunks; c += kBwdStages) {
     step(c, sQ0, sG0, sL0, sD0, sM0, sQ2, sG2, sL2, sD2, sM2);
