@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--traffic-key", default=None,
                     help="with --summarize: record per-launch HBM bytes of KERNEL@WORKLOAD in "
                          "profiles/traffic.json, e.g. dkdv@3")
+    ap.add_argument("--mfma-key", nargs="+", default=None,
+                    help="with --summarize: record the MFMA busy fraction, clock and executed rate of "
+                         "KERNEL@WORKLOAD in profiles/mfma.json, e.g. dkdv@3 fwd@3")
     return ap.parse_args()
 
 
@@ -96,6 +99,19 @@ KERNEL_SOURCES = {
     "aec_entropy": ["aec.hip", "aec.h"],
     "aec_grad": ["aec.hip", "aec.h"],
 }
+
+
+def mfma_from_profiles(kernel, workload):
+    """MFMA busy fraction, clock and executed rate of a kernel from rocprofv3 counters
+    (profiles/mfma.json), only if its source has not changed since they were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "mfma.json")) as f:
+            rec = json.load(f)[f"{kernel}@{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("src_sha256") != src_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "clock_ghz", "executed_tflops", "profiled_us") if k in rec}
 
 
 def traffic_from_profiles(kernel, workload):
@@ -194,6 +210,21 @@ def summarize(args):
         with open(args.summary_out, "w") as f:
             f.write(text + "\n")
     print(text)
+    if args.mfma_key and MFMA_STATS:
+        path = os.path.join(ROOT, "profiles", "mfma.json")
+        try:
+            with open(path) as f:
+                rec = json.load(f)
+        except (OSError, ValueError):
+            rec = {}
+        for key in args.mfma_key:
+            kern, _wl = key.split("@")
+            hits = [v for kn, v in MFMA_STATS.items() if KERNEL_SYMBOLS[kern] in kn]
+            if hits:
+                rec[key] = dict(hits[0], src_sha256=src_hash(KERNEL_SOURCES[kern]), command=args.command)
+                print(f"mfma {key}: {rec[key]}")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
     if args.traffic_key and traffic:
         kern, wl = args.traffic_key.split("@")
         path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -210,6 +241,7 @@ def summarize(args):
 
 
 SIMDS = 256 * 4                # MI355X: 256 compute units x 4 SIMDs
+MFMA_STATS = {}                # short kernel name -> MFMA counters of the last summary
 XCDS = 8
 
 
@@ -247,6 +279,8 @@ def _summarize_sq(rows):
             cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / len(ds) / XCDS
             busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / len(ds)
             flop = sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds) / len(ds) * 512.0
+            MFMA_STATS[kn] = {"mfma_busy": round(busy / (cyc * SIMDS), 4), "clock_ghz": round(cyc / dur / 1e9, 3),
+                              "executed_tflops": round(flop / dur / 1e12, 1), "profiled_us": round(dur * 1e6, 1)}
             out.append(f"| {kn} | {len(ds)} | {dur * 1e6:.1f} | {cyc / dur / 1e9:.2f} | {100 * busy / (cyc * SIMDS):.1f} | "
                        f"{flop / 1e12:.4f} | {flop / dur / 1e12:.0f} | {100 * flop / dur / 1e12 / PEAK_BF16_TFLOPS:.1f} |")
         out.append("")
@@ -679,6 +713,8 @@ def main():
     roof["work_per_launch"] = work
     roof["avg_launch_ms"] = round(avg_ms[dom], 4)
     roof["traffic"] = traffic_from_profiles(dom, k)
+    # rocprofv3 counters of the kernels (profiles/mfma.json; null when stale or absent)
+    counters = {n: mfma_from_profiles(n, k) for n in avg_ms if algo.get(n, ("",))[0] == "mfma"}
 
     cold = cold_serving(plan, q, kk, v, o, lse, fwd_names, algo, K) if k in FWD_ONLY else None
 
@@ -725,6 +761,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if any(v is not None for v in counters.values()):
+        out["mfma_counters"] = counters
     if cold is not None:
         out["cold"] = cold
     print(json.dumps(out), flush=True)
