@@ -49,7 +49,7 @@ FWD_ONLY = (2, 6)     # single-request serving steps: forward only, bandwidth-bo
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--seed", type=int, default=None)
@@ -676,6 +676,12 @@ def main():
             for j, n in enumerate(bwd_names):
                 per_kernel.setdefault(n, []).append(evb[i][j].elapsed_time(evb[i][j + 1]))
     avg_ms = {n: float(np.mean(v_)) for n, v_ in per_kernel.items()}
+    # spread over the timed steps: p10 / median / p90 of each kernel and of the
+    # step's kernels from the first launch to the last
+    pct = lambda v_: [round(float(x), 4) for x in np.percentile(v_, [10, 50, 90])]
+    spread = {n: pct(v_) for n, v_ in per_kernel.items()}
+    step_span = [evf[i][0].elapsed_time(evb[i][-1] if backward else evf[i][-1]) for i in range(K)]
+    spread["step (first to last kernel)"] = pct(step_span)
 
     D, Hq = m.head_dim, m.num_q_heads
     pairs = plan.visible_pairs
@@ -756,6 +762,7 @@ def main():
         },
         "eager_ms_per_step": round(ms_eager, 4),
         "kernels_ms": {n: round(t, 4) for n, t in avg_ms.items()},
+        "kernels_ms_p10_p50_p90": spread,
         "plan_ms": round(t_plan * 1e3, 3),
         "wall_s": round(wall, 3),
         "roofline": roof,
