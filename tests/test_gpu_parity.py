@@ -132,6 +132,52 @@ def test_graph_replay_of_the_serving_steps(k):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("k", [3, 4])
+def test_graph_replay_of_the_training_step(k):
+    # Forward and backward captured once in a HIP graph (packed replay; staircase,
+    # whose backward also runs the merge of split key tiles): every replay, with
+    # eager work of another plan in between, reproduces the eager outputs and
+    # gradients bit for bit.
+    wl = W.make_config(k)
+    _say(f"case graph replay fwd+bwd {wl.name}")
+    plan = b.Plan(wl.meta).upload("cuda")
+    dt = plan.dtype
+    q, kk, v, do = (torch.from_numpy(x).cuda().to(dt).contiguous() for x in (wl.q, wl.k, wl.v, wl.do))
+    o = torch.empty_like(q)
+    lse = torch.empty((plan.tq, wl.meta.num_q_heads), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(kk), torch.empty_like(v)
+    outs = (o, lse, dq, dk, dv)
+
+    def step():
+        b.fwd(plan, q, kk, v, o, lse)
+        b.bwd(plan, q, kk, v, o, lse, do, dq, dk, dv)
+
+    step()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in outs]
+    other = W.make_config(2, with_do=False)
+    oplan = b.Plan(other.meta).upload("cuda")
+    oq, ok_, ov = (torch.from_numpy(x).cuda().to(torch.bfloat16).contiguous() for x in (other.q, other.k, other.v))
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        for t in outs:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("o", "lse", "dq", "dk", "dv"), outs, refs):
+            assert torch.equal(t, r), name
+        b.fwd(oplan, oq, ok_, ov)             # eager work of another plan between replays
+        torch.cuda.synchronize()
+
+
 def test_denoise_step_no_split_matches_split():
     wl = W.make_config(2, with_do=False)
     g1, _ = run_gpu(wl, backward=False)
