@@ -14,7 +14,9 @@ from typing import Optional, Tuple
 import torch  # loaded first so the library binds to the HIP runtime torch already mapped
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbdattn.so")
+# BDATTN_LIBRARY selects another build of the same library (the host-sanitized
+# copy that build.py --sanitize writes); by default the in-tree libbdattn.so
+LIB_PATH = os.environ.get("BDATTN_LIBRARY") or os.path.join(_HERE, "libbdattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
@@ -286,10 +288,38 @@ def _ptr(t: Optional[torch.Tensor]) -> _vp:
     return _vp(0 if t is None else t.data_ptr())
 
 
-def _expect(t, shape, dtype, name):
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, got "
-                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} cuda={t.is_cuda}")
+def _expect(t, shape, dtype, name, device=None):
+    """Every tensor handed to the library must match the plan's layout exactly:
+    the kernels index raw pointers with the contiguous [rows, heads, D] strides."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda
+            or (device is not None and t.device != device)):
+        raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}"
+                         f"{'' if device is None else ' on ' + str(device)}, got {t.dtype} {tuple(t.shape)} "
+                         f"contiguous={t.is_contiguous()} device={t.device}")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name}: data pointer is not 16-byte aligned")
+
+
+def _shapes(plan):
+    m = plan.meta
+    return ((plan.tq, m.num_q_heads, m.head_dim), (plan.tk, m.num_kv_heads, m.head_dim),
+            (plan.tq, m.num_q_heads))
+
+
+def _out(t, shape, dtype, device, name):
+    """A caller-supplied output is checked like an input; otherwise a fresh
+    contiguous tensor of the plan's shape."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _expect(t, shape, dtype, name, device)
+    return t
+
+
+def _expect_meta(plan, device):
+    if plan.meta_dev.device != device:
+        raise ValueError(f"the plan was uploaded to {plan.meta_dev.device}, the tensors are on {device}")
 
 
 def _events_arg(events):
@@ -304,16 +334,15 @@ def _events_arg(events):
 
 def fwd(plan: Plan, q, k, v, o=None, lse=None, events=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward; ``events`` (optional list of torch.cuda.Event) time each kernel."""
-    m = plan.meta
-    _expect(q, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "q")
-    _expect(k, (plan.tk, m.num_kv_heads, m.head_dim), plan.dtype, "k")
-    _expect(v, (plan.tk, m.num_kv_heads, m.head_dim), plan.dtype, "v")
+    qshape, kshape, lshape = _shapes(plan)
+    _expect(q, qshape, plan.dtype, "q")
+    _expect(k, kshape, plan.dtype, "k", q.device)
+    _expect(v, kshape, plan.dtype, "v", q.device)
     if plan.meta_dev is None:
         plan.upload(q.device)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((plan.tq, m.num_q_heads), dtype=torch.float32, device=q.device)
+    _expect_meta(plan, q.device)
+    o = _out(o, qshape, plan.dtype, q.device, "o")
+    lse = _out(lse, lshape, torch.float32, q.device, "lse")
     args = (plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
             _ptr(plan.ws_fwd), _stream(q.device))
     if events is None:
@@ -326,15 +355,20 @@ def fwd(plan: Plan, q, k, v, o=None, lse=None, events=None) -> Tuple[torch.Tenso
 
 def bwd(plan: Plan, q, k, v, o, lse, do, dq=None, dk=None, dv=None, events=None):
     """Backward; ``events`` (optional list of 4 torch.cuda.Event) time each kernel."""
-    m = plan.meta
-    _expect(do, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "do")
-    _expect(o, (plan.tq, m.num_q_heads, m.head_dim), plan.dtype, "o")
-    _expect(lse, (plan.tq, m.num_q_heads), torch.float32, "lse")
+    qshape, kshape, lshape = _shapes(plan)
+    _expect(q, qshape, plan.dtype, "q")
+    dev = q.device
+    _expect(k, kshape, plan.dtype, "k", dev)
+    _expect(v, kshape, plan.dtype, "v", dev)
+    _expect(o, qshape, plan.dtype, "o", dev)
+    _expect(lse, lshape, torch.float32, "lse", dev)
+    _expect(do, qshape, plan.dtype, "do", dev)
     if plan.meta_dev is None:
-        plan.upload(q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+        plan.upload(dev)
+    _expect_meta(plan, dev)
+    dq = _out(dq, qshape, plan.dtype, dev, "dq")
+    dk = _out(dk, kshape, plan.dtype, dev, "dk")
+    dv = _out(dv, kshape, plan.dtype, dev, "dv")
     args = (plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
             _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(plan.ws_bwd), _stream(q.device))
     if events is None:
@@ -350,7 +384,9 @@ class BdAttnFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, plan):
-        o, lse = fwd(plan, q.contiguous(), k.contiguous(), v.contiguous())
+        # the kernels read the contiguous layout: the same copies serve the backward
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = fwd(plan, q, k, v)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.plan = plan
         return o

@@ -24,6 +24,15 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # registers and every element costs an extra copy before the vector ALU sees it.
 HIP_FILE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# Sanitizer build of the host code (address + undefined behaviour), for the CPU
+# test suite: every source goes through hipcc so one runtime (clang's) serves the
+# whole library; the options apply to the host compilation only (GPU code is
+# never built with a sanitizer). Load the result with the clang ASan runtime
+# preloaded (see sanitizer_env()).
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libbdattn.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def _run(cmd):
@@ -34,27 +43,60 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source and links libbdattn.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compiles every source and links libbdattn.so; returns its path.
+    sanitize=True builds the host-sanitized copy under _build/san instead."""
+    out_dir = SAN_DIR if sanitize else BUILD_DIR
+    lib = SAN_LIB if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
+    san = SAN_FLAGS if sanitize else []
     jobs = []
     for s in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, s.replace(".hip", ".o"))
-        jobs.append(([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj], obj))
+        obj = os.path.join(out_dir, s.replace(".hip", ".o"))
+        jobs.append(([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(s, []), *san, "-c", os.path.join(CSRC, s), "-o", obj],
+                     obj))
     for s in CXX_SOURCES:
-        obj = os.path.join(BUILD_DIR, s.replace(".cpp", ".o"))
-        jobs.append((["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj], obj))
+        obj = os.path.join(out_dir, s.replace(".cpp", ".o"))
+        if sanitize:
+            cmd = [HIPCC, "-x", "c++", *CXX_FLAGS, *san, "-c", os.path.join(CSRC, s), "-o", obj]
+        else:
+            cmd = ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj]
+        jobs.append((cmd, obj))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(lambda j: _run(j[0]), jobs))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[j[1] for j in jobs], "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    link_san = [*san, "-shared-libsan"] if sanitize else []
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_san, *[j[1] for j in jobs], "-o", tmp])
+    os.replace(tmp, lib)
+    return lib
+
+
+def sanitizer_env() -> dict:
+    """Environment for a process that loads the sanitized library: the clang
+    ASan runtime preloaded (the interpreter itself is not instrumented), leak
+    checking off (the interpreter's own allocations), BDATTN_LIBRARY pointing at
+    the sanitized build."""
+    import glob
+    rt = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not rt:
+        raise RuntimeError("clang ASan runtime not found under /opt/rocm/llvm")
+    env = dict(os.environ)
+    env.update(LD_PRELOAD=rt[-1], ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", BDATTN_LIBRARY=SAN_LIB)
+    return env
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    # python build.py [-v] [--sanitize [pytest args...]]: --sanitize builds the
+    # host-sanitized library and, given pytest arguments, runs them against it
+    if "--sanitize" in sys.argv:
+        rest = sys.argv[sys.argv.index("--sanitize") + 1:]
+        print(build(verbose="-v" in sys.argv, sanitize=True))
+        if rest:
+            sys.exit(subprocess.call([sys.executable, "-m", "pytest", *rest], env=sanitizer_env(), cwd=ROOT))
+    else:
+        print(build(verbose="-v" in sys.argv))

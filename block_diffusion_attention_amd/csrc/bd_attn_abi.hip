@@ -218,6 +218,7 @@ bd_attn_status bd_attn_fwd_timed(bd_attn_plan_t plan, const void* meta_dev, cons
   return fwd_impl(plan, meta_dev, q, k, v, o, lse, ws, stream, events, n_events);
 }
 
+
 static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
                                const void* v, const void* o, const float* lse, const void* dout, void* dq,
                                void* dk, void* dv, void* ws, bd_attn_stream_t stream,

@@ -200,53 +200,55 @@ def test_serving_steps_split_sizes(k, tiles):
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
-@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
-def test_staircase_full_kv_group_samples(flags):
-    wl = W.make_config(4)
-    _say(f"case {wl.name} seed 4 flags {flags}")
-    gpu, _ = run_gpu(wl, flags=flags)
-    for g in (0, 5):
-        sub = W.kv_group_slice(wl, g)
-        ref = run_oracle(sub)
-        G = wl.meta.num_q_heads // wl.meta.num_kv_heads
-        gs = {n: (gpu[n][:, g * G:(g + 1) * G] if n in ("o", "dq", "lse") else gpu[n][:, g:g + 1])
-              for n in gpu}
-        _compare(sub, gs, ref)
-
-
-def test_packed_replay_segment_samples():
-    wl = W.make_config(3)
-    _say(f"case {wl.name} seed 3")
-    gpu, _ = run_gpu(wl)
-    qo, ko = wl.meta.q_offsets(), wl.meta.k_offsets()
-    lens = wl.meta.ctx_len
-    for s in (int(np.argmin(lens)), int(np.argmax(lens))):
-        sub = W.kv_group_slice(W.segment_slice(wl, s), 3)
-        ref = run_oracle(sub)
-        gs = {}
-        for n, x in gpu.items():
-            if n in ("o", "dq", "lse"):
-                gs[n] = x[qo[s]:qo[s + 1], 12:16]
-            else:
-                gs[n] = x[ko[s]:ko[s + 1], 3:4]
-        _compare(sub, gs, ref)
-
-
-def test_large_pack_segment_sample():
-    wl = W.make_config(5)
-    _say(f"case {wl.name} seed 5")
-    gpu, _ = run_gpu(wl)
-    qo, ko = wl.meta.q_offsets(), wl.meta.k_offsets()
-    s, g = 2, 6
-    sub = W.kv_group_slice(W.segment_slice(wl, s), g)
-    ref = run_oracle(sub)
-    gs = {}
+def _all_finite(gpu):
+    # outputs start NaN-filled: every element must have been written
     for n, x in gpu.items():
-        if n in ("o", "dq", "lse"):
-            gs[n] = x[qo[s]:qo[s + 1], 4 * g:4 * g + 4]
-        else:
-            gs[n] = x[ko[s]:ko[s + 1], g:g + 1]
-    _compare(sub, gs, ref)
+        assert np.isfinite(x).all(), f"{n}: unwritten or non-finite elements"
+
+
+@pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
+def test_staircase_full(flags):
+    # every element of O, LSE, dQ, dK, dV of the 4096-token staircase (24
+    # canvases), compared one kv head (and its 4 query heads) at a time
+    wl = W.make_config(4)
+    _say(f"case {wl.name} seed 4 flags {flags} (full comparison)")
+    gpu, _ = run_gpu(wl, flags=flags)
+    _all_finite(gpu)
+    G = wl.meta.num_q_heads // wl.meta.num_kv_heads
+    for g in range(wl.meta.num_kv_heads):
+        sub = W.kv_group_slice(wl, g)
+        gs = {n: (x[:, g * G:(g + 1) * G] if n in ("o", "dq", "lse") else x[:, g:g + 1]) for n, x in gpu.items()}
+        _compare(sub, gs, run_oracle(sub))
+        _say(f"  kv head {g} ok")
+
+
+def test_packed_replay_full():
+    # every element of the 16-segment packed replay (the headline workload),
+    # compared one segment (all heads) at a time
+    wl = W.make_config(3)
+    _say(f"case {wl.name} seed 3 (full comparison)")
+    gpu, _ = run_gpu(wl)
+    _all_finite(gpu)
+    qo, ko = wl.meta.q_offsets(), wl.meta.k_offsets()
+    for s in range(wl.meta.num_segments):
+        sub = W.segment_slice(wl, s)
+        gs = {n: (x[qo[s]:qo[s + 1]] if n in ("o", "dq", "lse") else x[ko[s]:ko[s + 1]]) for n, x in gpu.items()}
+        _compare(sub, gs, run_oracle(sub))
+        _say(f"  segment {s} ({wl.meta.ctx_len[s]} context tokens) ok")
+
+
+@pytest.mark.parametrize("g", [1, 6])
+def test_large_pack_all_segments(g):
+    # all four 8192-token segments (16 canvases each) of one kv head and its 4
+    # query heads; the GPU runs the whole pack
+    wl = W.make_config(5)
+    _say(f"case {wl.name} seed 5 kv head {g} (all segments)")
+    gpu, _ = run_gpu(wl)
+    sub = W.kv_group_slice(wl, g)
+    G = wl.meta.num_q_heads // wl.meta.num_kv_heads
+    gs = {n: (x[:, g * G:(g + 1) * G] if n in ("o", "dq", "lse") else x[:, g:g + 1]) for n, x in gpu.items()}
+    _all_finite(gpu)          # the other heads were written too
+    _compare(sub, gs, run_oracle(sub))
 
 
 # ---------------------------------------------------------------- random packs, edge cases
@@ -408,7 +410,9 @@ def test_forced_split_matches_oracle(flags):
 
 @pytest.mark.parametrize("flags", [0, b.FLAG_FWD_VT])
 def test_key_shift_stress(flags):
-    # scores shifted by a large common offset exercise the running-maximum rescaling
+    # every key of the segment shifted by the same vector: each row's scores move
+    # by one common offset (the rescale branch itself is driven by
+    # tests/test_gpu_rescale.py, whose shifts differ between key tiles)
     rng = np.random.default_rng(43)
     meta = W.Meta([512], [0], [[3, 16, 9]], 32, 4, 1, 128, "bf16")
     wl = W.random_workload(rng, meta, sigma=1.0)
@@ -449,3 +453,56 @@ def test_autograd_function():
     assert_close("autograd:dq", q.grad.float().cpu().numpy(), ref["dq"], "bf16")
     assert_close("autograd:dk", k.grad.float().cpu().numpy(), ref["dk"], "bf16")
     assert_close("autograd:dv", v.grad.float().cpu().numpy(), ref["dv"], "bf16")
+
+
+def test_autograd_function_strided_inputs():
+    # q, k, v sliced out of one fused projection (non-contiguous views): the
+    # wrapper hands contiguous copies to the kernels and keeps those for backward
+    rng = np.random.default_rng(46)
+    meta = W.Meta([128, 64], [0, 64], [[1, 4], [2]], 32, 4, 2, 64, "bf16")
+    wl = W.random_workload(rng, meta, sigma=0.5)
+    plan = b.Plan(meta).upload("cuda")
+    Tq = meta.tq
+    assert meta.tk == Tq + 64
+    fused = torch.zeros((meta.tk, 4 + 2 + 2, 64), dtype=torch.bfloat16, device="cuda")
+    fused[:Tq, 0:4] = torch.from_numpy(wl.q).cuda().bfloat16()
+    fused[:, 4:6] = torch.from_numpy(wl.k).cuda().bfloat16()
+    fused[:, 6:8] = torch.from_numpy(wl.v).cuda().bfloat16()
+    fused.requires_grad_()
+    q, k, v = fused[:Tq, 0:4], fused[:, 4:6], fused[:, 6:8]
+    assert not q.is_contiguous() and not k.is_contiguous()
+    o = b.attention(q, k, v, plan)
+    o.backward(torch.from_numpy(wl.do).cuda().bfloat16())
+    ref = run_oracle(wl)
+    g = fused.grad.float().cpu().numpy()
+    assert_close("strided:o", o.detach().float().cpu().numpy(), ref["o"], "bf16")
+    assert_close("strided:dq", g[:Tq, 0:4], ref["dq"], "bf16")
+    assert_close("strided:dk", g[:, 4:6], ref["dk"], "bf16")
+    assert_close("strided:dv", g[:, 6:8], ref["dv"], "bf16")
+
+
+def test_binding_rejects_mismatched_buffers():
+    # every tensor the kernels write or read must match the plan's layout: a
+    # mis-shaped, mistyped or strided buffer raises before anything is launched
+    rng = np.random.default_rng(47)
+    meta = W.Meta([64], [0], [[2]], 32, 4, 1, 64, "bf16")
+    wl = W.random_workload(rng, meta, sigma=0.5)
+    plan = b.Plan(meta).upload("cuda")
+    q, k, v, do = (torch.from_numpy(x).cuda().bfloat16().contiguous() for x in (wl.q, wl.k, wl.v, wl.do))
+    o, lse = b.fwd(plan, q, k, v)
+    with pytest.raises(ValueError, match="dq"):
+        b.bwd(plan, q, k, v, o, lse, do, dq=torch.empty((q.shape[0] - 1,) + q.shape[1:], dtype=q.dtype,
+                                                           device="cuda"))
+    with pytest.raises(ValueError, match="dk"):
+        b.bwd(plan, q, k, v, o, lse, do, dk=torch.empty_like(k, dtype=torch.float32))
+    with pytest.raises(ValueError, match="dv"):
+        b.bwd(plan, q, k, v, o, lse, do, dv=torch.empty((k.shape[0], k.shape[1], 2 * k.shape[2]),
+                                                           dtype=k.dtype, device="cuda")[:, :, :64])
+    with pytest.raises(ValueError, match="q"):
+        b.bwd(plan, q[:-1], k, v, o, lse, do)
+    with pytest.raises(ValueError, match="k"):
+        b.fwd(plan, q, k.float(), v)
+    with pytest.raises(ValueError, match="o"):
+        b.fwd(plan, q, k, v, o=torch.empty((q.shape[0], q.shape[1] + 1, q.shape[2]), dtype=q.dtype, device="cuda"))
+    with pytest.raises(ValueError, match="lse"):
+        b.fwd(plan, q, k, v, lse=torch.empty((q.shape[0], q.shape[1]), dtype=torch.bfloat16, device="cuda"))
