@@ -64,6 +64,7 @@ _lib.bd_attn_plan_serialize.argtypes = [_vp, _vp, _sz]
 _lib.bd_attn_plan_upload.argtypes = [_vp, _vp, _vp]
 _lib.bd_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.bd_attn_bwd.argtypes = [_vp] * 13
+_lib.bd_attn_fwd_noalloc.argtypes = [_vp] * 8
 _lib.bd_attn_fwd_timed.argtypes = [_vp] * 10 + [ctypes.c_int]
 _lib.bd_attn_bwd_timed.argtypes = [_vp] * 14 + [ctypes.c_int]
 _lib.bd_attn_plan_kernels.argtypes = [_vp, ctypes.c_int32]
@@ -74,7 +75,8 @@ _lib.bd_attn_plan_destroy.argtypes = [_vp]
 _lib.bd_attn_last_error.restype = ctypes.c_char_p
 _lib.bd_attn_version.restype = ctypes.c_char_p
 for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
-           "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_destroy"):
+           "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_destroy",
+           "bd_attn_fwd_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -150,7 +152,10 @@ EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_
             "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
             "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version",
             "bd_attn_pack", "bd_aec_workspace", "bd_aec_fwd", "bd_aec_fwd_timed", "bd_aec_kernels",
-            "bd_aec_bwd", "bd_aec_bwd_timed")
+            "bd_aec_bwd", "bd_aec_bwd_timed", "bd_attn_fwd_noalloc")
+
+# size of the fixed forward workspace of bd_attn_fwd_noalloc (BD_ATTN_NOALLOC_WS_BYTES)
+NOALLOC_WS_BYTES = 32 << 20
 
 
 class BdAttnError(RuntimeError):
@@ -350,6 +355,23 @@ def fwd(plan: Plan, q, k, v, o=None, lse=None, events=None) -> Tuple[torch.Tenso
     else:
         arr, n = _events_arg(events)
         _check(_lib.bd_attn_fwd_timed(*args, ctypes.cast(arr, _vp), n))
+    return o, lse
+
+
+def fwd_noalloc(plan: Plan, q, k, v, o, lse):
+    """Forward through bd_attn_fwd_noalloc: the workspace is the library's fixed
+    per-GPU array, and o / lse are the caller's (no allocation in the call)."""
+    qshape, kshape, lshape = _shapes(plan)
+    _expect(q, qshape, plan.dtype, "q")
+    _expect(k, kshape, plan.dtype, "k", q.device)
+    _expect(v, kshape, plan.dtype, "v", q.device)
+    _expect(o, qshape, plan.dtype, "o", q.device)
+    _expect(lse, lshape, torch.float32, "lse", q.device)
+    if plan.meta_dev is None:
+        raise ValueError("upload the plan before calling fwd_noalloc")
+    _expect_meta(plan, q.device)
+    _check(_lib.bd_attn_fwd_noalloc(plan.handle, _ptr(plan.meta_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                    _ptr(lse), _stream(q.device)))
     return o, lse
 
 

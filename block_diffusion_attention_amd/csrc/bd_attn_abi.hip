@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -218,6 +219,61 @@ bd_attn_status bd_attn_fwd_timed(bd_attn_plan_t plan, const void* meta_dev, cons
   return fwd_impl(plan, meta_dev, q, k, v, o, lse, ws, stream, events, n_events);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Forward workspace of bd_attn_fwd_noalloc: a fixed array in the code object's
+// device memory, so a call allocates nothing. Each GPU the library runs on holds
+// its own copy until the process ends; host code only ever uses the address
+// hipGetSymbolAddress returns for the device (the array's name is a host-side
+// stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[BD_ATTN_NOALLOC_WS_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];   // scratch's device address per GPU, looked up once
+
+// Device address of scratch on the GPU that runs `stream`, looked up with that
+// GPU current (restoring the caller's current device afterwards).
+bd_attn_status scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(BD_ATTN_EUNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return hip_status(e, "hipSetDevice (restore)");
+    if (es != hipSuccess) return hip_status(es, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(BD_ATTN_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return BD_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bd_attn_status bd_attn_fwd_noalloc(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
+                                   const void* v, void* o, float* lse, bd_attn_stream_t stream) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  if (plan->p.ws_fwd > (size_t)BD_ATTN_NOALLOC_WS_BYTES)
+    return fail(BD_ATTN_EWORKSPACE, "the plan's forward workspace (" + std::to_string(plan->p.ws_fwd) +
+                                        " bytes) exceeds the fixed array of bd_attn_fwd_noalloc (" +
+                                        std::to_string((size_t)BD_ATTN_NOALLOC_WS_BYTES) + " bytes)");
+  void* ws = nullptr;
+  if (plan->p.ws_fwd > 0) {
+    if (bd_attn_status st = scratch_for(reinterpret_cast<hipStream_t>(stream), &ws)) return st;
+  }
+  return fwd_impl(plan, meta_dev, q, k, v, o, lse, ws, stream, nullptr, 0);
+}
 
 static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const void* q, const void* k,
                                const void* v, const void* o, const float* lse, const void* dout, void* dq,

@@ -167,6 +167,23 @@ bd_attn_status bd_attn_bwd(bd_attn_plan_t plan, const void* meta_dev,
                            const void* o, const float* lse, const void* dout,
                            void* dq, void* dk, void* dv, void* ws, bd_attn_stream_t stream);
 
+/* Forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same as
+ * bd_attn_fwd, except that the forward workspace is a fixed array of
+ * BD_ATTN_NOALLOC_WS_BYTES inside the library's device code object (one copy per
+ * GPU, held until the process ends) instead of a caller buffer; the call itself
+ * allocates nothing. Nothing in it needs to start at zero (every call writes what
+ * it later reads). All calls on one GPU share that array and it keeps the last
+ * call's contents: calls that overlap on one GPU (different streams, or host
+ * threads without ordering) race and may return wrong results.
+ * Errors: EWORKSPACE (checked before any device call) when the plan's
+ * ws_fwd_bytes exceeds BD_ATTN_NOALLOC_WS_BYTES; otherwise as bd_attn_fwd, plus
+ * EHIP if the array's device address cannot be looked up. */
+#define BD_ATTN_NOALLOC_WS_BYTES (32u << 20)
+bd_attn_status bd_attn_fwd_noalloc(bd_attn_plan_t plan, const void* meta_dev,
+                                   const void* q, const void* k, const void* v,
+                                   void* o, float* lse, bd_attn_stream_t stream);
+
 /* Same as bd_attn_fwd / bd_attn_bwd, and in addition records caller-created
  * hipEvent_t handles (passed as void*) on the stream around the kernels, for
  * per-kernel timing on the stream that runs them: events[0] before the first
