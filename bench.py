@@ -95,7 +95,7 @@ KERNEL_SOURCES = {
     "dkdv_masked": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "dq": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "bwd_pre": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
-    "combine": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "merge": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "aec_entropy": ["aec.hip", "aec.h"],
     "aec_grad": ["aec.hip", "aec.h"],
 }
@@ -128,7 +128,7 @@ def traffic_from_profiles(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-KERNEL_SYMBOLS = {"fwd": "fwd_", "combine": "combine_kernel", "bwd_pre": "bwd_pre_kernel",
+KERNEL_SYMBOLS = {"fwd": "fwd_", "merge": "merge_kernel", "bwd_pre": "bwd_pre_kernel",
                   "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel", "transpose_v": "transpose_v_kernel",
                   "aec_entropy": "aec_entropy_kernel", "aec_grad": "aec_grad_kernel"}
 COPY_SYMBOL = "MulFunctor"
@@ -698,7 +698,7 @@ def main():
         "dkdv": ("mfma", 8.0 * D * Hq * pairs),
         "dq": ("mfma", 6.0 * D * Hq * pairs),
         "bwd_pre": ("hbm", 2.0 * q_bytes + 3.0 * plan.tq * Hq * 4),
-        "combine": ("hbm", q_bytes + plan.tq * Hq * 4),
+        "merge": ("hbm", q_bytes + plan.tq * Hq * 4),
         "transpose_v": ("hbm", 2.0 * kv_bytes),
     }
     if k in FWD_ONLY:   # the serving steps are bandwidth-bound: their forward is priced in bytes

@@ -25,7 +25,11 @@ namespace {
 // LDS operand reads run this many products ahead of the MFMA that consumes them.
 constexpr int kFwdAhead = 4;
 
-template <int D>
+// SPLIT: one part of a split key range (short query streams over long contexts):
+// the item comes with its query tile in one record, the first two key tiles are
+// requested together before anything else, and the result is a partial (bf16 O
+// normalized by the part's own row sums, fp32 LSE) for the merge kernel.
+template <int D, bool SPLIT>
 __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   constexpr int KT = kKTile;
   constexpr int NDB = D / 32;
@@ -42,12 +46,11 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: copy targets in SGPRs
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
-  const int idx = a.order ? ld_rec1(a.order, blockIdx.x) : (int)blockIdx.x;
-  if (idx < 0) return;                              // empty slot of the split launch order
-  const int4 itv = ld_rec4(a.items, idx);
-  if (itv.x < 0) return;
-  const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
-  const QTile qt = load_qtile(a.qtiles, itv.x);
+  FwdWork w;
+  if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w) : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w))
+    return;                                         // empty launch slot
+  const int kvh = w.kvh, kt_begin = w.kt_begin, kt_end = w.kt_end;
+  const QTile& qt = w.qt;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
   const bf16* __restrict__ V = static_cast<const bf16*>(a.v);
@@ -76,6 +79,9 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
     fetch.issue(dV, V + off0, nvalid, last, wave);
   };
   issue(kt_begin, sK0, sV0);
+  // a split part is short: its second tile goes out at once too (one memory
+  // round trip for the whole part instead of one per tile)
+  if (SPLIT && kt_begin + 1 < kt_end) issue(kt_begin + 1, sK1, sV1);
 
   bf16x8 qf[NKS];
   {
@@ -117,8 +123,8 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
     });
     // the next tile's copies go out after the S products, so their LDS writes do
     // not compete with this tile's K operand reads (the other stage is free since
-    // the barrier)
-    if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
+    // the barrier; a split part's second tile is already on its way)
+    if (kt + 1 < kt_end && (!SPLIT || kt + 1 > kt_begin + 1)) issue(kt + 1, nK, nV);
 
     // masking only on tiles that cross a row limit or the end of a range
     if (need_mask) {
@@ -183,18 +189,8 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const float lt = l + swap_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
-  if (a.part_o) {
-    float* po = a.part_o + ((int64_t)idx * kQRows + row) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[db][g4 * 4 + e] * inv;
-        *reinterpret_cast<f32x4*>(po + db * 32 + g4 * 8 + h * 4) = v;
-      }
-    if (h == 0) a.part_lse[(int64_t)idx * kQRows + row] = lse;
+  if constexpr (SPLIT) {
+    store_partial<D>(a.part_o, a.part_lse, w.slot, wave, lane, acc, inv, lse);
   } else if (row_ok) {
     bf16* op = static_cast<bf16*>(a.o) + qrow * D;
 #pragma unroll
@@ -210,99 +206,103 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-// Merges the split partial results of one query tile: lse = log sum_i exp(lse_i),
-// O = sum_i exp(lse_i - lse) O_i. Workgroup: kCombRows rows of one merge item,
-// one thread per (row, 4 columns); blockIdx.x = item * (kQRows / rows) + group.
-constexpr int kCombFast = 16;   // splits merged from registers in one round trip
+// Merges the partial results of a split key range: for each row,
+//   lse = log sum_i exp(lse_i),  O = sum_i exp(lse_i - lse) O_i
+// over the parts i in key order. One wave per workgroup merges one block of the
+// partials' register-order layout (32 rows x 16 columns; lane j + 32 h holds row
+// 32 w + j, columns 32 db + 16 p + 4 h + {0..3} and + 8 + {0..3}): every load of
+// a part is one contiguous 1 KiB. Parts are taken kMergeBatch at a time with all
+// of a batch's loads issued before the first is used (one memory round trip per
+// batch), folded into a running maximum.
+constexpr int kMergeBatch = 32;
 
-template <int D, bool BF16>
-__global__ void __launch_bounds__(256) combine_kernel(CombArgs a) {
-  constexpr int C4 = D / 4;
-  constexpr int RPW = 256 / C4;                    // rows per workgroup
-  constexpr int GROUPS = kQRows / RPW;
-  const int item = blockIdx.x / GROUPS;
-  const int row = (blockIdx.x - item * GROUPS) * RPW + threadIdx.x / C4;
-  const int c = threadIdx.x % C4;
-  const int4 it = ld_rec4(a.items, item);
-  const QTile qt = load_qtile(a.qtiles, it.x);
-  const int kvh = it.y, first = it.z, count = it.w;
-  if (row >= qt.n_tok * a.G) return;
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(MergeArgs a) {
+  constexpr int NDB = D / 32;
+  const int i = blockIdx.x;
+  const int4 r0 = ld_rec4(a.items, 4 * i), r2 = ld_rec4(a.items, 4 * i + 2);
+  const int kvh = r2.x, first = r2.y, count = r2.z, blk = r2.w;
+  if (kvh < 0) return;                             // empty launch slot
+  const int q_tok = r0.x, n_tok = r0.y;
+  const int w = blk / (2 * NDB), db = (blk / 2) % NDB, p = blk % 2;
+  const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
+  const int row = w * 32 + j;
   const float* pl = a.part_lse + (int64_t)first * kQRows + row;
-  const float* po = a.part_o + ((int64_t)first * kQRows + row) * D + c * 4;
-  float mx = -INFINITY;
-  float wsum = 0.f;
-  f32x4 accv = f32x4{};
-  if (count <= kCombFast) {
-    // every partial LSE and O of the row is requested before the first is used:
-    // one memory round trip instead of one per loop iteration
-    float lv[kCombFast];
-    f32x4 ov[kCombFast];
+  const bf16* po = static_cast<const bf16*>(a.part_o) + ((int64_t)(first * 4 + w) * NDB * 2 + blk % (2 * NDB)) * 512 +
+                   8 * lane;
+  constexpr int64_t kSlotElems = (int64_t)kQRows * D;
+  float m = -INFINITY, wsum = 0.f;
+  float acc[8];
 #pragma unroll
-    for (int i = 0; i < kCombFast; ++i) {
-      lv[i] = -INFINITY;
-      ov[i] = f32x4{};
-      if (i < count) {
-        lv[i] = pl[(int64_t)i * kQRows];
-        ov[i] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * kQRows * D);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int i0 = 0; i0 < count; i0 += kMergeBatch) {
+    const int n = min(kMergeBatch, count - i0);
+    float lv[kMergeBatch];
+    u32x4 ov[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      lv[k] = -INFINITY;
+      ov[k] = u32x4{0u, 0u, 0u, 0u};
+      if (k < n) {
+        lv[k] = pl[(int64_t)(i0 + k) * kQRows];
+        ov[k] = *reinterpret_cast<const u32x4*>(po + (int64_t)(i0 + k) * kSlotElems);
       }
     }
+    float mx = m;
 #pragma unroll
-    for (int i = 0; i < kCombFast; ++i) mx = fmaxf(mx, lv[i]);
-    if (mx != -INFINITY) {
+    for (int k = 0; k < kMergeBatch; ++k) mx = fmaxf(mx, lv[k]);
+    if (mx == -INFINITY) continue;                  // no part of this batch sees the row
+    const float alpha = __expf(m - mx);             // 0 while m is -inf
+    wsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < kCombFast; ++i) {
-        if (i < count) {
-          const float w = __expf(lv[i] - mx);
-          wsum += w;
-          accv += w * ov[i];
-        }
-      }
-    }
-  } else {
-    for (int i = 0; i < count; ++i) mx = fmaxf(mx, pl[(int64_t)i * kQRows]);
-    if (mx != -INFINITY) {
-#pragma unroll 4
-      for (int i = 0; i < count; ++i) {
-        const float w = __expf(pl[(int64_t)i * kQRows] - mx);
-        wsum += w;
-        accv += w * *reinterpret_cast<const f32x4*>(po + (int64_t)i * kQRows * D);
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    m = mx;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wk = __expf(lv[k] - m);           // 0 for the padding entries
+      wsum += wk;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[2 * u] += wk * __builtin_bit_cast(float, ov[k][u] << 16);
+        acc[2 * u + 1] += wk * __builtin_bit_cast(float, ov[k][u] & 0xffff0000u);
       }
     }
   }
+  if (row >= n_tok * a.G) return;                   // padding row of the query tile
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int t = row / a.G, gh = row - t * a.G;
-  const int64_t qrow = (int64_t)(qt.q_tok + t) * a.hq + kvh * a.G + gh;
-  if (BF16) {
+  const int64_t qrow = (int64_t)(q_tok + t) * a.hq + kvh * a.G + gh;
+  bf16* op = static_cast<bf16*>(a.o) + qrow * D + db * 32 + p * 16 + h * 4;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
     u32x2 v;
-    v[0] = pack_bf16x2(accv[0] * inv, accv[1] * inv);
-    v[1] = pack_bf16x2(accv[2] * inv, accv[3] * inv);
-    *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.o) + qrow * D + c * 4) = v;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + qrow * D + c * 4) = accv * inv;
+    v[0] = pack_bf16x2(acc[4 * half + 0] * inv, acc[4 * half + 1] * inv);
+    v[1] = pack_bf16x2(acc[4 * half + 2] * inv, acc[4 * half + 3] * inv);
+    *reinterpret_cast<u32x2*>(op + 8 * half) = v;
   }
-  if (c == 0) a.lse[qrow] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+  if (h == 0 && blk % (2 * NDB) == 0) a.lse[qrow] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+  if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int items, hipStream_t s) {
-  if (items <= 0) return hipSuccess;
-  const int groups = kQRows / (256 / (head_dim / 4));
-  const dim3 grid((unsigned)(items * groups));
-  if (head_dim == 128) {
-    if (bf16_out) hipLaunchKernelGGL((combine_kernel<128, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<128, false>), grid, dim3(256), 0, s, a);
-  } else {
-    if (bf16_out) hipLaunchKernelGGL((combine_kernel<64, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<64, false>), grid, dim3(256), 0, s, a);
-  }
+hipError_t launch_fwd_split_direct(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, s, a);
+  else hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

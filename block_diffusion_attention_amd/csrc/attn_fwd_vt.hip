@@ -62,7 +62,9 @@ __device__ __forceinline__ bf16x8 ptr_operand(const float* p) {
   return __builtin_bit_cast(bf16x8, u32x4{(uint32_t)s02[0], (uint32_t)s13[0], (uint32_t)s02[1], (uint32_t)s13[1]});
 }
 
-template <int D>
+// SPLIT: one part of a split key range, item from the split list (with its query
+// tile), result written as a partial for the merge kernel.
+template <int D, bool SPLIT>
 __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   constexpr int KT = kKTile;
   constexpr int NDB = D / 32;
@@ -79,12 +81,11 @@ __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   const int j = lane & 31, h = lane >> 5;
   const int kbase = pad_base<D / 8>(lane);        // K operand rows
   const int vbase = pad_base<KT / 8>(lane);       // VT operand dimensions
-  const int idx = a.order ? __builtin_amdgcn_readfirstlane(a.order[blockIdx.x]) : (int)blockIdx.x;
-  if (idx < 0) return;                              // empty slot of the split launch order
-  const int4 itv = ld_rec4(a.items, idx);
-  if (itv.x < 0) return;
-  const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
-  const QTile qt = load_qtile(a.qtiles, itv.x);
+  FwdWork w;
+  if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w) : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w))
+    return;                                         // empty launch slot
+  const int kvh = w.kvh, kt_begin = w.kt_begin, kt_end = w.kt_end;
+  const QTile& qt = w.qt;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
   const bf16* __restrict__ VT = static_cast<const bf16*>(a.vt) + (int64_t)kvh * D * a.tk_pad;
@@ -198,18 +199,8 @@ __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   const float lt = l + swap_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
-  if (a.part_o) {
-    float* po = a.part_o + ((int64_t)idx * kQRows + row) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[db][g4 * 4 + e] * inv;
-        *reinterpret_cast<f32x4*>(po + db * 32 + g4 * 8 + h * 4) = v;
-      }
-    if (h == 0) a.part_lse[(int64_t)idx * kQRows + row] = lse;
+  if constexpr (SPLIT) {
+    store_partial<D>(a.part_o, a.part_lse, w.slot, wave, lane, acc, inv, lse);
   } else if (row_ok) {
     bf16* op = static_cast<bf16*>(a.o) + qrow * D;
 #pragma unroll
@@ -240,8 +231,15 @@ hipError_t launch_transpose_v(const void* v, void* vt, int tk, int tk_pad, int h
 
 hipError_t launch_fwd_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(fwd_vt_kernel<128>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(fwd_vt_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+  if (head_dim == 128) hipLaunchKernelGGL((fwd_vt_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fwd_vt_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_split_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL((fwd_vt_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fwd_vt_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

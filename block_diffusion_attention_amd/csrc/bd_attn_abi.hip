@@ -77,7 +77,7 @@ const char* kernel_name(const Plan& p, bool backward, int i) {
     if (i == 0) return "transpose_v";
     --i;
   }
-  return i == 0 ? "fwd" : "combine";
+  return i == 0 ? "fwd" : "merge";
 }
 
 template <class T>
@@ -183,27 +183,25 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
     a.vt = vt;
     a.tk_pad = (int)p.tk_pad;
   }
-  auto launch = [&](int grid) {
-    return p.use_vt ? bdattn::launch_fwd_vt(a, D, grid, s) : bdattn::launch_fwd_bf16(a, D, grid, s);
-  };
   if (!split) {
-    e = launch((int)p.fwd_items.size());
+    const int grid = (int)p.fwd_items.size();
+    e = p.use_vt ? bdattn::launch_fwd_vt(a, D, grid, s) : bdattn::launch_fwd_bf16(a, D, grid, s);
     if ((st = hip_status(e, "fwd launch"))) return st;
     return hip_status(ev.mark(mark), "hipEventRecord");
   }
-  a.order = section<int32_t>(meta_dev, p.off_fwd_order);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_part);
+  a.splits = section<bdattn::SplitItem>(meta_dev, p.off_split);
+  a.part_o = static_cast<char*>(ws) + p.off_ws_part;
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_lse);
-  e = launch((int)p.fwd_order.size());
+  const int grid = (int)p.split_items.size();
+  e = p.use_vt ? bdattn::launch_fwd_split_vt(a, D, grid, s) : bdattn::launch_fwd_split_direct(a, D, grid, s);
   if ((st = hip_status(e, "fwd (split) launch"))) return st;
   if ((st = hip_status(ev.mark(mark++), "hipEventRecord"))) return st;
-  bdattn::CombArgs c{};
-  c.qtiles = a.qtiles;
-  c.items = section<bdattn::CombItem>(meta_dev, p.off_comb);
+  bdattn::MergeArgs c{};
+  c.items = section<bdattn::MergeItem>(meta_dev, p.off_merge);
   c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
   c.hq = a.hq; c.G = a.G;
-  e = bdattn::launch_combine(c, D, true, (int)p.comb_items.size(), s);
-  if ((st = hip_status(e, "combine launch"))) return st;
+  e = bdattn::launch_merge(c, D, (int)p.merge_items.size(), s);
+  if ((st = hip_status(e, "merge launch"))) return st;
   return hip_status(ev.mark(mark), "hipEventRecord");
 }
 

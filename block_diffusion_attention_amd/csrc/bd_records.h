@@ -36,11 +36,11 @@ constexpr int kMaxGroup = 32;
 
 // Serialized plan: a header of kBlobHeaderInts int32 (magic, format version,
 // then count and int32 offset of each section: query tiles, forward items,
-// forward launch order, combine items, dQ items, key tiles, canvas-query
-// entries, dK/dV items, dK/dV merge items), followed by the sections, each
-// 16-byte aligned.
+// split-forward items, merge items, dQ items, key tiles, canvas-query entries,
+// dK/dV items, dK/dV merge items), followed by the sections, each 16-byte
+// aligned.
 constexpr int kBlobHeaderInts = 32;
-constexpr int kBlobVersion = 2;
+constexpr int kBlobVersion = 3;
 constexpr int kBlobSections = 9;
 constexpr int32_t kBlobMagic = 0x62646174;   // "bdat"
 
@@ -62,11 +62,30 @@ struct FwdItem {       // 4 x int32: one workgroup of the forward / dQ kernels
   int32_t kt_end;      // one past the last key tile
 };
 
-struct CombItem {      // 4 x int32: merge of the split partial results of one query tile
-  int32_t qtile;
-  int32_t kvh;
-  int32_t first;       // index of the first split item (partial slot)
-  int32_t count;       // number of consecutive split items
+// Forward split path (short query streams over long key ranges): the key range
+// of a (query tile, kv head) is cut into parts of a few key tiles; each part is
+// one workgroup that writes a partial result (bf16 O normalized by its own row
+// sums, fp32 LSE) into its slot, and a merge kernel combines the slots.
+// Both record kinds carry a copy of their query tile, so one scalar load of
+// 16 dwords gives a workgroup everything it needs; both lists are in launch
+// order (empty launch slots have kvh = -1).
+struct SplitItem {     // 16 x int32: one workgroup of the split forward
+  QTile qt;            // the query tile
+  int32_t kvh;         // kv head, or -1 for an empty launch slot
+  int32_t kt_begin;    // key tiles [kt_begin, kt_end) of the tile's list
+  int32_t kt_end;
+  int32_t slot;        // partial slot written
+  int32_t pad[4];
+};
+
+struct MergeItem {     // 16 x int32: one workgroup of the merge kernel
+  QTile qt;            // the query tile
+  int32_t kvh;         // kv head, or -1 for an empty launch slot
+  int32_t first;       // first partial slot of the tile's parts
+  int32_t count;       // consecutive slots, one per part, in key order
+  int32_t block;       // partial block merged: split wave w, 32-column block db and
+                       // 16-column pair p as (w * (D / 32) + db) * 2 + p
+  int32_t pad[4];
 };
 
 struct KTile {         // 8 x int32
@@ -102,7 +121,17 @@ struct BwdMerge {      // 4 x int32: sum of the partial dK/dV of one split key t
   int32_t count;       // consecutive partial slots, summed in slot order
 };
 
+// Partial O of a split part is stored in the order the forward kernel's
+// registers hold it, so every store instruction writes 1 KiB contiguously:
+// slot s, wave w (rows 32 w .. 32 w + 31), 32-column block db, pair p of
+// 8-column groups, lane l = j + 32 h (row 32 w + j) -> 8 bf16 at element
+//   ((s * 4 + w) * (D / 32) * 2 + db * 2 + p) * 512 + 8 l,
+// holding columns 32 db + 16 p + 4 h + e and 32 db + 16 p + 8 + 4 h + e
+// (e = 0..3). One merge wave per (part block w, db, p): 32 rows x 16 columns.
+constexpr int kMergeThreads = 64;
+
 static_assert(sizeof(QTile) == 32, "QTile layout");
+static_assert(sizeof(SplitItem) == 64 && sizeof(MergeItem) == 64, "split record layout");
 static_assert(sizeof(KTile) == 32, "KTile layout");
 
 }  // namespace bdattn

@@ -330,6 +330,54 @@ __device__ __forceinline__ QTile load_qtile(const int32_t* base, int i) {
   return q;
 }
 
+// Work of one forward workgroup: its query tile, kv head, key-tile range and, on
+// the split path, the partial slot it writes.
+struct FwdWork {
+  QTile qt;
+  int kvh, kt_begin, kt_end, slot;
+};
+
+// Direct path: item i (launch order) and its query tile, two dependent scalar
+// loads. Returns false for an empty launch slot.
+__device__ __forceinline__ bool load_fwd_work(const void* items, const int32_t* qtiles, int i, FwdWork* w) {
+  const int4 itv = ld_rec4(items, i);
+  if (itv.x < 0) return false;
+  w->kvh = itv.y; w->kt_begin = itv.z; w->kt_end = itv.w; w->slot = -1;
+  w->qt = load_qtile(qtiles, itv.x);
+  return true;
+}
+
+// Split path: item i carries its query tile; its three 16-byte parts are
+// independent scalar loads (one memory round trip).
+__device__ __forceinline__ bool load_split_work(const void* splits, int i, FwdWork* w) {
+  const int4 a = ld_rec4(splits, 4 * i), b = ld_rec4(splits, 4 * i + 1), c = ld_rec4(splits, 4 * i + 2);
+  w->qt.q_tok = a.x; w->qt.n_tok = a.y; w->qt.k_ctx = a.z; w->qt.pos0 = a.w;
+  w->qt.lim_max = b.x; w->qt.lim_min = b.y; w->qt.k_own = b.z; w->qt.n_own = b.w;
+  w->kvh = c.x; w->kt_begin = c.y; w->kt_end = c.z; w->slot = c.w;
+  return w->kvh >= 0;
+}
+
+// Partial result of a split workgroup, in register order (see the layout next to
+// kMergeThreads): wave w's acc[db][8 p .. 8 p + 7] times inv (the part's own row
+// sum) as 8 bf16 per lane, one contiguous 1 KiB store per (db, p); the part's
+// LSE of row 32 w + j from lane j.
+template <int D>
+__device__ __forceinline__ void store_partial(void* part_o, float* part_lse, int slot, int wave, int lane,
+                                              const f32x16 (&acc)[D / 32], float inv, float lse) {
+  constexpr int NDB = D / 32;
+  bf16* po = static_cast<bf16*>(part_o) + ((int64_t)(slot * 4 + wave) * NDB * 2) * 512 + 8 * lane;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = acc[db][8 * p + e] * inv;
+      *reinterpret_cast<bf16x8*>(po + (db * 2 + p) * 512) = pack8(x);
+    }
+  if (lane < 32) part_lse[(int64_t)slot * kQRows + wave * 32 + lane] = lse;
+}
+
 __device__ __forceinline__ KTile load_ktile(const int32_t* base, int i) {
   int4 a = ld_rec4(base, 2 * i), b = ld_rec4(base, 2 * i + 1);
   KTile k;

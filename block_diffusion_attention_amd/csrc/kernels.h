@@ -9,15 +9,15 @@ namespace bdattn {
 
 struct FwdArgs {
   const int32_t* qtiles;
-  const FwdItem* items;
-  const int32_t* order;      // launch order over items (split mode) or NULL
+  const FwdItem* items;      // direct path: one item per workgroup
+  const SplitItem* splits;   // split path: one item per workgroup (else NULL)
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
-  float* part_o;             // split mode: partial O [slot][kQRows][D] fp32, else NULL
-  float* part_lse;           // split mode: partial LSE [slot][kQRows]
+  void* part_o;              // split path: partial O [slot][kQRows][D] bf16
+  float* part_lse;           // split path: partial LSE [slot][kQRows] fp32
   const void* vt;            // V transposed, [Hkv][D][tk_pad] (pipelined kernel)
   int tk_pad;
   int hq, hkv, G;
@@ -26,11 +26,10 @@ struct FwdArgs {
   float scale;               // softmax scale
 };
 
-struct CombArgs {
-  const int32_t* qtiles;
-  const CombItem* items;
-  const float* part_o;
-  const float* part_lse;
+struct MergeArgs {
+  const MergeItem* items;    // one per workgroup, launch order
+  const void* part_o;        // [slot][kQRows][D] bf16
+  const float* part_lse;     // [slot][kQRows]
   void* o;
   float* lse;
   int hq, G;
@@ -63,7 +62,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
-hipError_t launch_combine(const CombArgs& a, int head_dim, bool bf16_out, int items, hipStream_t s);
+hipError_t launch_fwd_split_direct(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_fwd_split_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, bool masked, int grid, hipStream_t s);
 hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s);

@@ -224,58 +224,92 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   const int64_t direct_items = nq * Hkv;
   bool split = false;
   int64_t tps = 0;   // key tiles per split
-  if (!(d->flags & BD_ATTN_FLAG_NO_SPLIT)) {
-    const int64_t target = 2 * 256;   // two workgroups per compute unit
+  if (!(d->flags & BD_ATTN_FLAG_NO_SPLIT) && d->dtype == BD_ATTN_BF16) {
     const int64_t want = (d->flags >> 8) & 0xff;     // caller's key tiles per split
     if (d->flags & BD_ATTN_FLAG_FORCE_SPLIT) {
       tps = want > 0 ? want : std::max<int64_t>(1, (max_tiles + 1) / 2);
       split = tps < max_tiles;
-    } else if (direct_items < target && max_tiles >= 4) {
-      // at least 4 key tiles per split: fewer partial results to write and merge
-      // (measured best on the single-request denoising shape)
-      tps = want > 0 ? want : std::max<int64_t>(4, ceil_div(total_tiles * Hkv, target));
+    } else if (direct_items < 2 * 256 && max_tiles >= 4) {
+      // Short query streams over long key ranges (fewer direct items than two
+      // per compute unit): parts of about total / 256 key tiles, so that every
+      // compute unit gets one part, each part's loads are all in flight at once
+      // and a part's partial result is no larger than the keys it read.
+      tps = want > 0 ? want : std::max<int64_t>(1, ceil_div(total_tiles * Hkv, 256));
       split = tps < max_tiles;
     }
   }
   p.split = split;
-  p.fwd_items.clear(); p.comb_items.clear();
+  p.fwd_items.clear(); p.split_items.clear(); p.merge_items.clear();
   {
+    // raw items: (query tile, kv head, key-tile range); on the split path their
+    // index is the partial slot, and each (query tile, kv head) has a merge entry
     std::vector<FwdItem> raw;
     std::vector<int64_t> cost, cls;
+    struct Merge { int32_t qtile, kvh, first, count; };
+    std::vector<Merge> merges;
     for (int64_t i = 0; i < nq; ++i) {
       const int64_t nt = tiles_of(p.qtiles[i]);
       for (int h = 0; h < Hkv; ++h) {
-        if (split && nt > tps) {
-          CombItem ci{(int32_t)i, h, (int32_t)raw.size(), 0};
-          for (int64_t b0 = 0; b0 < nt; b0 += tps) {
-            raw.push_back(FwdItem{(int32_t)i, h, (int32_t)b0, (int32_t)std::min(nt, b0 + tps)});
-            cost.push_back(std::min(nt, b0 + tps) - b0 + 1);
-            cls.push_back((int64_t)qtile_seg[i] * Hkv + h);
-            ci.count++;
-          }
-          p.comb_items.push_back(ci);
-        } else if (split) {
-          CombItem ci{(int32_t)i, h, (int32_t)raw.size(), 1};
-          raw.push_back(FwdItem{(int32_t)i, h, 0, (int32_t)nt});
-          cost.push_back(nt + 1);
+        const int64_t step = split ? tps : nt;
+        Merge mg{(int32_t)i, h, (int32_t)raw.size(), 0};
+        for (int64_t b0 = 0; b0 < nt; b0 += step) {
+          const int64_t b1 = std::min(nt, b0 + step);
+          raw.push_back(FwdItem{(int32_t)i, h, (int32_t)b0, (int32_t)b1});
+          cost.push_back(b1 - b0 + 1);
           cls.push_back((int64_t)qtile_seg[i] * Hkv + h);
-          p.comb_items.push_back(ci);
-        } else {
-          raw.push_back(FwdItem{(int32_t)i, h, 0, (int32_t)nt});
-          cost.push_back(nt + 1);
-          cls.push_back((int64_t)qtile_seg[i] * Hkv + h);
+          mg.count++;
         }
+        if (split) merges.push_back(mg);
       }
     }
-    if (split) {
-      // Split items keep their partial-slot index: the launch order is a
-      // permutation stored beside them.
-      p.fwd_items = raw;
-      p.fwd_order = launch_order(cost, cls, xcd);
-    } else {
-      auto ord = launch_order(cost, cls, xcd);
+    const auto ord = launch_order(cost, cls, xcd);
+    if (!split) {
       for (int32_t o : ord) p.fwd_items.push_back(o < 0 ? FwdItem{-1, 0, 0, 0} : raw[o]);
-      p.fwd_order.clear();
+    } else {
+      // split workgroups in launch order; workgroup i runs on XCD i % 8, which
+      // the merge workgroups of the same (query tile, kv head) then share, so
+      // they find the partial results (and the tile's queries) in that L2
+      std::vector<int> xcd_of(raw.size(), 0);
+      for (size_t i = 0; i < ord.size(); ++i) {
+        SplitItem it{};
+        it.kvh = -1;
+        if (ord[i] >= 0) {
+          const FwdItem& r = raw[ord[i]];
+          it.qt = p.qtiles[r.qtile];
+          it.kvh = r.kvh;
+          it.kt_begin = r.kt_begin;
+          it.kt_end = r.kt_end;
+          it.slot = ord[i];
+          xcd_of[ord[i]] = (int)(i % kNumXcd);
+        }
+        p.split_items.push_back(it);
+      }
+      // one merge wave per block of the partials' register-order layout: 32 rows
+      // (one wave of the part) x 16 columns, for the waves that hold real rows
+      const int blocks_per_wave = 2 * (d->head_dim / 32);
+      std::vector<std::vector<MergeItem>> per(kNumXcd);
+      for (const Merge& mg : merges) {
+        const QTile& qt = p.qtiles[mg.qtile];
+        const int waves = (int)ceil_div((int64_t)qt.n_tok * G, 32);
+        for (int blk = 0; blk < waves * blocks_per_wave; ++blk) {
+          MergeItem m{};
+          m.qt = qt;
+          m.kvh = mg.kvh;
+          m.first = mg.first;
+          m.count = mg.count;
+          m.block = blk;
+          per[xcd_of[mg.first]].push_back(m);
+        }
+      }
+      size_t depth = 0;
+      for (auto& v : per) depth = std::max(depth, v.size());
+      MergeItem empty{};
+      empty.kvh = -1;
+      p.merge_items.assign(depth * kNumXcd, empty);
+      for (int x = 0; x < kNumXcd; ++x)
+        for (size_t r = 0; r < per[x].size(); ++r) p.merge_items[r * kNumXcd + x] = per[x][r];
+      while (!p.merge_items.empty() && p.merge_items.back().kvh < 0) p.merge_items.pop_back();
+      p.n_split_slots = (int64_t)raw.size();
     }
     // dQ items: every (query tile, kv head), whole key range, same order policy
     p.dq_items.clear();
@@ -287,8 +321,8 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
         dcost.push_back(tiles_of(p.qtiles[i]) + 1);
         dcls.push_back((int64_t)qtile_seg[i] * Hkv + h);
       }
-    auto ord = launch_order(dcost, dcls, xcd);
-    for (int32_t o : ord) p.dq_items.push_back(o < 0 ? FwdItem{-1, 0, 0, 0} : dq_raw[o]);
+    const auto dord = launch_order(dcost, dcls, xcd);
+    for (int32_t o : dord) p.dq_items.push_back(o < 0 ? FwdItem{-1, 0, 0, 0} : dq_raw[o]);
   }
 
   // ---------------- key tiles (dK / dV) and canvas-query lists
@@ -422,8 +456,8 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   p.blob.assign(kBlobHeaderInts, 0);
   append_records(p.blob, p.qtiles, p.off_qtiles);
   append_records(p.blob, p.fwd_items, p.off_fwd);
-  append_records(p.blob, p.fwd_order, p.off_fwd_order);
-  append_records(p.blob, p.comb_items, p.off_comb);
+  append_records(p.blob, p.split_items, p.off_split);
+  append_records(p.blob, p.merge_items, p.off_merge);
   append_records(p.blob, p.dq_items, p.off_dq);
   append_records(p.blob, p.ktiles, p.off_ktiles);
   append_records(p.blob, p.canvq, p.off_canvq);
@@ -435,10 +469,10 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
     hd[0] = kBlobMagic;
     hd[1] = kBlobVersion;
     const int64_t cnt[kBlobSections] = {
-        (int64_t)p.qtiles.size(), (int64_t)p.fwd_items.size(), (int64_t)p.fwd_order.size(),
-        (int64_t)p.comb_items.size(), (int64_t)p.dq_items.size(), (int64_t)p.ktiles.size(),
+        (int64_t)p.qtiles.size(), (int64_t)p.fwd_items.size(), (int64_t)p.split_items.size(),
+        (int64_t)p.merge_items.size(), (int64_t)p.dq_items.size(), (int64_t)p.ktiles.size(),
         (int64_t)p.canvq.size(), (int64_t)p.bwd_items.size(), (int64_t)p.bwd_merge.size()};
-    const int64_t off[kBlobSections] = {p.off_qtiles, p.off_fwd, p.off_fwd_order, p.off_comb, p.off_dq,
+    const int64_t off[kBlobSections] = {p.off_qtiles, p.off_fwd, p.off_split, p.off_merge, p.off_dq,
                                         p.off_ktiles, p.off_canvq, p.off_bwd, p.off_bmerge};
     static_assert(2 + 2 * kBlobSections <= kBlobHeaderInts, "blob header too small");
     for (int i = 0; i < kBlobSections; ++i) { hd[2 + 2 * i] = (int32_t)cnt[i]; hd[3 + 2 * i] = (int32_t)off[i]; }
@@ -459,8 +493,9 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   if (p.use_vt) off = ceil_div((int64_t)Hkv * D * p.tk_pad * 2, 256) * 256;
   p.off_ws_part = off;
   if (split) {
-    const int64_t nsplit = (int64_t)p.fwd_items.size();
-    p.off_ws_lse = off + nsplit * kQRows * D * 4;
+    // partial O in bf16 (normalized by the part's own row sums), partial LSE fp32
+    const int64_t nsplit = p.n_split_slots;
+    p.off_ws_lse = off + ceil_div(nsplit * kQRows * D * 2, 256) * 256;
     off = p.off_ws_lse + nsplit * kQRows * 4;
   }
   p.ws_fwd = (size_t)off;

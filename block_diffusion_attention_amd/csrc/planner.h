@@ -21,9 +21,10 @@ struct Plan {
 
   std::vector<QTile> qtiles;
   bool split = false;
-  std::vector<FwdItem> fwd_items;    // direct: launch order; split: partial-slot order
-  std::vector<int32_t> fwd_order;    // split only: launch order over fwd_items
-  std::vector<CombItem> comb_items;  // split only
+  std::vector<FwdItem> fwd_items;    // direct path: launch order (empty on the split path)
+  std::vector<SplitItem> split_items;  // split path: launch order
+  std::vector<MergeItem> merge_items;  // split path: launch order
+  int64_t n_split_slots = 0;         // partial slots of the split path
   std::vector<FwdItem> dq_items;     // launch order
   std::vector<KTile> ktiles;
   std::vector<CanvasQ> canvq;
@@ -32,15 +33,15 @@ struct Plan {
   int64_t n_dkv_slots = 0;           // partial dK/dV slots of the split key tiles
 
   std::vector<int32_t> blob;         // device metadata image
-  int64_t off_qtiles = 0, off_fwd = 0, off_fwd_order = 0, off_comb = 0, off_dq = 0,
+  int64_t off_qtiles = 0, off_fwd = 0, off_split = 0, off_merge = 0, off_dq = 0,
           off_ktiles = 0, off_canvq = 0, off_bwd = 0, off_bmerge = 0;   // int32 offsets into blob
   size_t ws_fwd = 0, ws_bwd = 0;
   bool use_vt = false;               // bf16 forward through the transposed V copy (B % 8 == 0)
   bool dkdv_masked = true;           // dK/dV needs per-score row limits (see build_plan)
   int64_t tk_pad = 0;                // row length of the transposed V copy
   int64_t off_ws_vt = 0;             // byte offsets in the forward workspace: V transposed,
-  int64_t off_ws_part = 0;           // partial O,
-  int64_t off_ws_lse = 0;            // partial LSE
+  int64_t off_ws_part = 0;           // partial O (bf16 or fp32, the plan's dtype),
+  int64_t off_ws_lse = 0;            // partial LSE (fp32)
   int64_t off_ws_lse2 = 0;           // byte offset of LSE*log2(e) in the backward workspace
   int64_t off_ws_dkv = 0;            // byte offset of the partial dK/dV slots (fp32)
 };

@@ -210,7 +210,7 @@ int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward);
 
 /* Short name of the i-th kernel (0-based, launch order) that bd_attn_fwd
  * (backward = 0) or bd_attn_bwd (backward = 1) launches for this plan, e.g.
- * "transpose_v", "fwd", "combine", "bwd_pre", "dq", "dkdv", "dkdv_merge"; NULL when i is out of
+ * "transpose_v", "fwd", "merge", "bwd_pre", "dq", "dkdv", "dkdv_merge"; NULL when i is out of
  * range or the plan is NULL. "dkdv_masked" names the bf16 dK/dV kernel that
  * applies a row limit to every score: plans whose query chunks are not all either
  * seen whole by a 32-key group or not at all (block size not a multiple of 32,

@@ -5,13 +5,13 @@ from __future__ import annotations
 import numpy as np
 
 MAGIC = 0x62646174
-SECTIONS = ["qtiles", "fwd", "fwd_order", "comb", "dq", "ktiles", "canvq", "bwd", "bmerge"]
-WIDTH = {"qtiles": 8, "fwd": 4, "fwd_order": 1, "comb": 4, "dq": 4, "ktiles": 8, "canvq": 4, "bwd": 4, "bmerge": 4}
+SECTIONS = ["qtiles", "fwd", "split", "merge", "dq", "ktiles", "canvq", "bwd", "bmerge"]
+WIDTH = {"qtiles": 8, "fwd": 4, "split": 16, "merge": 16, "dq": 4, "ktiles": 8, "canvq": 4, "bwd": 4, "bmerge": 4}
 
 
 def decode(blob):
     b = np.asarray(blob, dtype=np.int64)
-    assert b[0] == MAGIC and b[1] == 2
+    assert b[0] == MAGIC and b[1] == 3
     out = {}
     for i, name in enumerate(SECTIONS):
         cnt, off = int(b[2 + 2 * i]), int(b[3 + 2 * i])

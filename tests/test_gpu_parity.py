@@ -91,7 +91,7 @@ def test_denoise_step_split(seed, flags):
     _say(f"case {wl.name} seed {seed} flags {flags}")
     gpu, plan = run_gpu(wl, flags=flags, backward=False)
     assert ("transpose_v" in plan.kernel_names(False)) == bool(flags & b.FLAG_FWD_VT)
-    assert "combine" in plan.kernel_names(False), "the single-request shape takes the split path"
+    assert "merge" in plan.kernel_names(False), "the single-request shape takes the split path"
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
@@ -182,7 +182,7 @@ def test_denoise_step_no_split_matches_split():
     wl = W.make_config(2, with_do=False)
     g1, _ = run_gpu(wl, backward=False)
     g2, p2 = run_gpu(wl, flags=b.FLAG_NO_SPLIT, backward=False)
-    assert "combine" not in p2.kernel_names(False)
+    assert "merge" not in p2.kernel_names(False)
     st = error_stats(g1["o"], g2["o"])
     assert st["max_abs"] <= 4e-3, st
 
@@ -196,7 +196,7 @@ def test_serving_steps_split_sizes(k, tiles):
     wl = W.make_config(k, with_do=False)
     _say(f"case {wl.name} tiles per split {tiles}")
     gpu, plan = run_gpu(wl, flags=tiles << 8, backward=False)
-    assert "combine" in plan.kernel_names(False)
+    assert "merge" in plan.kernel_names(False)
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
@@ -338,7 +338,7 @@ def test_commit_folded_step(flags):
     wl = W.make_config(6)
     _say(f"case {wl.name} flags {flags}")
     gpu, plan = run_gpu(wl, flags=flags, backward=False)
-    assert ("combine" in plan.kernel_names(False)) == (not flags & b.FLAG_NO_SPLIT)
+    assert ("merge" in plan.kernel_names(False)) == (not flags & b.FLAG_NO_SPLIT)
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
@@ -370,7 +370,7 @@ def test_split_order_with_empty_slots():
     wl = W.random_workload(np.random.default_rng(609), meta, sigma=0.3)
     _say(f"case split order with empty slots tq={meta.tq} tk={meta.tk}")
     gpu, plan = run_gpu(wl, backward=False)
-    assert "combine" in plan.kernel_names(False)
+    assert "merge" in plan.kernel_names(False)
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
@@ -403,7 +403,7 @@ def test_forced_split_matches_oracle(flags):
     meta = W.Meta([1024, 512], [0, 512], [[5, 32, 0], [16]], 32, 8, 2, 128, "bf16")
     wl = W.random_workload(rng, meta, sigma=0.3)
     gpu, plan = run_gpu(wl, flags=b.FLAG_FORCE_SPLIT | flags)
-    assert "combine" in plan.kernel_names(False)
+    assert "merge" in plan.kernel_names(False)
     assert "dkdv_merge" in plan.kernel_names(True), "FORCE_SPLIT also splits the dK/dV key tiles"
     _compare(wl, gpu, run_oracle(wl))
 

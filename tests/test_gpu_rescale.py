@@ -50,7 +50,7 @@ def test_rescale_parity(kind, launch):
     sys.stdout.flush()
     gpu, plan = run_gpu(wl, flags=flags)
     if tps:
-        assert "combine" in plan.kernel_names(False)
+        assert "merge" in plan.kernel_names(False)
     ref = run_oracle(wl)
     for n in ("o", "dq", "dk", "dv"):
         assert_close(f"{wl.name}/{launch}:{n}", gpu[n], ref[n], "bf16")

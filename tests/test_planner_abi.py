@@ -170,21 +170,50 @@ def _check_plan(meta, flags=0):
     assert sorted(whole + merged) == sorted(itertools.product(range(nk), range(hkv)))
     if meta.dtype != "bf16" or flags & b.FLAG_NO_SPLIT:
         assert len(rec["bmerge"]) == 0
-    if len(rec["comb"]) == 0:
+    if len(rec["split"]) == 0:
         fw = [tuple(x[:2]) for x in rec["fwd"] if x[0] >= 0]
         assert sorted(fw) == sorted(dq)
+        assert len(rec["merge"]) == 0
     else:
-        # split: the splits of a (tile, head) cover its key tiles once, in order
-        order = [o for o in rec["fwd_order"] if o >= 0]
-        assert sorted(order) == list(range(len(rec["fwd"])))
-        for qt, h, first, count in rec["comb"]:
-            spans = rec["fwd"][first:first + count]
-            assert (spans[:, 0] == qt).all() and (spans[:, 1] == h).all()
-            assert spans[0, 2] == 0 and (spans[1:, 2] == spans[:-1, 3]).all()
-            t = rec["qtiles"][qt]
-            ntiles = -(-t[4] // 64) + -(-t[7] // 64)
-            assert spans[-1, 3] == ntiles
+        _check_split(rec, meta, G)
     return p, rec
+
+
+def _check_split(rec, meta, G):
+    """Split path: every partial slot is written by exactly one launched part;
+    the parts of a (query tile, kv head) cover its key tiles once, in slot
+    order; each part and merge record carries a copy of its query tile; the merge
+    workgroups of a tile cover its rows and run on the XCD of its first part."""
+    assert len(rec["fwd"]) == 0
+    hkv, D = meta.num_kv_heads, meta.head_dim
+    qt_index = {tuple(int(x) for x in q): i for i, q in enumerate(rec["qtiles"])}
+    sp = rec["split"]
+    live = [(i, r) for i, r in enumerate(sp) if r[8] >= 0]
+    slots = sorted(int(r[11]) for _, r in live)
+    assert slots == list(range(len(live)))
+    by_slot = {int(r[11]): r for _, r in live}
+    launch_pos = {int(r[11]): i for i, r in live}
+    bpw = 2 * (D // 32)          # merge blocks (32 rows x 16 columns) per 32-row wave of a part
+    seen = {}
+    for i, m in enumerate(rec["merge"]):
+        if m[8] < 0:
+            continue
+        qt = qt_index[tuple(int(x) for x in m[:8])]
+        kvh, first, count, blk = (int(x) for x in m[8:12])
+        seen.setdefault((qt, kvh, first, count), []).append(blk)
+        assert i % 8 == launch_pos[first] % 8, "merge workgroup off its parts' XCD"
+    assert sorted((q, h) for q, h, _, _ in seen) == sorted(itertools.product(range(len(rec["qtiles"])), range(hkv)))
+    covered = []
+    for (qt, kvh, first, count), rows in seen.items():
+        t = rec["qtiles"][qt]
+        assert sorted(rows) == list(range(-(-int(t[1]) * G // 32) * bpw))
+        spans = [by_slot[s] for s in range(first, first + count)]
+        assert all(qt_index[tuple(int(x) for x in r[:8])] == qt and r[8] == kvh for r in spans)
+        assert spans[0][9] == 0 and all(a_[10] == b_[9] and a_[10] > a_[9] for a_, b_ in zip(spans, spans[1:]))
+        ntiles = -(-t[4] // 64) + -(-t[7] // 64)
+        assert spans[-1][10] == ntiles
+        covered += range(first, first + count)
+    assert sorted(covered) == slots
 
 
 def test_plan_encodes_oracle_visibility_exhaustive():
@@ -270,17 +299,14 @@ def test_named_workload_plans(k):
     assert p.visible_pairs == orc.visible_pairs(meta)
     rec = decode(p.host_blob())
     if k == 2:
-        assert len(rec["comb"]) == 8, "the denoising-step shape is split along its key range"
-        # 2048 context keys + 32 own keys = 33 key tiles of 64 per kv head, 4 tiles per split
-        launched = sorted(o for o in rec["fwd_order"] if o >= 0)
-        assert launched == list(range(len(rec["fwd"])))
-        assert len(rec["fwd"]) == 8 * 9
-        for qtile, kvh, first, count in rec["comb"]:
-            spans = [tuple(rec["fwd"][first + i][2:4]) for i in range(count)]
-            assert spans[0][0] == 0 and spans[-1][1] == 33
-            assert all(a[1] == b_[0] for a, b_ in zip(spans, spans[1:]))
-            assert all(rec["fwd"][first + i][0] == qtile and rec["fwd"][first + i][1] == kvh
-                       for i in range(count))
+        # 2048 context keys + 32 own keys = 33 key tiles of 64 per kv head, cut
+        # into parts of 2 tiles (264 tiles over 256 compute units): 17 parts per
+        # kv head, merged by 4 x 8 one-wave workgroups (32 rows x 16 columns) each
+        live = rec["split"][rec["split"][:, 8] >= 0]
+        assert len(live) == 8 * 17
+        assert (live[:, 10] - live[:, 9] <= 2).all()
+        assert len(rec["merge"][rec["merge"][:, 8] >= 0]) == 8 * 32
+        _check_split(rec, meta, meta.num_q_heads // meta.num_kv_heads)
 
 
 def test_plan_is_deterministic():
@@ -375,4 +401,4 @@ SPLIT_WITH_EMPTY_SLOTS = Meta(
 
 def test_split_launch_order_has_empty_slots():
     p, rec = _check_plan(SPLIT_WITH_EMPTY_SLOTS)
-    assert len(rec["comb"]) > 0 and (rec["fwd_order"] < 0).any()
+    assert len(rec["merge"]) > 0 and (rec["split"][:, 8] < 0).any()
