@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -269,7 +269,7 @@ def _summarize_sq(rows):
     mfma = {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16"}
     if any(mfma <= set(d) for ds in by_kernel.values() for d in ds):
         out += ["## MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
-                "| kernel | dispatches | mean us | clock GHz | MFMA busy % | executed TFLOP | executed TFLOP/s | % of 2.5 PFLOP/s |",
+                "| kernel | dispatches | mean us | clock GHz | MFMA busy % | executed TFLOP | executed TFLOP/s | % of 2516.6 TFLOP/s |",
                 "|---|---|---|---|---|---|---|---|"]
         for kn, ds in sorted(by_kernel.items()):
             ds = [d for d in ds if mfma <= set(d) and d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] > 0]
@@ -688,6 +688,18 @@ def main():
     useful = (4.0 + (10.0 if backward else 0.0)) * D * Hq * pairs
     value = useful / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if m.dtype == "bf16" else PEAK_FP32_TFLOPS
+    # useful rate of each pass on its own: the forward's 4*D and the backward's
+    # 10*D FLOP per visible (row, key) pair and q head, over the summed average
+    # durations of that pass's kernels
+    fwd_ms = sum(avg_ms[n] for n in fwd_names)
+    passes = {"fwd": {"ms": round(fwd_ms, 4),
+                      "useful_tflops": round(4.0 * D * Hq * pairs / (fwd_ms * 1e-3) / 1e12, 2)}}
+    if backward:
+        bwd_ms = sum(avg_ms[n] for n in bwd_names)
+        passes["bwd"] = {"ms": round(bwd_ms, 4),
+                         "useful_tflops": round(10.0 * D * Hq * pairs / (bwd_ms * 1e-3) / 1e12, 2)}
+    for p_ in passes.values():
+        p_["pct_of_peak"] = round(100.0 * p_["useful_tflops"] / peak, 2)
 
     # algorithmic work per launch of each kernel
     esz = 2 if m.dtype == "bf16" else 4
@@ -710,11 +722,15 @@ def main():
     if bound == "mfma":
         achieved = work / dur_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
+                "frac": round(achieved / peak, 4),
+                # the products the kernel itself executes, which for the two backward
+                # kernels (8*D and 6*D per pair) sum to more than the pass's useful 10*D
+                "work_kind": "executed MFMA FLOPs of this kernel"}
     else:
         achieved = work / dur_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "work_kind": "compulsory bytes of this kernel"}
     roof["kernel"] = dom
     roof["work_per_launch"] = work
     roof["avg_launch_ms"] = round(avg_ms[dom], 4)
@@ -742,6 +758,7 @@ def main():
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "pct_of_peak": round(100.0 * value / peak, 2),
+        "per_pass": passes,
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,

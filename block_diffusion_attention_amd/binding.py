@@ -22,6 +22,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
 FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD, FLAG_FWD_DIRECT, FLAG_FWD_VT = 1, 2, 4, 8, 16
 FLAG_CLEAN_CAUSAL = 32
+FLAG_CHECK_PLAN = 64
 
 
 def flag_split_tiles(n: int) -> int:
@@ -61,6 +62,7 @@ _lib.bd_attn_plan_sizes.argtypes = [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.
                                     ctypes.POINTER(_sz), ctypes.POINTER(_sz), ctypes.POINTER(_sz),
                                     ctypes.POINTER(ctypes.c_int64)]
 _lib.bd_attn_plan_serialize.argtypes = [_vp, _vp, _sz]
+_lib.bd_attn_plan_check.argtypes = [_vp, _vp, _sz]
 _lib.bd_attn_plan_upload.argtypes = [_vp, _vp, _vp]
 _lib.bd_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.bd_attn_bwd.argtypes = [_vp] * 13
@@ -76,7 +78,7 @@ _lib.bd_attn_last_error.restype = ctypes.c_char_p
 _lib.bd_attn_version.restype = ctypes.c_char_p
 for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
            "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_destroy",
-           "bd_attn_fwd_noalloc"):
+           "bd_attn_fwd_noalloc", "bd_attn_plan_check"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -152,7 +154,7 @@ EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_
             "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
             "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version",
             "bd_attn_pack", "bd_aec_workspace", "bd_aec_fwd", "bd_aec_fwd_timed", "bd_aec_kernels",
-            "bd_aec_bwd", "bd_aec_bwd_timed", "bd_attn_fwd_noalloc")
+            "bd_aec_bwd", "bd_aec_bwd_timed", "bd_attn_fwd_noalloc", "bd_attn_plan_check")
 
 # size of the fixed forward workspace of bd_attn_fwd_noalloc (BD_ATTN_NOALLOC_WS_BYTES)
 NOALLOC_WS_BYTES = 32 << 20
@@ -266,6 +268,13 @@ class Plan:
         buf = (ctypes.c_int32 * (self.meta_bytes // 4))()
         _check(_lib.bd_attn_plan_serialize(self.handle, ctypes.cast(buf, _vp), self.meta_bytes))
         return list(buf)
+
+    def check(self, blob=None):
+        """Runs the work-list self-check on blob (a list of int32, by default the
+        plan's own image); raises BdAttnError naming the first bad record."""
+        vals = self.host_blob() if blob is None else list(blob)
+        buf = (ctypes.c_int32 * len(vals))(*vals)
+        _check(_lib.bd_attn_plan_check(self.handle, ctypes.cast(buf, _vp), ctypes.sizeof(buf)))
 
     def upload(self, device="cuda"):
         """Allocates (torch) and fills the device metadata buffer and workspaces."""

@@ -130,6 +130,18 @@ bd_attn_status bd_attn_plan_serialize(bd_attn_plan_t plan, void* meta_host, size
   return BD_ATTN_OK;
 }
 
+bd_attn_status bd_attn_plan_check(bd_attn_plan_t plan, const void* meta_host, size_t bytes) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  if (!meta_host) return fail(BD_ATTN_EINVAL, "meta_host is NULL");
+  const size_t need = plan->p.blob.size() * sizeof(int32_t);
+  if (bytes < need) return fail(BD_ATTN_EWORKSPACE, "meta_host buffer smaller than meta_bytes");
+  std::string why;
+  if (bdattn::check_blob(plan->p, static_cast<const int32_t*>(meta_host), need / sizeof(int32_t), &why) !=
+      BD_ATTN_OK)
+    return fail(BD_ATTN_EINVAL, why);
+  return BD_ATTN_OK;
+}
+
 bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_stream_t stream) {
   if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
   if (bd_attn_status st = check_ptr(meta_dev, "meta_dev")) return st;

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <numeric>
 #include <string>
@@ -514,6 +515,138 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   p.off_ws_lse2 = ceil_div(tq * Hq * 4, 256) * 256;          // delta [Tq, Hq] fp32, then LSE*log2(e)
   p.off_ws_dkv = 2 * p.off_ws_lse2;                          // then the partial dK/dV slots
   p.ws_bwd = (size_t)(p.off_ws_dkv + p.n_dkv_slots * 2 * kKBlock * D * 4);
+  if (d->flags & BD_ATTN_FLAG_CHECK_PLAN) {
+    std::string why;
+    if (check_blob(p, p.blob.data(), p.blob.size(), &why) != BD_ATTN_OK) {
+      *err = "plan self-check failed: " + why;
+      return BD_ATTN_EINVAL;
+    }
+  }
+  return BD_ATTN_OK;
+}
+
+namespace {
+
+// Bounds of one query tile as the forward / dQ kernels read it: its rows, its
+// clean key range and its own canvas keys all inside the packed tensors.
+bool qtile_ok(const Plan& p, const QTile& t, std::string* why) {
+  const int64_t rows = (int64_t)t.n_tok * p.G;
+  if (t.q_tok < 0 || t.n_tok < 1 || rows > kQRows || (int64_t)t.q_tok + t.n_tok > p.tq) {
+    *why = "query rows outside [0, Tq) or more than a tile";
+    return false;
+  }
+  if (t.lim_min < 0 || t.lim_min > t.lim_max || t.k_ctx < 0 || (int64_t)t.k_ctx + t.lim_max > p.tk) {
+    *why = "clean key range outside [0, Tk)";
+    return false;
+  }
+  if (t.n_own < 0 || (t.n_own > 0 && (t.k_own < 0 || (int64_t)t.k_own + t.n_own > p.tk))) {
+    *why = "own canvas keys outside [0, Tk)";
+    return false;
+  }
+  return true;
+}
+
+// Key tiles a query tile's list holds: its clean range, then its own keys.
+int64_t qtile_key_tiles(const QTile& t) { return ceil_div(t.lim_max, kKTile) + ceil_div(t.n_own, kKTile); }
+
+bool key_range_ok(const QTile& t, int32_t b, int32_t e) {
+  return b >= 0 && b <= e && e <= qtile_key_tiles(t);
+}
+
+}  // namespace
+
+bd_attn_status check_blob(const Plan& p, const int32_t* blob, size_t n_ints, std::string* why) {
+  const int Hkv = p.desc.num_kv_heads;
+  char buf[160];
+  auto bad = [&](const char* sec, int64_t i, const std::string& what) {
+    std::snprintf(buf, sizeof buf, "%s record %lld: ", sec, (long long)i);
+    *why = buf + what;
+    return BD_ATTN_EINVAL;
+  };
+  if (!blob || n_ints < (size_t)kBlobHeaderInts) { *why = "blob shorter than its header"; return BD_ATTN_EINVAL; }
+  if (blob[0] != kBlobMagic || blob[1] != kBlobVersion) { *why = "bad blob magic or version"; return BD_ATTN_EINVAL; }
+  static const char* names[kBlobSections] = {"qtiles", "fwd", "split", "merge", "dq",
+                                             "ktiles", "canvq", "bwd", "bmerge"};
+  static const int width[kBlobSections] = {8, 4, 16, 16, 4, 8, 4, 4, 4};
+  const int64_t expect[kBlobSections] = {
+      (int64_t)p.qtiles.size(), (int64_t)p.fwd_items.size(), (int64_t)p.split_items.size(),
+      (int64_t)p.merge_items.size(), (int64_t)p.dq_items.size(), (int64_t)p.ktiles.size(),
+      (int64_t)p.canvq.size(), (int64_t)p.bwd_items.size(), (int64_t)p.bwd_merge.size()};
+  const int32_t* sec[kBlobSections];
+  for (int i = 0; i < kBlobSections; ++i) {
+    const int64_t cnt = blob[2 + 2 * i], off = blob[3 + 2 * i];
+    if (cnt != expect[i]) return bad(names[i], -1, "record count differs from the plan's");
+    if (off < kBlobHeaderInts || off % 4 || off + cnt * width[i] > (int64_t)n_ints)
+      return bad(names[i], -1, "section outside the blob or misaligned");
+    sec[i] = blob + off;
+  }
+  const int64_t nq = expect[0], nkt = expect[5], ncv = expect[6];
+  const QTile* qt = reinterpret_cast<const QTile*>(sec[0]);
+  std::string w;
+  for (int64_t i = 0; i < nq; ++i)
+    if (!qtile_ok(p, qt[i], &w)) return bad("qtiles", i, w);
+  for (int s = 1; s <= 4; s += 3) {   // fwd, dq: FwdItem lists
+    const FwdItem* it = reinterpret_cast<const FwdItem*>(sec[s]);
+    for (int64_t i = 0; i < expect[s]; ++i) {
+      if (it[i].qtile < 0) continue;   // empty launch slot
+      if (it[i].qtile >= nq) return bad(names[s], i, "query tile index outside its section");
+      if (it[i].kvh < 0 || it[i].kvh >= Hkv) return bad(names[s], i, "kv head out of range");
+      if (!key_range_ok(qt[it[i].qtile], it[i].kt_begin, it[i].kt_end))
+        return bad(names[s], i, "key tile range outside the query tile's list");
+    }
+  }
+  {
+    const SplitItem* it = reinterpret_cast<const SplitItem*>(sec[2]);
+    for (int64_t i = 0; i < expect[2]; ++i) {
+      if (it[i].kvh < 0) continue;
+      if (it[i].kvh >= Hkv) return bad("split", i, "kv head out of range");
+      if (!qtile_ok(p, it[i].qt, &w)) return bad("split", i, w);
+      if (!key_range_ok(it[i].qt, it[i].kt_begin, it[i].kt_end))
+        return bad("split", i, "key tile range outside the query tile's list");
+      if (it[i].slot < 0 || it[i].slot >= p.n_split_slots) return bad("split", i, "partial slot out of range");
+    }
+    const MergeItem* mt = reinterpret_cast<const MergeItem*>(sec[3]);
+    const int blocks = 4 * (p.desc.head_dim / 32) * 2;
+    for (int64_t i = 0; i < expect[3]; ++i) {
+      if (mt[i].kvh < 0) continue;
+      if (mt[i].kvh >= Hkv) return bad("merge", i, "kv head out of range");
+      if (!qtile_ok(p, mt[i].qt, &w)) return bad("merge", i, w);
+      if (mt[i].first < 0 || mt[i].count < 1 || (int64_t)mt[i].first + mt[i].count > p.n_split_slots)
+        return bad("merge", i, "partial slots out of range");
+      if (mt[i].block < 0 || mt[i].block >= blocks) return bad("merge", i, "partial block out of range");
+    }
+  }
+  const KTile* kt = reinterpret_cast<const KTile*>(sec[5]);
+  for (int64_t i = 0; i < nkt; ++i) {
+    const KTile& t = kt[i];
+    if (t.k_tok < 0 || t.n_keys < 1 || t.n_keys > kKBlock || (int64_t)t.k_tok + t.n_keys > p.tk)
+      return bad("ktiles", i, "keys outside [0, Tk) or more than a tile");
+    if (t.cq_len < 0 || (t.cq_len > 0 && (t.cq_tok < 0 || (int64_t)t.cq_tok + t.cq_len > p.tq)))
+      return bad("ktiles", i, "clean query range outside [0, Tq)");
+    if (t.cv_begin < 0 || t.cv_count < 0 || (int64_t)t.cv_begin + t.cv_count > ncv)
+      return bad("ktiles", i, "canvas-query entries outside their section");
+  }
+  const CanvasQ* cv = reinterpret_cast<const CanvasQ*>(sec[6]);
+  for (int64_t i = 0; i < ncv; ++i)
+    if (cv[i].q_tok < 0 || cv[i].n_tok < 1 || (int64_t)cv[i].q_tok + cv[i].n_tok > p.tq ||
+        cv[i].lim < 0 || (cv[i].own != 0 && cv[i].own != 1))
+      return bad("canvq", i, "canvas query rows outside [0, Tq) or bad limit");
+  const BwdItem* bt = reinterpret_cast<const BwdItem*>(sec[7]);
+  for (int64_t i = 0; i < expect[7]; ++i) {
+    if (bt[i].ktile < 0) continue;
+    if (bt[i].ktile >= nkt) return bad("bwd", i, "key tile index outside its section");
+    if (bt[i].kvh_slot < 0) return bad("bwd", i, "negative kv head / slot");
+    const int64_t slot = bt[i].kvh_slot / Hkv - 1;
+    if (slot >= p.n_dkv_slots) return bad("bwd", i, "partial dK/dV slot out of range");
+    if (bt[i].c_begin < 0 || bt[i].c_begin > bt[i].c_end) return bad("bwd", i, "bad chunk range");
+  }
+  const BwdMerge* bm = reinterpret_cast<const BwdMerge*>(sec[8]);
+  for (int64_t i = 0; i < expect[8]; ++i) {
+    if (bm[i].ktile < 0 || bm[i].ktile >= nkt) return bad("bmerge", i, "key tile index outside its section");
+    if (bm[i].kvh < 0 || bm[i].kvh >= Hkv) return bad("bmerge", i, "kv head out of range");
+    if (bm[i].first < 0 || bm[i].count < 1 || (int64_t)bm[i].first + bm[i].count > p.n_dkv_slots)
+      return bad("bmerge", i, "partial dK/dV slots out of range");
+  }
   return BD_ATTN_OK;
 }
 

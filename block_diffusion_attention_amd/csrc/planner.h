@@ -49,6 +49,13 @@ struct Plan {
 // Validates desc and fills *plan. On error returns a non-OK status and sets *err.
 bd_attn_status build_plan(const bd_attn_desc* desc, Plan* plan, std::string* err);
 
+// Checks a serialized work-list image against the plan it claims to belong to:
+// header, section counts and bounds, and that every index a kernel follows
+// (query / key tile, canvas-query entry, kv head, key tile range, partial slot)
+// and every token range lies inside its section or tensor. EINVAL + *why on the
+// first violation.
+bd_attn_status check_blob(const Plan& plan, const int32_t* blob, size_t n_ints, std::string* why);
+
 }  // namespace bdattn
 
 struct bd_attn_plan_s {

@@ -94,6 +94,9 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
                                          (position <= own) instead of block-causally */
 /* Bits 8..15: key tiles (of 64 keys) per split of the forward split path;
  * 0 selects the library's choice. Ignored unless the plan splits. */
+#define BD_ATTN_FLAG_CHECK_PLAN  64u /* bd_attn_plan runs bd_attn_plan_check on its own
+                                       work lists before returning (EINVAL if they
+                                       break an invariant; a debugging aid) */
 #define BD_ATTN_FLAG_SPLIT_TILES(n) ((((uint32_t)(n)) & 0xffu) << 8)
 
 typedef struct bd_attn_plan_s* bd_attn_plan_t;
@@ -136,6 +139,17 @@ bd_attn_status bd_attn_plan_sizes(bd_attn_plan_t plan, int64_t* tq, int64_t* tk,
 /* Copies the plan's host work lists into meta_host (meta_bytes bytes, host
  * memory owned by the caller), e.g. to stage them into pinned memory. */
 bd_attn_status bd_attn_plan_serialize(bd_attn_plan_t plan, void* meta_host, size_t bytes);
+
+/* Checks a work-list image (meta_bytes bytes of host memory laid out as
+ * bd_attn_plan_serialize writes it) against plan: the header and the section
+ * counts match the plan, every section lies inside the image, and every index a
+ * kernel follows lies inside its list or tensor (query / key tile indices,
+ * canvas-query entries, kv heads, key tile ranges of a query tile, partial
+ * slots, query and key token ranges inside [0, Tq) / [0, Tk)). For debugging a
+ * planner change or an image that was edited or copied by hand: the kernels do
+ * not re-check these bounds. Errors: EINVAL naming the first bad section and
+ * record (bd_attn_last_error), EWORKSPACE if bytes is smaller than meta_bytes. */
+bd_attn_status bd_attn_plan_check(bd_attn_plan_t plan, const void* meta_host, size_t bytes);
 
 /* Enqueues an asynchronous copy of the work lists into meta_dev (device memory
  * of at least meta_bytes bytes, 16-byte aligned) on stream. The source is the

@@ -402,3 +402,86 @@ SPLIT_WITH_EMPTY_SLOTS = Meta(
 def test_split_launch_order_has_empty_slots():
     p, rec = _check_plan(SPLIT_WITH_EMPTY_SLOTS)
     assert len(rec["merge"]) > 0 and (rec["split"][:, 8] < 0).any()
+
+
+# ---------------------------------------------------------------- work-list self-check
+
+def _sections(blob):
+    return {name: (blob[2 + 2 * i], blob[3 + 2 * i]) for i, name in enumerate(
+        ["qtiles", "fwd", "split", "merge", "dq", "ktiles", "canvq", "bwd", "bmerge"])}
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 6])
+@pytest.mark.parametrize("flags", [0, b.FLAG_NO_XCD, b.FLAG_FORCE_SPLIT, b.FLAG_NO_SPLIT])
+def test_plan_self_check_accepts_every_plan(k, flags):
+    meta = config_meta(k, np.random.default_rng(k))
+    p = b.Plan(meta, flags | b.FLAG_CHECK_PLAN)   # bd_attn_plan runs the check itself
+    p.check()
+    assert b.Plan(meta, flags).host_blob() == p.host_blob()   # the flag changes nothing else
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_self_check_accepts_random_plans(seed):
+    rng = np.random.default_rng(seed)
+    meta = random_meta(rng, hq=4, hkv=2, d=64, max_segments=4, max_blocks=8,
+                       block_sizes=(1, 2, 4, 8, 16, 32, 48), max_canvases=4, dtype="bf16",
+                       offsets=seed % 2 == 1, clean_causal=seed % 3 == 2)
+    for flags in (0, b.FLAG_FORCE_SPLIT):
+        b.Plan(meta, flags | b.FLAG_CHECK_PLAN).check()
+
+
+# (section, record, field, value as a function of the plan's section sizes, expected message)
+CORRUPTIONS = [
+    ("dq", 0, 0, lambda n: n["qtiles"], "query tile index"),
+    ("dq", 0, 1, lambda n: 8, "kv head"),
+    ("dq", 0, 3, lambda n: 10 ** 6, "key tile range"),
+    ("split", 0, 11, lambda n: 10 ** 6, "partial slot"),
+    ("split", 0, 1, lambda n: 10 ** 6, "query rows"),
+    ("merge", 0, 10, lambda n: 10 ** 6, "partial slots"),
+    ("ktiles", 0, 7, lambda n: n["canvq"] + 1, "canvas-query entries"),
+    ("ktiles", 0, 1, lambda n: 129, "keys outside"),
+    ("canvq", 0, 0, lambda n: -1, "canvas query rows"),
+    ("bwd", 0, 0, lambda n: n["ktiles"], "key tile index"),
+    ("qtiles", 0, 4, lambda n: 10 ** 7, "clean key range"),
+]
+
+
+@pytest.mark.parametrize("sec,rec,field,val,needle", CORRUPTIONS)
+def test_plan_check_rejects_bad_records(sec, rec, field, val, needle):
+    # the single-request serving workload uses every forward record kind (split
+    # parts and merge blocks) as well as the backward lists
+    meta = config_meta(2, np.random.default_rng(2))
+    p = b.Plan(meta)
+    blob = p.host_blob()
+    secs = _sections(blob)
+    counts = {n: c for n, (c, _) in secs.items()}
+    width = {"qtiles": 8, "fwd": 4, "split": 16, "merge": 16, "dq": 4, "ktiles": 8, "canvq": 4, "bwd": 4,
+             "bmerge": 4}[sec]
+    cnt, off = secs[sec]
+    assert cnt > rec
+    # first live record of the launch lists (empty slots carry -1 and are skipped)
+    live_field = {"dq": 0, "bwd": 0, "split": 8, "merge": 8}.get(sec)
+    if live_field is not None:
+        while blob[off + rec * width + live_field] < 0:
+            rec += 1
+    blob[off + rec * width + field] = val(counts)
+    with pytest.raises(b.BdAttnError, match=needle) as e:
+        p.check(blob)
+    assert f"{sec} record {rec}" in str(e.value)
+
+
+def test_plan_check_rejects_bad_header_and_size():
+    p = b.Plan(config_meta(4, np.random.default_rng(4)))
+    blob = p.host_blob()
+    bad = list(blob)
+    bad[2] += 1                       # query tile count
+    with pytest.raises(b.BdAttnError, match="record count"):
+        p.check(bad)
+    bad = list(blob)
+    bad[1] = 99                       # version
+    with pytest.raises(b.BdAttnError, match="magic or version"):
+        p.check(bad)
+    with pytest.raises(b.BdAttnError) as e:
+        p.check(blob[:-4])
+    assert e.value.status == 3        # BD_ATTN_EWORKSPACE
+    p.check(blob)
