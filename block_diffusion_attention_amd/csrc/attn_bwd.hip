@@ -1,9 +1,10 @@
 // Backward staircase block-diffusion attention for gfx950 (bf16 in, fp32 accumulate).
 //
-// Deterministic kernels, no atomics (ORL paper, appendix D.2 paragraph on the
-// kernel: the backward pass uses the same visibility, dQ follows the query
-// traversal and dK/dV derive the valid query ranges of each key tile), in
-// launch order:
+// Deterministic kernels, no atomics (ORL paper, appendix D.2, the paragraph on
+// the kernel). The gradients use exactly the forward's visibility: dQ walks each
+// query tile's key ranges as the forward does, and dK/dV walks, for each key
+// tile, the query ranges that can see it, computed by the planner. In launch
+// order:
 //   dq         : one workgroup per (query tile, kv head), looping over the same
 //                key tiles as the forward pass; it also writes the row terms
 //                delta = rowsum(dO * O) and LSE * log2(e) of its rows;

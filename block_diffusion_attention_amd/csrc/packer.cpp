@@ -1,14 +1,18 @@
 // Host packer: builds replay rows from captured denoising states and assigns
 // them to data-parallel groups, largest estimated cost first.
 //
-// ORL paper, section 3.2 "Packed and cost-balanced state training" and appendix
-// D.3: a row holds one response's clean tokens once, together with the states of
-// its blocks at the same denoising step k (the slicing of TraceRL), so every state
-// reuses the clean context before it; rows of different responses are packed as
-// mutually invisible documents; a weighted proxy of sequence tokens, supervised
-// positions and resident pages drives a deterministic largest-cost-first
-// assignment to data-parallel groups. Each state (and so each of its labels) has
-// exactly one owning row. Pure C++17, no HIP calls.
+// Follows the ORL paper, section 3.2 "Packed and cost-balanced state training"
+// and appendix D.3. What this file does: for every (response, step) pair it emits
+// one row that stores the response's clean tokens a single time and appends, as
+// canvases at their block indices, the captured states of that step; the canvases
+// then attend to the shared clean prefix instead of carrying copies of it. Rows of
+// different responses become separate documents of one packed sequence (no
+// attention across them). Each row gets a cost estimate, a weighted sum of its
+// token count, its supervised positions and its KV pages, and rows are handed to
+// the data-parallel groups in decreasing cost order, each to the group with the
+// least cost so far (ties broken by index, so the result is deterministic). Every
+// state, and every label it carries, lands in exactly one row. Pure C++17, no HIP
+// calls.
 #include "packer.h"
 
 #include <algorithm>

@@ -121,12 +121,15 @@ def key_roles(meta):
 def visible(qr, kr, block_size, block_offset=0, clean_causal=False):
     """Block-diffusion visibility of key role ``kr`` from query role ``qr``.
 
-    ORL section 3.2 "Staircase attention kernel" / appendix D.2: a noisy block
-    (canvas) sees the prompt and the clean blocks before it and itself, never
-    its own clean copy, later blocks, other noisy blocks or other documents;
-    clean queries never see noisy keys. ``block_offset`` is the offset o of the
-    query's segment (context position p lies in block (p + o) // B);
-    ``clean_causal`` selects token-causal clean rows.
+    ORL section 3.2 "Staircase attention kernel" / appendix D.2. A canvas
+    query at block b attends to clean keys of its document whose block index is
+    below b, and to every token of its own canvas; nothing else (not the clean
+    copy of block b, not later clean blocks, not other canvases, not other
+    documents). A clean query attends to clean keys only, up to the end of its
+    own block (or up to itself under the token-causal rule).
+    ``block_offset`` is the offset o of the query's segment (context position p
+    lies in block (p + o) // B); ``clean_causal`` selects token-causal clean
+    rows.
     """
     qs, q_canvas, qpos, qc, qb = qr
     ks, k_canvas, kpos, kc, _kb = kr

@@ -6,11 +6,12 @@ nothing from the library.
 
 What is computed (ORL paper, section 3.2 "Packed and cost-balanced state
 training" and appendix D.3):
-  * a row holds one response's clean tokens once together with the states of
-    its blocks captured at the same denoising step k (the slicing of TraceRL);
-    every state is a canvas at its block index and reuses the clean context
-    before it;
-  * rows of different responses are packed as mutually invisible documents;
+  * one row per (response, step): the response's clean tokens stored a single
+    time, followed by that step's captured block states, each placed as a
+    canvas at its own block index so that it attends to the clean prefix in
+    the row rather than to a private copy;
+  * rows of different responses sit side by side as separate documents with no
+    attention between them;
   * a weighted proxy of sequence tokens, supervised positions and resident pages
     is each row's estimated cost, and rows go to data-parallel groups largest
     cost first, deterministically;
