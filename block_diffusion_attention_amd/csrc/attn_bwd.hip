@@ -536,6 +536,8 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
       else opq[i + kDqAhead - NSD] = fetch_q(i + kDqAhead - NSD);
       __builtin_amdgcn_sched_barrier(0);
     });
+    // dS at raised wave priority, as the forward's softmax
+    __builtin_amdgcn_s_setprio(1);
     // the next tile's copies go out after the S and dP products (as in the forward)
     if (kt + 1 < kt_end) issue(kt + 1, nK, nV);
     if (need_mask) {
@@ -562,6 +564,7 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
     }
     // dQ^T += K^T dS^T: product i = kq NDB + db, reads kDqAhead products ahead
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     static_for<NQ>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       acc[i % NDB] = mfma32(opq[i], sb[i / NDB], acc[i % NDB]);

@@ -124,6 +124,11 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
     // the next tile's copies go out after the S products, so their LDS writes do
     // not compete with this tile's K operand reads (the other stage is free since
     // the barrier; a split part's second tile is already on its way)
+    // The softmax runs at raised wave priority: of the two waves that share a
+    // SIMD, the one in its vector-ALU phase issues first, and the other one's
+    // products fill the matrix unit meanwhile (measured 1-2 % faster than equal
+    // priorities).
+    __builtin_amdgcn_s_setprio(1);
     if (kt + 1 < kt_end && (!SPLIT || kt + 1 > kt_begin + 1)) issue(kt + 1, nK, nV);
 
     // masking only on tiles that cross a row limit or the end of a range
@@ -174,6 +179,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
     // O^T += V^T P^T, V^T read transposed out of the natural V tile; product
     // i = kq NDB + db, so consecutive products accumulate into different blocks
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     static_for<NPV>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       acc[i % NDB] = mfma32(opv[i], pb[i / NDB], acc[i % NDB]);
