@@ -486,9 +486,13 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   // call) is taken only on request: with swizzled row-major K/V tiles, the direct
   // kernel's transposing LDS reads of V measured faster than the copy plus its
   // launch on every workload here.
-  p.use_vt = !(d->flags & BD_ATTN_FLAG_FWD_DIRECT) && (d->flags & BD_ATTN_FLAG_FWD_VT) &&
-             d->dtype == BD_ATTN_BF16 && B % 8 == 0;
+  // Its V^T tiles are read with 32-bit byte offsets within a kv head's rows of
+  // tk_pad keys (up to D - 1 rows from a tile's start), so very long key streams
+  // take the direct kernel.
   p.tk_pad = ceil_div(tk, 64) * 64 + 64;
+  p.use_vt = !(d->flags & BD_ATTN_FLAG_FWD_DIRECT) && (d->flags & BD_ATTN_FLAG_FWD_VT) &&
+             d->dtype == BD_ATTN_BF16 && B % 8 == 0 &&
+             (int64_t)d->head_dim * p.tk_pad * 2 < ((int64_t)1 << 31);
   int64_t off = 0;
   p.off_ws_vt = 0;
   if (p.use_vt) off = ceil_div((int64_t)Hkv * D * p.tk_pad * 2, 256) * 256;

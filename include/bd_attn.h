@@ -88,7 +88,10 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
 #define BD_ATTN_FLAG_FWD_DIRECT 8u /* bf16 forward without the transposed V copy (the
                                        default; kept for callers that set it) */
 #define BD_ATTN_FLAG_FWD_VT     16u /* bf16 forward through a transposed copy of V (a
-                                       pre-pass) when the block size is a multiple of 8;
+                                       pre-pass) when the block size is a multiple of 8
+                                       and the packed key stream holds fewer than about
+                                       2^30 / head_dim keys (8M at head_dim 128; longer
+                                       streams take the direct kernel);
                                        FWD_DIRECT wins if both are set */
 #define BD_ATTN_FLAG_CLEAN_CAUSAL 32u /* clean queries see clean keys token-causally
                                          (position <= own) instead of block-causally */

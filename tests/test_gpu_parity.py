@@ -506,3 +506,59 @@ def test_binding_rejects_mismatched_buffers():
         b.fwd(plan, q, k, v, o=torch.empty((q.shape[0], q.shape[1] + 1, q.shape[2]), dtype=q.dtype, device="cuda"))
     with pytest.raises(ValueError, match="lse"):
         b.fwd(plan, q, k, v, lse=torch.empty((q.shape[0], q.shape[1]), dtype=torch.bfloat16, device="cuda"))
+
+
+# ------------------------------------------------ tensors past 4 GiB (64-bit addressing)
+
+def test_tensors_beyond_4gib():
+    # 520 segments of a 4096-token context and one canvas at its end: Tk = 2,146,560
+    # keys, so K and V hold 4.4 GB each (the last segments' rows lie past byte 2^32)
+    # and Q, O, dO, dQ 17.6 GB each. Inputs are drawn on the GPU (seeded); the
+    # oracle gets the same bf16 values of the first and last segment, for two kv heads.
+    S, B, Hq, Hkv, D = 520, 32, 32, 8, 128
+    meta = W.Meta([4096] * S, [0] * S, [[128]] * S, B, Hq, Hkv, D, "bf16")
+    free, _ = torch.cuda.mem_get_info()
+    if free < 120 * 2**30:
+        pytest.skip(f"needs ~100 GiB of free device memory ({free / 2**30:.0f} GiB free)")
+    plan = b.Plan(meta).upload("cuda")
+    tq, tk = plan.tq, plan.tk
+    assert tk * Hkv * D * 2 > 2**32
+    _say(f"case beyond-4GiB: {S} segments, tq={tq} tk={tk}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+
+    def draw(rows, heads, sigma):
+        t = torch.empty((rows, heads, D), dtype=torch.bfloat16, device="cuda")
+        step = 1 << 18
+        for r0 in range(0, rows, step):
+            r1 = min(rows, r0 + step)
+            t[r0:r1] = (torch.randn((r1 - r0, heads, D), generator=gen, device="cuda") * sigma).to(torch.bfloat16)
+        return t
+
+    q, k, v = draw(tq, Hq, D ** -0.5), draw(tk, Hkv, D ** -0.5), draw(tk, Hkv, D ** -0.5)
+    do = draw(tq, Hq, 1.0)
+    nan = float("nan")
+    o = torch.full_like(q, nan)
+    lse = torch.full((tq, Hq), nan, dtype=torch.float32, device="cuda")
+    o, lse = b.fwd(plan, q, k, v, o, lse)
+    dq, dk, dv = torch.full_like(q, nan), torch.full_like(k, nan), torch.full_like(v, nan)
+    dq, dk, dv = b.bwd(plan, q, k, v, o, lse, do, dq, dk, dv)
+    torch.cuda.synchronize()
+    qo, ko = meta.q_offsets(), meta.k_offsets()
+    G = Hq // Hkv
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    for s in (0, S - 1):
+        for g in (0, Hkv - 1):
+            qs, ks, hs = slice(qo[s], qo[s + 1]), slice(ko[s], ko[s + 1]), slice(g * G, (g + 1) * G)
+            sub_meta = W.Meta([4096], [0], [[128]], B, G, 1, D, "bf16")
+            f32 = lambda t: t.float().cpu().numpy()
+            sub = W.Workload(f"beyond4gib[seg{s},kv{g}]", sub_meta, f32(q[qs, hs]), f32(k[ks, g:g + 1]),
+                             f32(v[ks, g:g + 1]), f32(do[qs, hs]), "fwd+bwd")
+            gs = {"o": f64(o[qs, hs]), "lse": lse[qs, hs].cpu().numpy().astype(np.float64),
+                  "dq": f64(dq[qs, hs]), "dk": f64(dk[ks, g:g + 1]), "dv": f64(dv[ks, g:g + 1])}
+            _compare(sub, gs, run_oracle(sub))
+            _say(f"  segment {s} kv head {g} ok (K rows from byte {ko[s] * Hkv * D * 2})")
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t).all()
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()

@@ -485,3 +485,13 @@ def test_plan_check_rejects_bad_header_and_size():
         p.check(blob[:-4])
     assert e.value.status == 3        # BD_ATTN_EWORKSPACE
     p.check(blob)
+
+
+def test_transposed_v_copy_only_below_its_offset_range():
+    # the transposed-V kernel addresses V^T rows with 32-bit byte offsets: a key
+    # stream past 2^30 / head_dim keys falls back to the direct kernel
+    small = Meta([4096], [0], [[1]], 32, 4, 1, 128, "bf16")
+    assert "transpose_v" in b.Plan(small, b.FLAG_FWD_VT).kernel_names(False)
+    n = (1 << 30) // 128                         # keys at which D * tk_pad * 2 reaches 2^31
+    big = Meta([n], [n], [[n // 32]], 32, 4, 1, 128, "bf16")   # canvas-only: few query tiles
+    assert "transpose_v" not in b.Plan(big, b.FLAG_FWD_VT).kernel_names(False)
