@@ -562,3 +562,69 @@ def test_tensors_beyond_4gib():
         assert torch.isfinite(t).all()
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------ canaries around outputs and workspaces
+
+def _canaried(n, dtype, fill):
+    """A view of n elements in the middle of a larger buffer whose guard regions
+    (64 KiB on each side, a multiple of 256 bytes) hold a fill pattern; returns
+    (view, check) where check() asserts that the guards still hold the pattern."""
+    guard = (64 << 10) // torch.tensor([], dtype=dtype).element_size()
+    big = torch.full((n + 2 * guard,), fill, dtype=dtype, device="cuda")
+    ref = big[:guard].clone()
+    view = big[guard:guard + n]
+
+    def check(name):
+        for side, part in (("before", big[:guard]), ("after", big[guard + n:])):
+            assert torch.equal(part, ref), f"{name}: write {side} the buffer"
+    return view, check
+
+
+CANARY_CASES = [
+    ("packed replay", lambda: W.make_config(3), 0),
+    ("staircase, split dK/dV", lambda: W.make_config(4), 0),
+    ("denoising step, split forward", lambda: W.make_config(2), 0),
+    ("commit-folded step, transposed V", lambda: W.make_config(6), b.FLAG_FWD_VT),
+    ("ragged: B=3, G=3, D=64", lambda: W.random_workload(np.random.default_rng(91), W.random_meta(
+        np.random.default_rng(90), max_segments=3, max_blocks=12, block_sizes=(3,), max_canvases=4,
+        hq=6, hkv=2, d=64, dtype="bf16"), sigma=0.5), b.FLAG_FORCE_SPLIT),
+    ("fp32", lambda: W.make_config(1), 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CANARY_CASES)))
+def test_writes_stay_inside_outputs_and_workspaces(case):
+    name, make, flags = CANARY_CASES[case]
+    wl = make()
+    _say(f"case canaries: {name}")
+    plan = b.Plan(wl.meta, flags).upload("cuda")
+    dt = plan.dtype
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dt) for x in (wl.q, wl.k, wl.v))
+    checks = []
+    # workspaces: byte buffers with a 0xA5 pattern around them
+    if plan.ws_fwd is not None:
+        plan.ws_fwd, c = _canaried(plan.ws_fwd.numel(), torch.uint8, 0xA5)
+        checks.append(("forward workspace", c))
+    plan.ws_bwd, c = _canaried(plan.ws_bwd.numel(), torch.uint8, 0xA5)
+    checks.append(("backward workspace", c))
+    sentinel = -12352.0                       # exact in bf16 and fp32
+
+    def out(shape, dtype, label):
+        n = int(np.prod(shape))
+        t, c = _canaried(n, dtype, sentinel)
+        checks.append((label, c))
+        return t.view(shape)
+
+    qs, ks = tuple(q.shape), tuple(k.shape)
+    o = out(qs, dt, "o")
+    lse = out((plan.tq, wl.meta.num_q_heads), torch.float32, "lse")
+    o, lse = b.fwd(plan, q, k, v, o, lse)
+    do = torch.from_numpy(np.ascontiguousarray(wl.do)).to("cuda").to(dt) if wl.do is not None else torch.ones_like(q)
+    dq, dk, dv = out(qs, dt, "dq"), out(ks, dt, "dk"), out(ks, dt, "dv")
+    dq, dk, dv = b.bwd(plan, q, k, v, o, lse, do, dq, dk, dv)
+    torch.cuda.synchronize()
+    for label, c in checks:
+        c(label)
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t).all() and not (t == sentinel).any()
