@@ -15,8 +15,10 @@ import torch  # loaded first so the library binds to the HIP runtime torch alrea
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # BDATTN_LIBRARY selects another build of the same library (the host-sanitized
-# copy that build.py --sanitize writes); by default the in-tree libbdattn.so
+# copy that build.py --sanitize writes, or the device-checked one that build.py
+# --device-checks writes); by default the in-tree libbdattn.so
 LIB_PATH = os.environ.get("BDATTN_LIBRARY") or os.path.join(_HERE, "libbdattn.so")
+CHECKED_LIB_PATH = os.path.join(_HERE, "libbdattn_checked.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
@@ -63,6 +65,7 @@ _lib.bd_attn_plan_sizes.argtypes = [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.
                                     ctypes.POINTER(ctypes.c_int64)]
 _lib.bd_attn_plan_serialize.argtypes = [_vp, _vp, _sz]
 _lib.bd_attn_plan_check.argtypes = [_vp, _vp, _sz]
+_lib.bd_attn_device_check_errors.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_int]
 _lib.bd_attn_plan_upload.argtypes = [_vp, _vp, _vp]
 _lib.bd_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.bd_attn_bwd.argtypes = [_vp] * 13
@@ -78,7 +81,7 @@ _lib.bd_attn_last_error.restype = ctypes.c_char_p
 _lib.bd_attn_version.restype = ctypes.c_char_p
 for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
            "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_destroy",
-           "bd_attn_fwd_noalloc", "bd_attn_plan_check"):
+           "bd_attn_fwd_noalloc", "bd_attn_plan_check", "bd_attn_device_check_errors"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -154,7 +157,8 @@ EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_
             "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_kernels",
             "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version",
             "bd_attn_pack", "bd_aec_workspace", "bd_aec_fwd", "bd_aec_fwd_timed", "bd_aec_kernels",
-            "bd_aec_bwd", "bd_aec_bwd_timed", "bd_attn_fwd_noalloc", "bd_attn_plan_check")
+            "bd_aec_bwd", "bd_aec_bwd_timed", "bd_attn_fwd_noalloc", "bd_attn_plan_check",
+            "bd_attn_device_check_errors")
 
 # size of the fixed forward workspace of bd_attn_fwd_noalloc (BD_ATTN_NOALLOC_WS_BYTES)
 NOALLOC_WS_BYTES = 32 << 20
@@ -173,6 +177,16 @@ def _check(st):
 
 def version() -> str:
     return _lib.bd_attn_version().decode()
+
+
+def device_check_errors(reset: bool = False) -> int:
+    """Workgroups that rejected a work record on the current device since the
+    last reset (blocking). Only a library built with device-side checks
+    (libbdattn_checked.so, selected with BDATTN_LIBRARY) has the counters; other
+    builds raise BdAttnError with EUNSUPPORTED."""
+    n = ctypes.c_uint64(0)
+    _check(_lib.bd_attn_device_check_errors(ctypes.byref(n), 1 if reset else 0))
+    return int(n.value)
 
 
 def _arr(vals):

@@ -245,9 +245,15 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const SwLane<D> lo(lane);
   const int4 itv = ld_rec4(a.bwd_items, blockIdx.x);
   if (itv.x < 0) return;
+  if (reject_record(itv.x >= a.n_ktiles || itv.y < 0 || itv.y / a.hkv - 1 >= a.n_dkv_slots || itv.z < 0 ||
+                    itv.z > itv.w))
+    return;
   const int kvh = itv.y % a.hkv;
   const int slot = itv.y / a.hkv - 1;                   // partial slot of a split tile, or -1
   const KTile kt = load_ktile(a.ktiles, itv.x);
+  if (kDeviceChecks && reject_record(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq) ||
+                                     !ktile_canvq_in_bounds(kt, a.canvq, a.B, a.tq)))
+    return;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
   const bf16* __restrict__ V = static_cast<const bf16*>(a.v);
@@ -400,7 +406,11 @@ __global__ void __launch_bounds__(256) dkdv_merge_kernel(BwdArgs a) {
   constexpr int Q4 = D / 4;
   constexpr int WG_PER = kKBlock * Q4 / 256;
   const int4 mv = ld_rec4(a.bmerge, blockIdx.x / WG_PER);
+  if (reject_record(mv.x < 0 || mv.x >= a.n_ktiles || mv.y < 0 || mv.y >= a.hkv || mv.z < 0 || mv.w < 1 ||
+                    (int64_t)mv.z + mv.w > a.n_dkv_slots))
+    return;
   const KTile kt = load_ktile(a.ktiles, mv.x);
+  if (reject_record(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq))) return;
   const int idx = (blockIdx.x % WG_PER) * 256 + threadIdx.x;
   const int key = idx / Q4, d0 = (idx % Q4) * 4;
   if (key >= kt.n_keys) return;
@@ -443,8 +453,12 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   const SwLane<D> lo(lane);
   const int4 itv = ld_rec4(a.dq_items, blockIdx.x);
   if (itv.x < 0) return;
+  if (reject_record(itv.x >= a.n_qtiles)) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
   const QTile qt = load_qtile(a.qtiles, itv.x);
+  if (reject_record(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk) ||
+                    !key_range_in_bounds(qt, kt_begin, kt_end)))
+    return;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
   const bf16* __restrict__ V = static_cast<const bf16*>(a.v);
@@ -635,5 +649,7 @@ hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t 
   else hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+BD_ATTN_DEVICE_ERRORS_QUERY(device_errors_bwd)
 
 }  // namespace bdattn

@@ -28,8 +28,10 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdArgs a) {
   __shared__ float sV[kF32Tile][D];
   const int4 itv = reinterpret_cast<const int4*>(a.items)[blockIdx.x];
   if (itv.x < 0) return;
+  if (reject_record(itv.x >= a.n_qtiles)) return;
   const int kvh = itv.y;
   const QTile qt = load_qtile(a.qtiles, itv.x);
+  if (reject_record(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk))) return;
   const float* __restrict__ Q = static_cast<const float*>(a.q);
   const float* __restrict__ K = static_cast<const float*>(a.k);
   const float* __restrict__ V = static_cast<const float*>(a.v);
@@ -92,8 +94,10 @@ __global__ void __launch_bounds__(128) dq_f32_kernel(BwdArgs a) {
   __shared__ float sV[kF32Tile][D];
   const int4 itv = reinterpret_cast<const int4*>(a.dq_items)[blockIdx.x];
   if (itv.x < 0) return;
+  if (reject_record(itv.x >= a.n_qtiles)) return;
   const int kvh = itv.y;
   const QTile qt = load_qtile(a.qtiles, itv.x);
+  if (reject_record(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk))) return;
   const float* __restrict__ Q = static_cast<const float*>(a.q);
   const float* __restrict__ K = static_cast<const float*>(a.k);
   const float* __restrict__ V = static_cast<const float*>(a.v);
@@ -155,8 +159,12 @@ __global__ void __launch_bounds__(128) dkdv_f32_kernel(BwdArgs a) {
   __shared__ int sLim[R];
   const int4 itv = reinterpret_cast<const int4*>(a.bwd_items)[blockIdx.x];
   if (itv.x < 0) return;
+  if (reject_record(itv.x >= a.n_ktiles || itv.y < 0 || itv.y >= a.hkv)) return;   // fp32 tiles are never split
   const int kvh = itv.y;
   const KTile kt = load_ktile(a.ktiles, itv.x);
+  if (kDeviceChecks && reject_record(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq) ||
+                                     !ktile_canvq_in_bounds(kt, a.canvq, a.B, a.tq)))
+    return;
   const float* __restrict__ Q = static_cast<const float*>(a.q);
   const float* __restrict__ K = static_cast<const float*>(a.k);
   const float* __restrict__ V = static_cast<const float*>(a.v);
@@ -257,5 +265,7 @@ hipError_t launch_dkdv_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t
   else hipLaunchKernelGGL(dkdv_f32_kernel<64>, dim3(grid), dim3(128), 0, s, a);
   return hipGetLastError();
 }
+
+BD_ATTN_DEVICE_ERRORS_QUERY(device_errors_f32)
 
 }  // namespace bdattn

@@ -47,8 +47,10 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
   FwdWork w;
-  if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w) : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w))
+  if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w)
+            : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles))
     return;                                         // empty launch slot
+  if (reject_record(!fwd_work_in_bounds(w, SPLIT, a.G, a.hkv, a.tq, a.tk, a.n_slots))) return;
   const int kvh = w.kvh, kt_begin = w.kt_begin, kt_end = w.kt_end;
   const QTile& qt = w.qt;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
@@ -230,6 +232,10 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(MergeArgs a) {
   const int kvh = r2.x, first = r2.y, count = r2.z, blk = r2.w;
   if (kvh < 0) return;                             // empty launch slot
   const int q_tok = r0.x, n_tok = r0.y;
+  if (reject_record(kvh >= a.hq / a.G || q_tok < 0 || n_tok < 1 || n_tok * a.G > kQRows ||
+                    (int64_t)q_tok + n_tok > a.tq || first < 0 || count < 1 ||
+                    (int64_t)first + count > a.n_slots || blk < 0 || blk >= 8 * NDB))
+    return;
   const int w = blk / (2 * NDB), db = (blk / 2) % NDB, p = blk % 2;
   const int lane = threadIdx.x, j = lane & 31, h = lane >> 5;
   const int row = w * 32 + j;
@@ -311,5 +317,7 @@ hipError_t launch_merge(const MergeArgs& a, int head_dim, int grid, hipStream_t 
   else hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
+
+BD_ATTN_DEVICE_ERRORS_QUERY(device_errors_fwd)
 
 }  // namespace bdattn

@@ -82,8 +82,10 @@ __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   const int kbase = pad_base<D / 8>(lane);        // K operand rows
   const int vbase = pad_base<KT / 8>(lane);       // VT operand dimensions
   FwdWork w;
-  if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w) : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w))
+  if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w)
+            : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles))
     return;                                         // empty launch slot
+  if (reject_record(!fwd_work_in_bounds(w, SPLIT, a.G, a.hkv, a.tq, a.tk, a.n_slots))) return;
   const int kvh = w.kvh, kt_begin = w.kt_begin, kt_end = w.kt_end;
   const QTile& qt = w.qt;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
@@ -242,5 +244,7 @@ hipError_t launch_fwd_split_vt(const FwdArgs& a, int head_dim, int grid, hipStre
   else hipLaunchKernelGGL((fwd_vt_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+BD_ATTN_DEVICE_ERRORS_QUERY(device_errors_fwd_vt)
 
 }  // namespace bdattn

@@ -142,6 +142,23 @@ bd_attn_status bd_attn_plan_check(bd_attn_plan_t plan, const void* meta_host, si
   return BD_ATTN_OK;
 }
 
+bd_attn_status bd_attn_device_check_errors(uint64_t* count, int reset) {
+  if (!count) return fail(BD_ATTN_EINVAL, "count is NULL");
+#ifdef BD_ATTN_DEVICE_CHECKS
+  uint64_t n = 0;
+  hipError_t e = bdattn::device_errors_fwd(&n, reset != 0);
+  if (e == hipSuccess) e = bdattn::device_errors_fwd_vt(&n, reset != 0);
+  if (e == hipSuccess) e = bdattn::device_errors_bwd(&n, reset != 0);
+  if (e == hipSuccess) e = bdattn::device_errors_f32(&n, reset != 0);
+  if (bd_attn_status st = hip_status(e, "device check counters")) return st;
+  *count = n;
+  return BD_ATTN_OK;
+#else
+  (void)reset;
+  return fail(BD_ATTN_EUNSUPPORTED, "this library was built without device-side record checks");
+#endif
+}
+
 bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_stream_t stream) {
   if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
   if (bd_attn_status st = check_ptr(meta_dev, "meta_dev")) return st;
@@ -176,6 +193,8 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.hq = p.desc.num_q_heads; a.hkv = p.desc.num_kv_heads; a.G = p.G; a.grain = p.grain;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.tq = p.tq; a.tk = p.tk;
+  a.n_qtiles = (int)p.qtiles.size(); a.n_slots = (int)p.n_split_slots;
   const int D = p.desc.head_dim;
   hipError_t e;
   if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
@@ -212,6 +231,7 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   c.items = section<bdattn::MergeItem>(meta_dev, p.off_merge);
   c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
   c.hq = a.hq; c.G = a.G;
+  c.tq = p.tq; c.n_slots = (int)p.n_split_slots;
   e = bdattn::launch_merge(c, D, (int)p.merge_items.size(), s);
   if ((st = hip_status(e, "merge launch"))) return st;
   return hip_status(ev.mark(mark), "hipEventRecord");
@@ -323,6 +343,9 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.grain = p.grain;
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.tq = p.tq; a.tk = p.tk;
+  a.n_qtiles = (int)p.qtiles.size(); a.n_ktiles = (int)p.ktiles.size();
+  a.n_canvq = (int)p.canvq.size(); a.n_dkv_slots = (int)p.n_dkv_slots;
   if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
   hipError_t e;
   if (bf16) {

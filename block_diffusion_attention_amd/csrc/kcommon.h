@@ -337,11 +337,99 @@ struct FwdWork {
   int kvh, kt_begin, kt_end, slot;
 };
 
+// ---------------------------------------------------------------------------
+// Device-side record checks. A build compiled with BD_ATTN_DEVICE_CHECKS checks
+// every work record a workgroup reads against the list and tensor sizes before it
+// follows any index or token range in it. A record that fails is counted (one
+// counter per source file, read and cleared from the host) and its workgroup does
+// nothing. The values checked are wave-uniform and every wave of a workgroup reads
+// the same records, so a rejected workgroup leaves as a whole, before its first
+// barrier. Without the macro every check folds away and the kernels are unchanged.
+#ifdef BD_ATTN_DEVICE_CHECKS
+constexpr bool kDeviceChecks = true;
+static __device__ unsigned long long g_bad_records;
+#else
+constexpr bool kDeviceChecks = false;
+#endif
+
+// Host side of the counter: NAME(count, reset) waits for all work on the current
+// device, adds the count of that device's copy to *count and clears it when asked.
+// Each source file that launches checked kernels defines one with a name of its own.
+#ifdef BD_ATTN_DEVICE_CHECKS
+#define BD_ATTN_DEVICE_ERRORS_QUERY(NAME)                                                  \
+  hipError_t NAME(uint64_t* count, bool reset) {                                           \
+    void* p = nullptr;                                                                     \
+    hipError_t e = hipDeviceSynchronize();                                                 \
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_bad_records));           \
+    if (e != hipSuccess) return e;                                                         \
+    unsigned long long v = 0;                                                              \
+    if ((e = hipMemcpy(&v, p, sizeof v, hipMemcpyDeviceToHost)) != hipSuccess) return e;   \
+    *count += v;                                                                           \
+    if (reset) {                                                                           \
+      const unsigned long long zero = 0;                                                   \
+      e = hipMemcpy(p, &zero, sizeof zero, hipMemcpyHostToDevice);                         \
+    }                                                                                      \
+    return e;                                                                              \
+  }
+#else
+#define BD_ATTN_DEVICE_ERRORS_QUERY(NAME)
+#endif
+
+// True (and the record counted, once per workgroup) when a checked build finds
+// `bad`; always false otherwise.
+__device__ __forceinline__ bool reject_record(bool bad) {
+#ifdef BD_ATTN_DEVICE_CHECKS
+  if (bad) {
+    if (threadIdx.x == 0) atomicAdd(&g_bad_records, 1ull);
+    return true;
+  }
+#endif
+  (void)bad;
+  return false;
+}
+
+// A query tile's rows lie in [0, Tq) and fill at most one tile; its clean and own
+// key ranges lie in [0, Tk).
+__device__ __forceinline__ bool qtile_in_bounds(const QTile& t, int G, int64_t tq, int64_t tk) {
+  return t.q_tok >= 0 && t.n_tok >= 1 && t.n_tok * G <= kQRows && (int64_t)t.q_tok + t.n_tok <= tq &&
+         t.lim_min >= 0 && t.lim_min <= t.lim_max && t.k_ctx >= 0 && (int64_t)t.k_ctx + t.lim_max <= tk &&
+         t.n_own >= 0 && (t.n_own == 0 || (t.k_own >= 0 && (int64_t)t.k_own + t.n_own <= tk));
+}
+
+// A key-tile range [b, e) within a query tile's list (its clean tiles, then its own).
+__device__ __forceinline__ bool key_range_in_bounds(const QTile& t, int b, int e) {
+  const int n = (t.lim_max + kKTile - 1) / kKTile + (t.n_own + kKTile - 1) / kKTile;
+  return b >= 0 && b <= e && e <= n;
+}
+
+// A key tile's keys lie in [0, Tk), its clean query range in [0, Tq) and its
+// canvas-query entries in their list.
+__device__ __forceinline__ bool ktile_in_bounds(const KTile& t, int64_t tq, int64_t tk, int n_canvq) {
+  return t.k_tok >= 0 && t.n_keys >= 1 && t.n_keys <= kKBlock && (int64_t)t.k_tok + t.n_keys <= tk &&
+         t.cq_len >= 0 && (t.cq_len == 0 || (t.cq_tok >= 0 && (int64_t)t.cq_tok + t.cq_len <= tq)) &&
+         t.cv_begin >= 0 && t.cv_count >= 0 && (int64_t)t.cv_begin + t.cv_count <= n_canvq;
+}
+
+// A canvas-query entry holds one whole canvas (B rows) in [0, Tq).
+__device__ __forceinline__ bool canvq_in_bounds(const int4& e, int B, int64_t tq) {
+  return e.x >= 0 && e.y == B && (int64_t)e.x + e.y <= tq && e.z >= 0 && (e.w == 0 || e.w == 1);
+}
+
+// Every canvas-query entry a key tile lists (its range already checked).
+__device__ __forceinline__ bool ktile_canvq_in_bounds(const KTile& t, const void* canvq, int B, int64_t tq) {
+  bool ok = true;
+  for (int e = 0; e < t.cv_count; ++e) ok &= canvq_in_bounds(ld_rec4(canvq, t.cv_begin + e), B, tq);
+  return ok;
+}
+
 // Direct path: item i (launch order) and its query tile, two dependent scalar
-// loads. Returns false for an empty launch slot.
-__device__ __forceinline__ bool load_fwd_work(const void* items, const int32_t* qtiles, int i, FwdWork* w) {
+// loads. Returns false for an empty launch slot (and, in a checked build, for an
+// item whose query tile index lies outside the n_qtiles tiles).
+__device__ __forceinline__ bool load_fwd_work(const void* items, const int32_t* qtiles, int i, FwdWork* w,
+                                              int n_qtiles) {
   const int4 itv = ld_rec4(items, i);
   if (itv.x < 0) return false;
+  if (reject_record(itv.x >= n_qtiles)) return false;
   w->kvh = itv.y; w->kt_begin = itv.z; w->kt_end = itv.w; w->slot = -1;
   w->qt = load_qtile(qtiles, itv.x);
   return true;
@@ -355,6 +443,14 @@ __device__ __forceinline__ bool load_split_work(const void* splits, int i, FwdWo
   w->qt.lim_max = b.x; w->qt.lim_min = b.y; w->qt.k_own = b.z; w->qt.n_own = b.w;
   w->kvh = c.x; w->kt_begin = c.y; w->kt_end = c.z; w->slot = c.w;
   return w->kvh >= 0;
+}
+
+// A forward work item (either path) whose kv head, query tile, key-tile range and
+// partial slot (split path) are in bounds.
+__device__ __forceinline__ bool fwd_work_in_bounds(const FwdWork& w, bool split, int G, int hkv, int64_t tq,
+                                                   int64_t tk, int n_slots) {
+  return w.kvh >= 0 && w.kvh < hkv && qtile_in_bounds(w.qt, G, tq, tk) &&
+         key_range_in_bounds(w.qt, w.kt_begin, w.kt_end) && (!split || (w.slot >= 0 && w.slot < n_slots));
 }
 
 // Partial result of a split workgroup, in register order (see the layout next to

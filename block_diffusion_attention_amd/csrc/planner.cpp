@@ -632,9 +632,9 @@ bd_attn_status check_blob(const Plan& p, const int32_t* blob, size_t n_ints, std
   }
   const CanvasQ* cv = reinterpret_cast<const CanvasQ*>(sec[6]);
   for (int64_t i = 0; i < ncv; ++i)
-    if (cv[i].q_tok < 0 || cv[i].n_tok < 1 || (int64_t)cv[i].q_tok + cv[i].n_tok > p.tq ||
+    if (cv[i].q_tok < 0 || cv[i].n_tok != p.desc.block_size || (int64_t)cv[i].q_tok + cv[i].n_tok > p.tq ||
         cv[i].lim < 0 || (cv[i].own != 0 && cv[i].own != 1))
-      return bad("canvq", i, "canvas query rows outside [0, Tq) or bad limit");
+      return bad("canvq", i, "not one whole canvas of rows in [0, Tq), or bad limit");
   const BwdItem* bt = reinterpret_cast<const BwdItem*>(sec[7]);
   for (int64_t i = 0; i < expect[7]; ++i) {
     if (bt[i].ktile < 0) continue;

@@ -32,6 +32,39 @@ def test_exports_every_declared_function():
     assert set(b.EXPORTED) == names
 
 
+def test_device_check_query_needs_the_checked_build():
+    # the normal build's kernels check nothing and say so; no HIP call is made
+    n = ctypes.c_uint64(7)
+    assert b._lib.bd_attn_device_check_errors(ctypes.byref(n), 0) == b.EUNSUPPORTED
+    assert "without device-side record checks" in b._lib.bd_attn_last_error().decode()
+    assert n.value == 7
+    assert b._lib.bd_attn_device_check_errors(None, 0) == b.EINVAL
+
+
+CHECKED_EXPORTS = r'''
+import ctypes, sys
+sys.path.insert(0, ROOT)
+from block_diffusion_attention_amd import binding as b
+assert b.LIB_PATH == b.CHECKED_LIB_PATH, b.LIB_PATH
+lib = ctypes.CDLL(b.LIB_PATH)
+missing = [n for n in b.EXPORTED if not hasattr(lib, n)]
+assert not missing, missing
+assert b._lib.bd_attn_device_check_errors(None, 0) == b.EINVAL
+print("ok")
+'''
+
+
+def test_device_checked_build_loads_and_exports_everything():
+    import subprocess
+    import sys
+    if not os.path.exists(b.CHECKED_LIB_PATH):
+        pytest.skip("libbdattn_checked.so not built (build.py --device-checks)")
+    env = dict(os.environ, BDATTN_LIBRARY=b.CHECKED_LIB_PATH)
+    r = subprocess.run([sys.executable, "-c", f"ROOT = {ROOT!r}\n" + CHECKED_EXPORTS], env=env,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=300)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-3000:]
+
+
 def _status(meta, **over):
     d = dict(ctx=meta.ctx_len, q0=meta.ctx_q_begin, off=meta.canvas_offsets, cb=meta.flat_canvas_block_idx,
              B=meta.block_size, hq=meta.num_q_heads, hkv=meta.num_kv_heads, D=meta.head_dim,
@@ -440,7 +473,8 @@ CORRUPTIONS = [
     ("merge", 0, 10, lambda n: 10 ** 6, "partial slots"),
     ("ktiles", 0, 7, lambda n: n["canvq"] + 1, "canvas-query entries"),
     ("ktiles", 0, 1, lambda n: 129, "keys outside"),
-    ("canvq", 0, 0, lambda n: -1, "canvas query rows"),
+    ("canvq", 0, 0, lambda n: -1, "whole canvas"),
+    ("canvq", 0, 1, lambda n: 1, "whole canvas"),
     ("bwd", 0, 0, lambda n: n["ktiles"], "key tile index"),
     ("qtiles", 0, 4, lambda n: 10 ** 7, "clean key range"),
 ]
