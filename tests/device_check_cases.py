@@ -24,6 +24,9 @@ CASES = [
     ("ragged: B=3, G=3, D=64, token-causal", lambda: W.random_meta(
         np.random.default_rng(90), max_segments=3, max_blocks=12, block_sizes=(3,), max_canvases=4,
         hq=6, hkv=2, d=64, dtype="bf16", clean_causal=True), ("FLAG_FORCE_SPLIT",)),
+    ("fp32 random pack: B in {4, 8}, G=2, D=64", lambda: W.random_meta(
+        np.random.default_rng(7), max_segments=3, max_blocks=6, block_sizes=(4, 8), max_canvases=3,
+        hq=4, hkv=2, d=64, dtype="fp32"), ()),
 ]
 
 
@@ -69,10 +72,12 @@ def _rec(blob, secs, name, i):
 def plant(meta, plan, blob, sections):
     """Plants one record out of range per named section in a copy of the
     work-list image:
-      fwd, dq        : kv head = Hkv (forward / dQ item)
+      fwd, dq        : kv head = Hkv (forward / dQ item; an fp32 plan's forward reads the
+                       dQ items too, so there the record is rejected twice)
       split, merge   : kv head = Hkv (split-forward part / merge block)
       bwd            : chunk range with begin = end + 1 (dK/dV item)
       bmerge         : kv head = Hkv (dK/dV merge)
+      bwd_kvh        : kv head = Hkv in a dK/dV item of an fp32 plan (never split there)
     Each record is picked so that following it unchecked would still stay inside
     every tensor and workspace (checked here with asserts): a kv head of Hkv
     addresses head 0 of the next token, so the tiles chosen end before the last
@@ -92,6 +97,19 @@ def plant(meta, plan, blob, sections):
         o = _rec(blob, secs, "qtiles", i)
         return blob[o:o + 8]
 
+    def ktile_clear_of_end(i):
+        ko = _rec(blob, secs, "ktiles", i)
+        k_tok, n_keys, _, cq_tok, cq_len, _, cv_begin, cv_count = blob[ko:ko + 8]
+        if k_tok + n_keys >= tk or (cq_len > 0 and cq_tok + cq_len >= tq):
+            return False
+        for e in range(cv_begin, cv_begin + cv_count):
+            co = _rec(blob, secs, "canvq", e)
+            if blob[co] + blob[co + 1] >= tq:
+                return False
+        return True
+
+    fp32 = meta.dtype != "bf16"
+
     def pick(sec, ok):
         cnt, _ = secs[sec]
         assert cnt > 0, f"the plan has no {sec} records"
@@ -106,7 +124,7 @@ def plant(meta, plan, blob, sections):
         if sec in ("fwd", "dq"):
             o = pick(sec, lambda o: blob[o] >= 0 and clear_of_end(qtile_at(blob[o])))
             blob[o + 1] = hkv
-            expect += 1
+            expect += 2 if fp32 and sec == "dq" else 1
         elif sec in ("split", "merge"):
             o = pick(sec, lambda o: blob[o + 8] >= 0 and clear_of_end(blob[o:o + 8]))
             blob[o + 8] = hkv
@@ -122,10 +140,15 @@ def plant(meta, plan, blob, sections):
             o = pick(sec, kt_clear)
             blob[o + 1] = hkv
             expect += 128 * (d // 4) // 256      # workgroups per dK/dV merge record
+        elif sec == "bwd_kvh":
+            assert fp32, "bwd_kvh plants an fp32 plan's dK/dV item"
+            o = pick("bwd", lambda o: blob[o] >= 0 and ktile_clear_of_end(blob[o]))
+            blob[o + 1] = hkv
+            expect += 1
         else:
             raise ValueError(sec)
     return blob, expect
 
 
 # (case index, sections planted)
-PLANTS = [(3, ("fwd", "dq", "bwd", "bmerge")), (5, ("split", "merge", "bmerge"))]
+PLANTS = [(3, ("fwd", "dq", "bwd", "bmerge")), (5, ("split", "merge", "bmerge")), (8, ("dq", "bwd_kvh"))]

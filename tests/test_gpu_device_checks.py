@@ -5,8 +5,9 @@ on the GPU.
   the normal build's (forward direct and split with its merge, with and without
   the transposed V copy; dQ; dK/dV, split with its merge and masked; fp32).
 * Records planted out of range in the device copy of the work lists are counted
-  and their workgroups skipped: a kv head equal to Hkv in a forward, a dQ and a
-  dK/dV merge record, and an inverted chunk range in a dK/dV record. Each planted
+  and their workgroups skipped: a kv head equal to Hkv in a forward, dQ, split-part,
+  merge and dK/dV merge record and in an fp32 dK/dV record, and an inverted chunk
+  range in a dK/dV record. Each planted
   record is chosen (and asserted on the host) so that even a build without the
   checks would stay inside every tensor and workspace while following it.
 
