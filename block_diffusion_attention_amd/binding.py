@@ -15,16 +15,15 @@ import torch  # loaded first so the library binds to the HIP runtime torch alrea
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # BDATTN_LIBRARY selects another build of the same library (the host-sanitized
-# copy that build.py --sanitize writes, or the device-checked one that build.py
-# --device-checks writes); by default the in-tree libbdattn.so
+# copy that build.py --sanitize writes); by default the in-tree libbdattn.so
 LIB_PATH = os.environ.get("BDATTN_LIBRARY") or os.path.join(_HERE, "libbdattn.so")
-CHECKED_LIB_PATH = os.path.join(_HERE, "libbdattn_checked.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
 BF16, FP32 = 0, 1
 FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD, FLAG_FWD_DIRECT, FLAG_FWD_VT = 1, 2, 4, 8, 16
 FLAG_CLEAN_CAUSAL = 32
 FLAG_CHECK_PLAN = 64
+FLAG_DEBUG_CHECKS = 128
 
 
 def flag_split_tiles(n: int) -> int:
@@ -180,10 +179,8 @@ def version() -> str:
 
 
 def device_check_errors(reset: bool = False) -> int:
-    """Workgroups that rejected a work record on the current device since the
-    last reset (blocking). Only a library built with device-side checks
-    (libbdattn_checked.so, selected with BDATTN_LIBRARY) has the counters; other
-    builds raise BdAttnError with EUNSUPPORTED."""
+    """Workgroups of plans made with FLAG_DEBUG_CHECKS that rejected a work
+    record on the current device since the last reset (blocking)."""
     n = ctypes.c_uint64(0)
     _check(_lib.bd_attn_device_check_errors(ctypes.byref(n), 1 if reset else 0))
     return int(n.value)

@@ -1,7 +1,5 @@
 """Builds libbdattn.so (gfx950) in-tree with hipcc; the planner is plain C++ (g++).
-Two debug builds of the same sources: a host-sanitized copy (--sanitize) and
-libbdattn_checked.so (--device-checks), whose kernels check every work record
-against the plan's sizes before following it."""
+A debug build of the same sources with the host code sanitized: --sanitize."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -36,12 +34,6 @@ SAN_DIR = os.path.join(BUILD_DIR, "san")
 SAN_LIB = os.path.join(SAN_DIR, "libbdattn.so")
 SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
-# Device-checked build: every kernel validates its work records (indices inside
-# their lists, token ranges inside the tensors) and counts and skips a bad one;
-# bd_attn_device_check_errors reads the count. Same optimisation level otherwise.
-CHK_DIR = os.path.join(BUILD_DIR, "chk")
-CHK_LIB = os.path.join(HERE, "libbdattn_checked.so")
-CHK_FLAGS = ["-DBD_ATTN_DEVICE_CHECKS"]
 
 
 def _run(cmd):
@@ -52,21 +44,17 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, sanitize: bool = False, device_checks: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     """Compiles every source and links libbdattn.so; returns its path.
-    sanitize=True builds the host-sanitized copy under _build/san instead;
-    device_checks=True builds libbdattn_checked.so (objects under _build/chk)."""
-    if sanitize and device_checks:
-        raise ValueError("one debug build at a time")
-    out_dir = SAN_DIR if sanitize else CHK_DIR if device_checks else BUILD_DIR
-    lib = SAN_LIB if sanitize else CHK_LIB if device_checks else LIB
+    sanitize=True builds the host-sanitized copy under _build/san instead."""
+    out_dir = SAN_DIR if sanitize else BUILD_DIR
+    lib = SAN_LIB if sanitize else LIB
     os.makedirs(out_dir, exist_ok=True)
     san = SAN_FLAGS if sanitize else []
-    chk = CHK_FLAGS if device_checks else []
     jobs = []
     for s in HIP_SOURCES:
         obj = os.path.join(out_dir, s.replace(".hip", ".o"))
-        jobs.append(([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(s, []), *san, *chk, "-c", os.path.join(CSRC, s),
+        jobs.append(([HIPCC, *HIP_FLAGS, *HIP_FILE_FLAGS.get(s, []), *san, "-c", os.path.join(CSRC, s),
                       "-o", obj], obj))
     for s in CXX_SOURCES:
         obj = os.path.join(out_dir, s.replace(".cpp", ".o"))
@@ -104,12 +92,9 @@ def sanitizer_env() -> dict:
 
 
 if __name__ == "__main__":
-    # python build.py [-v] [--device-checks] [--sanitize [pytest args...]]:
-    # --sanitize builds the host-sanitized library and, given pytest arguments,
-    # runs them against it; --device-checks builds libbdattn_checked.so
-    if "--device-checks" in sys.argv:
-        print(build(verbose="-v" in sys.argv, device_checks=True))
-    elif "--sanitize" in sys.argv:
+    # python build.py [-v] [--sanitize [pytest args...]]: --sanitize builds the
+    # host-sanitized library and, given pytest arguments, runs them against it
+    if "--sanitize" in sys.argv:
         rest = sys.argv[sys.argv.index("--sanitize") + 1:]
         print(build(verbose="-v" in sys.argv, sanitize=True))
         if rest:

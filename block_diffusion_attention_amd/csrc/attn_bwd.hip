@@ -222,7 +222,7 @@ __device__ __forceinline__ void dkdv_chunk(const bf16x8 (&kf)[D / 16], const bf1
   });
 }
 
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool CHK>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) dkdv_bf16_kernel(BwdArgs a) {
   using Gm = DkdvGeom<D>;
   constexpr int NKS = D / 16, NDB = D / 32;
@@ -245,14 +245,14 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const SwLane<D> lo(lane);
   const int4 itv = ld_rec4(a.bwd_items, blockIdx.x);
   if (itv.x < 0) return;
-  if (reject_record(itv.x >= a.n_ktiles || itv.y < 0 || itv.y / a.hkv - 1 >= a.n_dkv_slots || itv.z < 0 ||
+  if (reject_record<CHK>(itv.x >= a.n_ktiles || itv.y < 0 || itv.y / a.hkv - 1 >= a.n_dkv_slots || itv.z < 0 ||
                     itv.z > itv.w))
     return;
   const int kvh = itv.y % a.hkv;
   const int slot = itv.y / a.hkv - 1;                   // partial slot of a split tile, or -1
   const KTile kt = load_ktile(a.ktiles, itv.x);
-  if (kDeviceChecks && reject_record(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq) ||
-                                     !ktile_canvq_in_bounds(kt, a.canvq, a.B, a.tq)))
+  if (CHK && reject_record<CHK>(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq) ||
+                                !ktile_canvq_in_bounds(kt, a.canvq, a.B, a.tq)))
     return;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ K = static_cast<const bf16*>(a.k);
@@ -401,16 +401,16 @@ __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 
 // Sums the fp32 partial dK/dV of a split key tile in slot order, applies the
 // softmax scale to dK and writes both in bf16. Workgroup: 256 threads, each four
 // consecutive dimensions of one key; (kKBlock * D / 4) / 256 workgroups per tile.
-template <int D>
+template <int D, bool CHK>
 __global__ void __launch_bounds__(256) dkdv_merge_kernel(BwdArgs a) {
   constexpr int Q4 = D / 4;
   constexpr int WG_PER = kKBlock * Q4 / 256;
   const int4 mv = ld_rec4(a.bmerge, blockIdx.x / WG_PER);
-  if (reject_record(mv.x < 0 || mv.x >= a.n_ktiles || mv.y < 0 || mv.y >= a.hkv || mv.z < 0 || mv.w < 1 ||
+  if (reject_record<CHK>(mv.x < 0 || mv.x >= a.n_ktiles || mv.y < 0 || mv.y >= a.hkv || mv.z < 0 || mv.w < 1 ||
                     (int64_t)mv.z + mv.w > a.n_dkv_slots))
     return;
   const KTile kt = load_ktile(a.ktiles, mv.x);
-  if (reject_record(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq))) return;
+  if (reject_record<CHK>(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq))) return;
   const int idx = (blockIdx.x % WG_PER) * 256 + threadIdx.x;
   const int key = idx / Q4, d0 = (idx % Q4) * 4;
   if (key >= kt.n_keys) return;
@@ -437,7 +437,7 @@ __global__ void __launch_bounds__(256) dkdv_merge_kernel(BwdArgs a) {
 // dQ: LDS operand reads run this many products ahead of the MFMA that consumes them.
 constexpr int kDqAhead = 3;   // (3 measured 0.6 % faster than 4 on the packed replay; 6 spills)
 
-template <int D>
+template <int D, bool CHK>
 __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   constexpr int KT = kKTile;
   constexpr int NDB = D / 32, NKS = D / 16;
@@ -453,10 +453,10 @@ __global__ void __launch_bounds__(256, 2) dq_bf16_kernel(BwdArgs a) {
   const SwLane<D> lo(lane);
   const int4 itv = ld_rec4(a.dq_items, blockIdx.x);
   if (itv.x < 0) return;
-  if (reject_record(itv.x >= a.n_qtiles)) return;
+  if (reject_record<CHK>(itv.x >= a.n_qtiles)) return;
   const int kvh = itv.y, kt_begin = itv.z, kt_end = itv.w;
   const QTile qt = load_qtile(a.qtiles, itv.x);
-  if (reject_record(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk) ||
+  if (reject_record<CHK>(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk) ||
                     !key_range_in_bounds(qt, kt_begin, kt_end)))
     return;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
@@ -622,31 +622,51 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool bf16, hipStream_t
   return hipGetLastError();
 }
 
+namespace {
+template <int D, bool CHK>
+void launch_dkdv_d(const BwdArgs& a, bool masked, int grid, hipStream_t s) {
+  if (masked) hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, CHK>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, CHK>), dim3(grid), dim3(256), 0, s, a);
+}
+}  // namespace
+
 hipError_t launch_dkdv_bf16(const BwdArgs& a, int head_dim, bool masked, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (head_dim == 128) {
-    if (masked) hipLaunchKernelGGL((dkdv_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dkdv_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.checks) launch_dkdv_d<128, true>(a, masked, grid, s);
+    else launch_dkdv_d<128, false>(a, masked, grid, s);
   } else {
-    if (masked) hipLaunchKernelGGL((dkdv_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dkdv_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+    if (a.checks) launch_dkdv_d<64, true>(a, masked, grid, s);
+    else launch_dkdv_d<64, false>(a, masked, grid, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_dkdv_merge(const BwdArgs& a, int head_dim, int n_merge, hipStream_t s) {
   if (n_merge <= 0) return hipSuccess;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(dkdv_merge_kernel<128>, dim3(n_merge * (kKBlock * 32 / 256)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(dkdv_merge_kernel<64>, dim3(n_merge * (kKBlock * 16 / 256)), dim3(256), 0, s, a);
+  const dim3 b(256);
+  if (head_dim == 128) {
+    const dim3 g(n_merge * (kKBlock * 32 / 256));
+    if (a.checks) hipLaunchKernelGGL((dkdv_merge_kernel<128, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_merge_kernel<128, false>), g, b, 0, s, a);
+  } else {
+    const dim3 g(n_merge * (kKBlock * 16 / 256));
+    if (a.checks) hipLaunchKernelGGL((dkdv_merge_kernel<64, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_merge_kernel<64, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dq_bf16(const BwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+  const dim3 g(grid), b(256);
+  if (head_dim == 128) {
+    if (a.checks) hipLaunchKernelGGL((dq_bf16_kernel<128, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((dq_bf16_kernel<128, false>), g, b, 0, s, a);
+  } else {
+    if (a.checks) hipLaunchKernelGGL((dq_bf16_kernel<64, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((dq_bf16_kernel<64, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -22,16 +22,16 @@ struct F32Ranges {
       : n1((qt.lim_max + kF32Tile - 1) / kF32Tile), n2((qt.n_own + kF32Tile - 1) / kF32Tile) {}
 };
 
-template <int D>
+template <int D, bool CHK>
 __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdArgs a) {
   __shared__ float sK[kF32Tile][D];
   __shared__ float sV[kF32Tile][D];
   const int4 itv = reinterpret_cast<const int4*>(a.items)[blockIdx.x];
   if (itv.x < 0) return;
-  if (reject_record(itv.x >= a.n_qtiles)) return;
+  if (reject_record<CHK>(itv.x >= a.n_qtiles)) return;
   const int kvh = itv.y;
   const QTile qt = load_qtile(a.qtiles, itv.x);
-  if (reject_record(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk))) return;
+  if (reject_record<CHK>(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk))) return;
   const float* __restrict__ Q = static_cast<const float*>(a.q);
   const float* __restrict__ K = static_cast<const float*>(a.k);
   const float* __restrict__ V = static_cast<const float*>(a.v);
@@ -88,16 +88,16 @@ __global__ void __launch_bounds__(128) fwd_f32_kernel(FwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool CHK>
 __global__ void __launch_bounds__(128) dq_f32_kernel(BwdArgs a) {
   __shared__ float sK[kF32Tile][D];
   __shared__ float sV[kF32Tile][D];
   const int4 itv = reinterpret_cast<const int4*>(a.dq_items)[blockIdx.x];
   if (itv.x < 0) return;
-  if (reject_record(itv.x >= a.n_qtiles)) return;
+  if (reject_record<CHK>(itv.x >= a.n_qtiles)) return;
   const int kvh = itv.y;
   const QTile qt = load_qtile(a.qtiles, itv.x);
-  if (reject_record(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk))) return;
+  if (reject_record<CHK>(kvh < 0 || kvh >= a.hkv || !qtile_in_bounds(qt, a.G, a.tq, a.tk))) return;
   const float* __restrict__ Q = static_cast<const float*>(a.q);
   const float* __restrict__ K = static_cast<const float*>(a.k);
   const float* __restrict__ V = static_cast<const float*>(a.v);
@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(128) dq_f32_kernel(BwdArgs a) {
 }
 
 // dK/dV: thread = key of the tile; the query rows of each chunk are staged in LDS.
-template <int D>
+template <int D, bool CHK>
 __global__ void __launch_bounds__(128) dkdv_f32_kernel(BwdArgs a) {
   constexpr int R = 8;                      // query rows per stage
   __shared__ float sQ[R][D];
@@ -159,11 +159,11 @@ __global__ void __launch_bounds__(128) dkdv_f32_kernel(BwdArgs a) {
   __shared__ int sLim[R];
   const int4 itv = reinterpret_cast<const int4*>(a.bwd_items)[blockIdx.x];
   if (itv.x < 0) return;
-  if (reject_record(itv.x >= a.n_ktiles || itv.y < 0 || itv.y >= a.hkv)) return;   // fp32 tiles are never split
+  if (reject_record<CHK>(itv.x >= a.n_ktiles || itv.y < 0 || itv.y >= a.hkv)) return;   // fp32 tiles are never split
   const int kvh = itv.y;
   const KTile kt = load_ktile(a.ktiles, itv.x);
-  if (kDeviceChecks && reject_record(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq) ||
-                                     !ktile_canvq_in_bounds(kt, a.canvq, a.B, a.tq)))
+  if (CHK && reject_record<CHK>(!ktile_in_bounds(kt, a.tq, a.tk, a.n_canvq) ||
+                                !ktile_canvq_in_bounds(kt, a.canvq, a.B, a.tq)))
     return;
   const float* __restrict__ Q = static_cast<const float*>(a.q);
   const float* __restrict__ K = static_cast<const float*>(a.k);
@@ -245,24 +245,34 @@ __global__ void __launch_bounds__(128) dkdv_f32_kernel(BwdArgs a) {
 
 }  // namespace
 
+// Launches kernel template K<D, CHK> for the head dimension and check mode.
+#define BD_F32_LAUNCH(K, a, head_dim, grid, s)                                                        \
+  do {                                                                                             \
+    const dim3 g_(grid), b_(128);                                                                  \
+    if (head_dim == 128) {                                                                         \
+      if ((a).checks) hipLaunchKernelGGL((K<128, true>), g_, b_, 0, s, a);                          \
+      else hipLaunchKernelGGL((K<128, false>), g_, b_, 0, s, a);                                    \
+    } else {                                                                                       \
+      if ((a).checks) hipLaunchKernelGGL((K<64, true>), g_, b_, 0, s, a);                           \
+      else hipLaunchKernelGGL((K<64, false>), g_, b_, 0, s, a);                                     \
+    }                                                                                              \
+  } while (0)
+
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(grid), dim3(128), 0, s, a);
-  else hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(grid), dim3(128), 0, s, a);
+  BD_F32_LAUNCH(fwd_f32_kernel, a, head_dim, grid, s);
   return hipGetLastError();
 }
 
 hipError_t launch_dq_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(dq_f32_kernel<128>, dim3(grid), dim3(128), 0, s, a);
-  else hipLaunchKernelGGL(dq_f32_kernel<64>, dim3(grid), dim3(128), 0, s, a);
+  BD_F32_LAUNCH(dq_f32_kernel, a, head_dim, grid, s);
   return hipGetLastError();
 }
 
 hipError_t launch_dkdv_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(dkdv_f32_kernel<128>, dim3(grid), dim3(128), 0, s, a);
-  else hipLaunchKernelGGL(dkdv_f32_kernel<64>, dim3(grid), dim3(128), 0, s, a);
+  BD_F32_LAUNCH(dkdv_f32_kernel, a, head_dim, grid, s);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ constexpr int kFwdAhead = 4;
 // the item comes with its query tile in one record, the first two key tiles are
 // requested together before anything else, and the result is a partial (bf16 O
 // normalized by the part's own row sums, fp32 LSE) for the merge kernel.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool CHK>
 __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   constexpr int KT = kKTile;
   constexpr int NDB = D / 32;
@@ -48,9 +48,9 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const SwLane<D> lo(lane);
   FwdWork w;
   if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w)
-            : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles))
+            : !load_fwd_work<CHK>(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles))
     return;                                         // empty launch slot
-  if (reject_record(!fwd_work_in_bounds(w, SPLIT, a.G, a.hkv, a.tq, a.tk, a.n_slots))) return;
+  if (reject_record<CHK>(!fwd_work_in_bounds(w, SPLIT, a.G, a.hkv, a.tq, a.tk, a.n_slots))) return;
   const int kvh = w.kvh, kt_begin = w.kt_begin, kt_end = w.kt_end;
   const QTile& qt = w.qt;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
 // batch), folded into a running maximum.
 constexpr int kMergeBatch = 32;
 
-template <int D>
+template <int D, bool CHK>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(MergeArgs a) {
   constexpr int NDB = D / 32;
   const int i = blockIdx.x;
@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(MergeArgs a) {
   const int kvh = r2.x, first = r2.y, count = r2.z, blk = r2.w;
   if (kvh < 0) return;                             // empty launch slot
   const int q_tok = r0.x, n_tok = r0.y;
-  if (reject_record(kvh >= a.hq / a.G || q_tok < 0 || n_tok < 1 || n_tok * a.G > kQRows ||
+  if (reject_record<CHK>(kvh >= a.hq / a.G || q_tok < 0 || n_tok < 1 || n_tok * a.G > kQRows ||
                     (int64_t)q_tok + n_tok > a.tq || first < 0 || count < 1 ||
                     (int64_t)first + count > a.n_slots || blk < 0 || blk >= 8 * NDB))
     return;
@@ -297,24 +297,40 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
+namespace {
+template <bool SPLIT>
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+  const dim3 g(grid), b(256);
+  if (head_dim == 128) {
+    if (a.checks) hipLaunchKernelGGL((fwd_bf16_kernel<128, SPLIT, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<128, SPLIT, false>), g, b, 0, s, a);
+  } else {
+    if (a.checks) hipLaunchKernelGGL((fwd_bf16_kernel<64, SPLIT, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, SPLIT, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
+  return launch_fwd<false>(a, head_dim, grid, s);
 }
 
 hipError_t launch_fwd_split_direct(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_fwd<true>(a, head_dim, grid, s);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, s, a);
-  else hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, s, a);
+  const dim3 g(grid), b(kMergeThreads);
+  if (head_dim == 128) {
+    if (a.checks) hipLaunchKernelGGL((merge_kernel<128, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((merge_kernel<128, false>), g, b, 0, s, a);
+  } else {
+    if (a.checks) hipLaunchKernelGGL((merge_kernel<64, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((merge_kernel<64, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
 }
 

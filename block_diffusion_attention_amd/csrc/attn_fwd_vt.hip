@@ -64,7 +64,7 @@ __device__ __forceinline__ bf16x8 ptr_operand(const float* p) {
 
 // SPLIT: one part of a split key range, item from the split list (with its query
 // tile), result written as a partial for the merge kernel.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool CHK>
 __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   constexpr int KT = kKTile;
   constexpr int NDB = D / 32;
@@ -83,9 +83,9 @@ __global__ void __launch_bounds__(256, 2) fwd_vt_kernel(FwdArgs a) {
   const int vbase = pad_base<KT / 8>(lane);       // VT operand dimensions
   FwdWork w;
   if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w)
-            : !load_fwd_work(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles))
+            : !load_fwd_work<CHK>(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles))
     return;                                         // empty launch slot
-  if (reject_record(!fwd_work_in_bounds(w, SPLIT, a.G, a.hkv, a.tq, a.tk, a.n_slots))) return;
+  if (reject_record<CHK>(!fwd_work_in_bounds(w, SPLIT, a.G, a.hkv, a.tq, a.tk, a.n_slots))) return;
   const int kvh = w.kvh, kt_begin = w.kt_begin, kt_end = w.kt_end;
   const QTile& qt = w.qt;
   const bf16* __restrict__ Q = static_cast<const bf16*>(a.q);
@@ -231,18 +231,28 @@ hipError_t launch_transpose_v(const void* v, void* vt, int tk, int tk_pad, int h
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
+namespace {
+template <bool SPLIT>
+hipError_t launch_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((fwd_vt_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((fwd_vt_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+  const dim3 g(grid), b(256);
+  if (head_dim == 128) {
+    if (a.checks) hipLaunchKernelGGL((fwd_vt_kernel<128, SPLIT, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((fwd_vt_kernel<128, SPLIT, false>), g, b, 0, s, a);
+  } else {
+    if (a.checks) hipLaunchKernelGGL((fwd_vt_kernel<64, SPLIT, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((fwd_vt_kernel<64, SPLIT, false>), g, b, 0, s, a);
+  }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fwd_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
+  return launch_vt<false>(a, head_dim, grid, s);
 }
 
 hipError_t launch_fwd_split_vt(const FwdArgs& a, int head_dim, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((fwd_vt_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((fwd_vt_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_vt<true>(a, head_dim, grid, s);
 }
 
 BD_ATTN_DEVICE_ERRORS_QUERY(device_errors_fwd_vt)

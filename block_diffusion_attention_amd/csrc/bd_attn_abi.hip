@@ -144,7 +144,6 @@ bd_attn_status bd_attn_plan_check(bd_attn_plan_t plan, const void* meta_host, si
 
 bd_attn_status bd_attn_device_check_errors(uint64_t* count, int reset) {
   if (!count) return fail(BD_ATTN_EINVAL, "count is NULL");
-#ifdef BD_ATTN_DEVICE_CHECKS
   uint64_t n = 0;
   hipError_t e = bdattn::device_errors_fwd(&n, reset != 0);
   if (e == hipSuccess) e = bdattn::device_errors_fwd_vt(&n, reset != 0);
@@ -153,10 +152,6 @@ bd_attn_status bd_attn_device_check_errors(uint64_t* count, int reset) {
   if (bd_attn_status st = hip_status(e, "device check counters")) return st;
   *count = n;
   return BD_ATTN_OK;
-#else
-  (void)reset;
-  return fail(BD_ATTN_EUNSUPPORTED, "this library was built without device-side record checks");
-#endif
 }
 
 bd_attn_status bd_attn_plan_upload(bd_attn_plan_t plan, void* meta_dev, bd_attn_stream_t stream) {
@@ -195,6 +190,7 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.scale_log2 = p.scale * 1.4426950408889634f;
   a.tq = p.tq; a.tk = p.tk;
   a.n_qtiles = (int)p.qtiles.size(); a.n_slots = (int)p.n_split_slots;
+  a.checks = p.checks;
   const int D = p.desc.head_dim;
   hipError_t e;
   if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
@@ -232,6 +228,7 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
   c.hq = a.hq; c.G = a.G;
   c.tq = p.tq; c.n_slots = (int)p.n_split_slots;
+  c.checks = p.checks;
   e = bdattn::launch_merge(c, D, (int)p.merge_items.size(), s);
   if ((st = hip_status(e, "merge launch"))) return st;
   return hip_status(ev.mark(mark), "hipEventRecord");
@@ -346,6 +343,7 @@ static bd_attn_status bwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
   a.tq = p.tq; a.tk = p.tk;
   a.n_qtiles = (int)p.qtiles.size(); a.n_ktiles = (int)p.ktiles.size();
   a.n_canvq = (int)p.canvq.size(); a.n_dkv_slots = (int)p.n_dkv_slots;
+  a.checks = p.checks;
   if ((st = hip_status(ev.mark(0), "hipEventRecord"))) return st;
   hipError_t e;
   if (bf16) {

@@ -338,24 +338,19 @@ struct FwdWork {
 };
 
 // ---------------------------------------------------------------------------
-// Device-side record checks. A build compiled with BD_ATTN_DEVICE_CHECKS checks
-// every work record a workgroup reads against the list and tensor sizes before it
-// follows any index or token range in it. A record that fails is counted (one
-// counter per source file, read and cleared from the host) and its workgroup does
+// Device-side record checks (plans made with BD_ATTN_FLAG_DEBUG_CHECKS). Every
+// kernel has a CHK template parameter; its CHK instantiation checks each work
+// record a workgroup reads against the list and tensor sizes before it follows any
+// index or token range in it. A record that fails is counted (one counter per
+// source file and device, read and cleared from the host) and its workgroup does
 // nothing. The values checked are wave-uniform and every wave of a workgroup reads
 // the same records, so a rejected workgroup leaves as a whole, before its first
-// barrier. Without the macro every check folds away and the kernels are unchanged.
-#ifdef BD_ATTN_DEVICE_CHECKS
-constexpr bool kDeviceChecks = true;
+// barrier. In the instantiations without CHK every check folds away.
 static __device__ unsigned long long g_bad_records;
-#else
-constexpr bool kDeviceChecks = false;
-#endif
 
 // Host side of the counter: NAME(count, reset) waits for all work on the current
 // device, adds the count of that device's copy to *count and clears it when asked.
 // Each source file that launches checked kernels defines one with a name of its own.
-#ifdef BD_ATTN_DEVICE_CHECKS
 #define BD_ATTN_DEVICE_ERRORS_QUERY(NAME)                                                  \
   hipError_t NAME(uint64_t* count, bool reset) {                                           \
     void* p = nullptr;                                                                     \
@@ -371,19 +366,17 @@ constexpr bool kDeviceChecks = false;
     }                                                                                      \
     return e;                                                                              \
   }
-#else
-#define BD_ATTN_DEVICE_ERRORS_QUERY(NAME)
-#endif
 
-// True (and the record counted, once per workgroup) when a checked build finds
-// `bad`; always false otherwise.
+// True (and the record counted, once per workgroup) when a checking instantiation
+// finds `bad`; always false in the others.
+template <bool CHK>
 __device__ __forceinline__ bool reject_record(bool bad) {
-#ifdef BD_ATTN_DEVICE_CHECKS
-  if (bad) {
-    if (threadIdx.x == 0) atomicAdd(&g_bad_records, 1ull);
-    return true;
+  if constexpr (CHK) {
+    if (bad) {
+      if (threadIdx.x == 0) atomicAdd(&g_bad_records, 1ull);
+      return true;
+    }
   }
-#endif
   (void)bad;
   return false;
 }
@@ -423,13 +416,14 @@ __device__ __forceinline__ bool ktile_canvq_in_bounds(const KTile& t, const void
 }
 
 // Direct path: item i (launch order) and its query tile, two dependent scalar
-// loads. Returns false for an empty launch slot (and, in a checked build, for an
-// item whose query tile index lies outside the n_qtiles tiles).
+// loads. Returns false for an empty launch slot (and, with CHK, for an item whose
+// query tile index lies outside the n_qtiles tiles).
+template <bool CHK>
 __device__ __forceinline__ bool load_fwd_work(const void* items, const int32_t* qtiles, int i, FwdWork* w,
                                               int n_qtiles) {
   const int4 itv = ld_rec4(items, i);
   if (itv.x < 0) return false;
-  if (reject_record(itv.x >= n_qtiles)) return false;
+  if (reject_record<CHK>(itv.x >= n_qtiles)) return false;
   w->kvh = itv.y; w->kt_begin = itv.z; w->kt_end = itv.w; w->slot = -1;
   w->qt = load_qtile(qtiles, itv.x);
   return true;

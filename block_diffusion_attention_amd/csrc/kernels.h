@@ -24,9 +24,10 @@ struct FwdArgs {
   int grain;                 // step of the clean row limits: block size, or 1 (token-causal)
   float scale_log2;          // softmax scale * log2(e)
   float scale;               // softmax scale
-  // list and tensor sizes, read only by builds with device-side record checks
+  // list and tensor sizes, read only by the record-checking instantiations
   int64_t tq, tk;            // packed query / key tokens
   int n_qtiles, n_slots;     // query tiles; partial slots of the split path
+  bool checks;               // launch the record-checking instantiations (host side)
 };
 
 struct MergeArgs {
@@ -36,8 +37,9 @@ struct MergeArgs {
   void* o;
   float* lse;
   int hq, G;
-  int64_t tq;                // (device-side record checks) packed query tokens
-  int n_slots;               // (device-side record checks) partial slots
+  int64_t tq;                // (record checks) packed query tokens
+  int n_slots;               // (record checks) partial slots
+  bool checks;               // launch the record-checking instantiation (host side)
 };
 
 struct BwdArgs {
@@ -64,9 +66,10 @@ struct BwdArgs {
   int grain;                 // step of the clean row limits: block size, or 1 (token-causal)
   float scale_log2;
   float scale;
-  // list and tensor sizes, read only by builds with device-side record checks
+  // list and tensor sizes, read only by the record-checking instantiations
   int64_t tq, tk;
   int n_qtiles, n_ktiles, n_canvq, n_dkv_slots;
+  bool checks;               // launch the record-checking instantiations (host side)
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, int grid, hipStream_t s);
@@ -86,9 +89,9 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, int grid, hipStream_t 
 hipError_t launch_dkdv_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
 hipError_t launch_dq_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s);
 
-// Workgroups that rejected a work record since the last reset, one counter per
-// source file, added to *count (defined only in builds with BD_ATTN_DEVICE_CHECKS;
-// blocking: waits for all work on the current device).
+// Workgroups of record-checking launches that rejected a work record on the
+// current device since the last reset, one counter per source file, added to
+// *count (blocking: waits for all work on the current device).
 hipError_t device_errors_fwd(uint64_t* count, bool reset);
 hipError_t device_errors_fwd_vt(uint64_t* count, bool reset);
 hipError_t device_errors_bwd(uint64_t* count, bool reset);

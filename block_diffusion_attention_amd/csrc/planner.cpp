@@ -519,7 +519,8 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
   p.off_ws_lse2 = ceil_div(tq * Hq * 4, 256) * 256;          // delta [Tq, Hq] fp32, then LSE*log2(e)
   p.off_ws_dkv = 2 * p.off_ws_lse2;                          // then the partial dK/dV slots
   p.ws_bwd = (size_t)(p.off_ws_dkv + p.n_dkv_slots * 2 * kKBlock * D * 4);
-  if (d->flags & BD_ATTN_FLAG_CHECK_PLAN) {
+  p.checks = (d->flags & BD_ATTN_FLAG_DEBUG_CHECKS) != 0;
+  if (d->flags & (BD_ATTN_FLAG_CHECK_PLAN | BD_ATTN_FLAG_DEBUG_CHECKS)) {
     std::string why;
     if (check_blob(p, p.blob.data(), p.blob.size(), &why) != BD_ATTN_OK) {
       *err = "plan self-check failed: " + why;

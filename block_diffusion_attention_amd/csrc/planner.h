@@ -36,6 +36,7 @@ struct Plan {
   int64_t off_qtiles = 0, off_fwd = 0, off_split = 0, off_merge = 0, off_dq = 0,
           off_ktiles = 0, off_canvq = 0, off_bwd = 0, off_bmerge = 0;   // int32 offsets into blob
   size_t ws_fwd = 0, ws_bwd = 0;
+  bool checks = false;               // launch the record-checking kernel instantiations
   bool use_vt = false;               // bf16 forward through the transposed V copy (B % 8 == 0)
   bool dkdv_masked = true;           // dK/dV needs per-score row limits (see build_plan)
   int64_t tk_pad = 0;                // row length of the transposed V copy

@@ -100,6 +100,10 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
 #define BD_ATTN_FLAG_CHECK_PLAN  64u /* bd_attn_plan runs bd_attn_plan_check on its own
                                        work lists before returning (EINVAL if they
                                        break an invariant; a debugging aid) */
+#define BD_ATTN_FLAG_DEBUG_CHECKS 128u /* debugging: the plan runs the record-checking
+                                         kernels (see bd_attn_device_check_errors), and
+                                         bd_attn_plan self-checks its work lists as with
+                                         CHECK_PLAN */
 #define BD_ATTN_FLAG_SPLIT_TILES(n) ((((uint32_t)(n)) & 0xffu) << 8)
 
 typedef struct bd_attn_plan_s* bd_attn_plan_t;
@@ -149,27 +153,26 @@ bd_attn_status bd_attn_plan_serialize(bd_attn_plan_t plan, void* meta_host, size
  * kernel follows lies inside its list or tensor (query / key tile indices,
  * canvas-query entries, kv heads, key tile ranges of a query tile, partial
  * slots, query and key token ranges inside [0, Tq) / [0, Tk)). For debugging a
- * planner change or an image that was edited or copied by hand: the kernels of
- * a normal build do not re-check these bounds (a build with device-side checks
- * does; see bd_attn_device_check_errors). Errors: EINVAL naming the first bad
- * section and record (bd_attn_last_error), EWORKSPACE if bytes is smaller than
- * meta_bytes. */
+ * planner change or an image that was edited or copied by hand: the kernels
+ * re-check these bounds only for plans made with BD_ATTN_FLAG_DEBUG_CHECKS (see
+ * bd_attn_device_check_errors). Errors: EINVAL naming the first bad section and
+ * record (bd_attn_last_error), EWORKSPACE if bytes is smaller than meta_bytes. */
 bd_attn_status bd_attn_plan_check(bd_attn_plan_t plan, const void* meta_host, size_t bytes);
 
-/* Debug builds only: a library compiled with BD_ATTN_DEVICE_CHECKS (the
- * package's build.py --device-checks writes libbdattn_checked.so) checks, in
- * every kernel, each work record a workgroup reads against the plan's list and
- * tensor sizes before following any index or token range in it (the bounds
- * bd_attn_plan_check tests on the host, applied to the image in device memory as
- * the kernels see it). A workgroup that finds a bad record is counted and does
- * nothing, so its part of the outputs is left unwritten; one bad record can be
- * counted by several workgroups (the dK/dV merge reads each record from several).
- * This call waits for all work on the current device, stores in *count the
- * number of such workgroups on that device since the last reset, and clears the
- * counters when reset is non-zero. Calls that overlap with kernels running on
- * other host threads race with them. Errors: EINVAL if count is NULL,
- * EUNSUPPORTED in a build without the checks (whose kernels check nothing),
- * EHIP if a HIP call fails. */
+/* Debugging. For a plan made with BD_ATTN_FLAG_DEBUG_CHECKS, bd_attn_fwd and
+ * bd_attn_bwd launch instantiations of their kernels that check each work record
+ * a workgroup reads against the plan's list and tensor sizes before following any
+ * index or token range in it (the bounds bd_attn_plan_check tests on the host,
+ * applied to the image in device memory as the kernels see it). A workgroup that
+ * finds a bad record is counted and does nothing, so its part of the outputs is
+ * left unwritten; one bad record can be counted by several workgroups (the dK/dV
+ * merge reads each record from several, and an fp32 plan's forward and dQ
+ * kernels read the same list). Other plans run kernels without these checks
+ * (their code is unchanged by them). This call waits for all work on the current
+ * device, stores in *count the number of such workgroups on that device since
+ * the last reset, and clears the counters when reset is non-zero. Calls that
+ * overlap with kernels running on other host threads race with them. Errors:
+ * EINVAL if count is NULL, EHIP if a HIP call fails. */
 bd_attn_status bd_attn_device_check_errors(uint64_t* count, int reset);
 
 /* Enqueues an asynchronous copy of the work lists into meta_dev (device memory

@@ -1,7 +1,6 @@
-"""Workloads and planted records for the device-checked build (imported by
-test_gpu_device_checks.py in the parent process and in the child that loads
-libbdattn_checked.so; the binding module is passed in, so the child binds the
-checked library)."""
+"""Workloads and planted records for the record-checking kernels (plans made
+with BD_ATTN_FLAG_DEBUG_CHECKS), used by test_gpu_device_checks.py; the binding
+module is passed in."""
 from __future__ import annotations
 
 import numpy as np
