@@ -47,9 +47,12 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int j = lane & 31, h = lane >> 5;
   const SwLane<D> lo(lane);
   FwdWork w;
-  if (SPLIT ? !load_split_work(a.splits, blockIdx.x, &w)
-            : !load_fwd_work<CHK>(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles))
-    return;                                         // empty launch slot
+  if constexpr (SPLIT) {
+    if (a.grid_parts > 0) grid_split_work(a.grid_qt, a.hkv, a.grid_parts, a.grid_tps, a.grid_tiles, blockIdx.x, &w);
+    else if (!load_split_work(a.splits, blockIdx.x, &w)) return;   // empty launch slot
+  } else {
+    if (!load_fwd_work<CHK>(a.items, a.qtiles, blockIdx.x, &w, a.n_qtiles)) return;   // empty launch slot
+  }
   if (reject_record<CHK>(!fwd_work_in_bounds(w, SPLIT, a.G, a.hkv, a.tq, a.tk, a.n_slots))) return;
   const int kvh = w.kvh, kt_begin = w.kt_begin, kt_end = w.kt_end;
   const QTile& qt = w.qt;

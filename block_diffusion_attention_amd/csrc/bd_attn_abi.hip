@@ -217,6 +217,10 @@ static bd_attn_status fwd_impl(bd_attn_plan_t plan, const void* meta_dev, const 
     return hip_status(ev.mark(mark), "hipEventRecord");
   }
   a.splits = section<bdattn::SplitItem>(meta_dev, p.off_split);
+  if (p.grid_parts > 0) {
+    a.grid_qt = p.qtiles[0];
+    a.grid_parts = p.grid_parts; a.grid_tps = p.grid_tps; a.grid_tiles = p.grid_tiles;
+  }
   a.part_o = static_cast<char*>(ws) + p.off_ws_part;
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + p.off_ws_lse);
   const int grid = (int)p.split_items.size();

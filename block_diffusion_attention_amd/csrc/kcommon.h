@@ -439,6 +439,19 @@ __device__ __forceinline__ bool load_split_work(const void* splits, int i, FwdWo
   return w->kvh >= 0;
 }
 
+// Split part i of a regular split grid (one query tile whose key range of ntiles
+// tiles each kv head cuts into parts of tps tiles): kv head i % hkv, part i / hkv,
+// slot kv head * parts + part. Computed from the index: no dependent record load.
+__device__ __forceinline__ void grid_split_work(const QTile& qt, int hkv, int parts, int tps, int ntiles, int i,
+                                                FwdWork* w) {
+  const int kvh = i % hkv, part = i / hkv;
+  w->qt = qt;
+  w->kvh = kvh;
+  w->kt_begin = part * tps;
+  w->kt_end = min(ntiles, (part + 1) * tps);
+  w->slot = kvh * parts + part;
+}
+
 // A forward work item (either path) whose kv head, query tile, key-tile range and
 // partial slot (split path) are in bounds.
 __device__ __forceinline__ bool fwd_work_in_bounds(const FwdWork& w, bool split, int G, int hkv, int64_t tq,

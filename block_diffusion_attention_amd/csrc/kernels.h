@@ -28,6 +28,11 @@ struct FwdArgs {
   int64_t tq, tk;            // packed query / key tokens
   int n_qtiles, n_slots;     // query tiles; partial slots of the split path
   bool checks;               // launch the record-checking instantiations (host side)
+  // regular split grid (split path; grid_parts = 0: the items are loaded): one query
+  // tile whose key range of grid_tiles tiles each kv head cuts into grid_parts parts
+  // of grid_tps tiles; workgroup i is part i / Hkv of kv head i % Hkv
+  QTile grid_qt;
+  int grid_parts, grid_tps, grid_tiles;
 };
 
 struct MergeArgs {

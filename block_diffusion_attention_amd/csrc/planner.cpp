@@ -88,6 +88,35 @@ void append_records(std::vector<int32_t>& blob, const std::vector<T>& v, int64_t
   blob.insert(blob.end(), p, p + v.size() * (sizeof(T) / sizeof(int32_t)));
 }
 
+// Sets p.grid_* when the split items and merge items follow the regular grid
+// described in planner.h (a single query tile, e.g. one request's denoising step).
+void find_split_grid(Plan& p, int Hkv, int64_t tps, int blocks_per_wave) {
+  p.grid_parts = p.grid_tps = p.grid_tiles = 0;
+  if (p.qtiles.size() != 1 || tps <= 0) return;
+  const QTile& qt = p.qtiles[0];
+  const int64_t nt = ceil_div(qt.lim_max, kKTile) + ceil_div(qt.n_own, kKTile);
+  const int64_t parts = ceil_div(nt, tps);
+  const int64_t blocks = ceil_div((int64_t)qt.n_tok * p.G, 32) * blocks_per_wave;
+  if ((int64_t)p.split_items.size() != parts * Hkv || (int64_t)p.merge_items.size() != blocks * Hkv) return;
+  for (int64_t i = 0; i < parts * Hkv; ++i) {
+    const SplitItem& it = p.split_items[i];
+    const int64_t kvh = i % Hkv, part = i / Hkv;
+    if (it.kvh != kvh || it.kt_begin != part * tps || it.kt_end != std::min(nt, (part + 1) * tps) ||
+        it.slot != kvh * parts + part || std::memcmp(&it.qt, &qt, sizeof qt) != 0)
+      return;
+  }
+  for (int64_t i = 0; i < blocks * Hkv; ++i) {
+    const MergeItem& m = p.merge_items[i];
+    const int64_t kvh = i % Hkv;
+    if (m.kvh != kvh || m.block != i / Hkv || m.first != kvh * parts || m.count != parts ||
+        std::memcmp(&m.qt, &qt, sizeof qt) != 0)
+      return;
+  }
+  p.grid_parts = (int)parts;
+  p.grid_tps = (int)tps;
+  p.grid_tiles = (int)nt;
+}
+
 }  // namespace
 
 bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
@@ -311,6 +340,7 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
         for (size_t r = 0; r < per[x].size(); ++r) p.merge_items[r * kNumXcd + x] = per[x][r];
       while (!p.merge_items.empty() && p.merge_items.back().kvh < 0) p.merge_items.pop_back();
       p.n_split_slots = (int64_t)raw.size();
+      find_split_grid(p, Hkv, tps, blocks_per_wave);
     }
     // dQ items: every (query tile, kv head), whole key range, same order policy
     p.dq_items.clear();

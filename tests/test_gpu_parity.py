@@ -200,6 +200,30 @@ def test_serving_steps_split_sizes(k, tiles):
     _compare(wl, gpu, run_oracle(wl, backward=False))
 
 
+def test_regular_split_grid_reads_no_records():
+    """A single-request denoising step is a regular split grid: its split workgroups
+    compute their work from their index. An edit to a split record of its uploaded
+    work lists (a part shortened by one key tile, inside every buffer) therefore
+    changes nothing. The commit-folded step has two query tiles, so its kernel reads
+    the same edit, and the edit changes its output."""
+    import device_check_cases as C
+    for k, grid in ((2, True), (6, False)):
+        _say(f"case regular split grid: workload {k}")
+        meta = W.config_meta(k, np.random.default_rng(k))
+        plan, ref = C.run_case(b, meta, 0)
+        blob = plan.host_blob()
+        secs = C._sections(blob)
+        so = C._rec(blob, secs, "split", 0)
+        assert blob[so + 8] >= 0 and blob[so + 10] - blob[so + 9] >= 2
+        blob[so + 10] -= 1
+        img = torch.tensor(blob, dtype=torch.int32).view(torch.uint8)
+        plan.meta_dev[:img.numel()].copy_(img.to(plan.meta_dev.device))
+        torch.cuda.synchronize()
+        _, out = C.run_case(b, meta, 0, plan=plan)
+        same = all(torch.equal(out[n].view(torch.uint8), ref[n].view(torch.uint8)) for n in ("o", "lse"))
+        assert same == grid, f"workload {k}: outputs {'changed' if grid else 'unchanged'} by the edited records"
+
+
 def _all_finite(gpu):
     # outputs start NaN-filled: every element must have been written
     for n, x in gpu.items():
