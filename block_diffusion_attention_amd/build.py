@@ -36,6 +36,25 @@ SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=und
              "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
+# A plain C99 program that uses the library through include/bd_attn.h alone (the
+# C-ABI consumer test): strict C, ROCm headers as system headers, the in-tree
+# library found next to the package at run time.
+CONSUMER_SRC = os.path.join(ROOT, "tests", "c_consumer", "bd_attn_consumer.c")
+CONSUMER_BIN = os.path.join(ROOT, "tests", "c_consumer", "bd_attn_consumer")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_consumer(cc: str = "gcc") -> str:
+    """Compiles the C consumer against the in-tree libbdattn.so; returns its path."""
+    tmp = CONSUMER_BIN + ".tmp"
+    _run([cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+          "-isystem", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), CONSUMER_SRC,
+          "-o", tmp, "-L", HERE, "-lbdattn", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/../../block_diffusion_attention_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")])
+    os.replace(tmp, CONSUMER_BIN)
+    return CONSUMER_BIN
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
@@ -73,6 +92,8 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     link_san = [*san, "-shared-libsan"] if sanitize else []
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_san, *[j[1] for j in jobs], "-o", tmp])
     os.replace(tmp, lib)
+    if not sanitize:
+        build_consumer()
     return lib
 
 
