@@ -45,7 +45,10 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
 def build_consumer(cc: str = "gcc") -> str:
-    """Compiles the C consumer against the in-tree libbdattn.so; returns its path."""
+    """Compiles the C consumer against the in-tree libbdattn.so; returns its path
+    (None for a copy of the package without the tests)."""
+    if not os.path.exists(CONSUMER_SRC):
+        return None
     tmp = CONSUMER_BIN + ".tmp"
     _run([cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
           "-isystem", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), CONSUMER_SRC,
