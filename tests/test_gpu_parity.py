@@ -224,6 +224,45 @@ def test_regular_split_grid_reads_no_records():
         assert same == grid, f"workload {k}: outputs {'changed' if grid else 'unchanged'} by the edited records"
 
 
+def test_two_streams_at_once():
+    """Two plans of one batch (the staircase with a forced split: split forward with
+    its merge, split dK/dV with its merge, so both workspaces are in use) run forward
+    and backward on two streams at the same time, three times each; every result is
+    bit for bit the one the same plan gives alone on the default stream."""
+    meta = W.config_meta(4, np.random.default_rng(4))
+    plans = [b.Plan(meta, b.FLAG_FORCE_SPLIT).upload("cuda") for _ in range(2)]
+    assert "merge" in plans[0].kernel_names(False) and "dkdv_merge" in plans[0].kernel_names(True)
+    hq, hkv, d = meta.num_q_heads, meta.num_kv_heads, meta.head_dim
+
+    def inputs(seed):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        r = lambda n, h, sc: (torch.randn(n, h, d, generator=g, device="cuda") * sc).to(torch.bfloat16)
+        return r(plans[0].tq, hq, 0.5), r(plans[0].tk, hkv, 0.5), r(plans[0].tk, hkv, 1.0), r(plans[0].tq, hq, 1.0)
+
+    def step(plan, x):
+        q, k, v, do = x
+        o, lse = b.fwd(plan, q, k, v)
+        return (o, lse) + tuple(b.bwd(plan, q, k, v, o, lse, do))
+
+    xs = [inputs(1), inputs(2)]
+    refs = [step(plans[i], xs[i]) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = [[], []]
+    for rep in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(step(plans[i], xs[i]))
+    torch.cuda.synchronize()
+    for i in range(2):
+        for res in outs[i]:
+            for got, ref in zip(res, refs[i]):
+                assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"stream {i}"
+
+
 def _all_finite(gpu):
     # outputs start NaN-filled: every element must have been written
     for n, x in gpu.items():

@@ -67,6 +67,38 @@ def _status(meta, **over):
 GOOD = Meta([64, 32], [0, 32], [[1, 2], [1]], 16, 4, 2, 128, "bf16")
 
 
+def test_planning_from_many_threads():
+    # plans are built on the caller's thread with no shared state: concurrent
+    # planning gives the same work lists as planning alone, and each thread's
+    # last error message is its own (ctypes releases the interpreter lock)
+    import threading
+    metas = [config_meta(k, np.random.default_rng(k)) for k in (1, 2, 4, 6)]
+    metas += [random_meta(np.random.default_rng(s), hq=4, hkv=2, d=64, dtype="bf16", offsets=True)
+              for s in range(4)]
+    ref = [b.Plan(m).host_blob() for m in metas]
+    bad = [(dict(D=96), "head_dim must be 64 or 128"), (dict(hq=3), "multiple of num_kv_heads"),
+           (dict(B=0), "block_size must be >= 1")]
+    failures = []
+
+    def work(tid):
+        try:
+            for rep in range(6):
+                over, needle = bad[(tid + rep) % len(bad)]
+                st, msg = _status(GOOD, **over)
+                assert st != 0 and needle in msg, (tid, rep, st, msg)
+                i = (tid + rep) % len(metas)
+                assert b.Plan(metas[i]).host_blob() == ref[i], (tid, rep, i)
+        except Exception as e:  # collected and reported by the main thread
+            failures.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not failures, failures[:3]
+
+
 @pytest.mark.parametrize("over,code", [
     (dict(S=0), b.EINVAL),
     (dict(B=0), b.EINVAL),
