@@ -88,28 +88,22 @@ void append_records(std::vector<int32_t>& blob, const std::vector<T>& v, int64_t
   blob.insert(blob.end(), p, p + v.size() * (sizeof(T) / sizeof(int32_t)));
 }
 
-// Sets p.grid_* when the split items and merge items follow the regular grid
-// described in planner.h (a single query tile, e.g. one request's denoising step).
-void find_split_grid(Plan& p, int Hkv, int64_t tps, int blocks_per_wave) {
+// Sets p.grid_* when the split items follow the regular grid described in
+// planner.h (a single query tile, e.g. one request's denoising step). The merge
+// items read their slots from their records, which the grid's slot numbering
+// matches by construction (slot = index of the raw item = kv head * parts + part).
+void find_split_grid(Plan& p, int Hkv, int64_t tps) {
   p.grid_parts = p.grid_tps = p.grid_tiles = 0;
   if (p.qtiles.size() != 1 || tps <= 0) return;
   const QTile& qt = p.qtiles[0];
   const int64_t nt = ceil_div(qt.lim_max, kKTile) + ceil_div(qt.n_own, kKTile);
   const int64_t parts = ceil_div(nt, tps);
-  const int64_t blocks = ceil_div((int64_t)qt.n_tok * p.G, 32) * blocks_per_wave;
-  if ((int64_t)p.split_items.size() != parts * Hkv || (int64_t)p.merge_items.size() != blocks * Hkv) return;
+  if ((int64_t)p.split_items.size() != parts * Hkv || p.n_split_slots != parts * Hkv) return;
   for (int64_t i = 0; i < parts * Hkv; ++i) {
     const SplitItem& it = p.split_items[i];
     const int64_t kvh = i % Hkv, part = i / Hkv;
     if (it.kvh != kvh || it.kt_begin != part * tps || it.kt_end != std::min(nt, (part + 1) * tps) ||
         it.slot != kvh * parts + part || std::memcmp(&it.qt, &qt, sizeof qt) != 0)
-      return;
-  }
-  for (int64_t i = 0; i < blocks * Hkv; ++i) {
-    const MergeItem& m = p.merge_items[i];
-    const int64_t kvh = i % Hkv;
-    if (m.kvh != kvh || m.block != i / Hkv || m.first != kvh * parts || m.count != parts ||
-        std::memcmp(&m.qt, &qt, sizeof qt) != 0)
       return;
   }
   p.grid_parts = (int)parts;
@@ -292,7 +286,19 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
         if (split) merges.push_back(mg);
       }
     }
-    const auto ord = launch_order(cost, cls, xcd);
+    std::vector<int32_t> ord;
+    if (split && nq == 1 && Hkv % kNumXcd == 0) {
+      // one query tile (a single request's step) and kv heads a multiple of the XCD
+      // count: part-major order, workgroup i = part i / Hkv of kv head i % Hkv. It is
+      // largest-first (only the last part can be shorter), keeps each kv head's parts
+      // on one XCD (i % 8), and is the regular grid whose workgroups need no record
+      // (find_split_grid). With fewer kv heads a head's parts would span several XCDs
+      // either way, and the plain order measured as fast or faster.
+      const int64_t parts = ceil_div(tiles_of(p.qtiles[0]), tps);
+      for (int64_t i = 0; i < parts * Hkv; ++i) ord.push_back((int32_t)((i % Hkv) * parts + i / Hkv));
+    } else {
+      ord = launch_order(cost, cls, xcd);
+    }
     if (!split) {
       for (int32_t o : ord) p.fwd_items.push_back(o < 0 ? FwdItem{-1, 0, 0, 0} : raw[o]);
     } else {
@@ -340,7 +346,7 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
         for (size_t r = 0; r < per[x].size(); ++r) p.merge_items[r * kNumXcd + x] = per[x][r];
       while (!p.merge_items.empty() && p.merge_items.back().kvh < 0) p.merge_items.pop_back();
       p.n_split_slots = (int64_t)raw.size();
-      find_split_grid(p, Hkv, tps, blocks_per_wave);
+      find_split_grid(p, Hkv, tps);
     }
     // dQ items: every (query tile, kv head), whole key range, same order policy
     p.dq_items.clear();

@@ -27,10 +27,9 @@ struct Plan {
   int64_t n_split_slots = 0;         // partial slots of the split path
   // Regular split grid (0 parts: none): one query tile whose key range of grid_tiles
   // key tiles every kv head cuts into grid_parts parts of grid_tps tiles; split item
-  // i is (kv head i % Hkv, part i / Hkv) writing slot kv head * parts + part, merge
-  // item i is (kv head i % Hkv, block i / Hkv). Its split workgroups compute their
-  // work from their index instead of loading their record (one dependent memory
-  // round trip less before the first K/V request).
+  // i is (kv head i % Hkv, part i / Hkv) writing slot kv head * parts + part. Its
+  // split workgroups compute their work from their index instead of loading their
+  // record (one dependent memory round trip less before the first K/V request).
   int grid_parts = 0, grid_tps = 0, grid_tiles = 0;
   std::vector<FwdItem> dq_items;     // launch order
   std::vector<KTile> ktiles;

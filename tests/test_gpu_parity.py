@@ -224,6 +224,42 @@ def test_regular_split_grid_reads_no_records():
         assert same == grid, f"workload {k}: outputs {'changed' if grid else 'unchanged'} by the edited records"
 
 
+# single-request steps (one canvas over its context): (Hq, Hkv, D, B, context)
+SINGLE_REQUEST_SHAPES = [(32, 8, 128, 32, 2048), (16, 4, 64, 16, 1024), (12, 4, 128, 8, 2000),
+                         (8, 8, 64, 32, 1024), (16, 16, 128, 16, 4096), (4, 2, 128, 32, 5984),
+                         (6, 3, 64, 16, 960)]
+
+
+@pytest.mark.parametrize("shape", SINGLE_REQUEST_SHAPES)
+def test_single_request_steps_on_the_regular_grid(shape):
+    """Single-request steps of several head counts, head dims and block sizes match the
+    oracle. Those with kv heads a multiple of 8 are regular split grids whose split
+    workgroups read no record: with the forward workspace cleared, pointing a split
+    record at another part's slot (inside every buffer) changes nothing. For the
+    others the kernel reads the edited record, and the output changes."""
+    import device_check_cases as C
+    hq, hkv, d, B, ctx = shape
+    _say(f"case single request {shape}")
+    meta = W.Meta([ctx], [ctx], [[ctx // B]], B, hq, hkv, d, "bf16")
+    wl = W.random_workload(np.random.default_rng(ctx + hq), meta, sigma=0.5, with_do=False)
+    gpu, plan = run_gpu(wl, backward=False)
+    assert "merge" in plan.kernel_names(False)
+    _compare(wl, gpu, run_oracle(wl, backward=False))
+    plan, ref = C.run_case(b, meta, 0)
+    blob = plan.host_blob()
+    secs = C._sections(blob)
+    s0, s1 = C._rec(blob, secs, "split", 0), C._rec(blob, secs, "split", 1)
+    assert blob[s0 + 11] != blob[s1 + 11]
+    blob[s0 + 11] = blob[s1 + 11]
+    img = torch.tensor(blob, dtype=torch.int32).view(torch.uint8)
+    plan.meta_dev[:img.numel()].copy_(img.to(plan.meta_dev.device))
+    plan.ws_fwd.zero_()
+    torch.cuda.synchronize()
+    _, out = C.run_case(b, meta, 0, plan=plan)
+    same = all(torch.equal(out[n].view(torch.uint8), ref[n].view(torch.uint8)) for n in ("o", "lse"))
+    assert same == (hkv % 8 == 0), f"{shape}: outputs {'changed' if same else 'unchanged'} by the edited record"
+
+
 def test_two_streams_at_once():
     """Two plans of one batch (the staircase with a forced split: split forward with
     its merge, split dK/dV with its merge, so both workspaces are in use) run forward
