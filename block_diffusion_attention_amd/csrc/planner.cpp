@@ -287,7 +287,7 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
       }
     }
     std::vector<int32_t> ord;
-    if (split && nq == 1 && Hkv % kNumXcd == 0) {
+    if (split && nq == 1 && Hkv % kNumXcd == 0 && xcd) {
       // one query tile (a single request's step) and kv heads a multiple of the XCD
       // count: part-major order, workgroup i = part i / Hkv of kv head i % Hkv. It is
       // largest-first (only the last part can be shorter), keeps each kv head's parts

@@ -84,7 +84,9 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
 /* flags */
 #define BD_ATTN_FLAG_NO_SPLIT   1u  /* never split a query tile's key range (forward) */
 #define BD_ATTN_FLAG_FORCE_SPLIT 2u /* always split long key ranges (forward; for tests) */
-#define BD_ATTN_FLAG_NO_XCD     4u  /* plain largest-cost-first order, no XCD grouping */
+#define BD_ATTN_FLAG_NO_XCD     4u  /* plain largest-cost-first order, no XCD grouping
+                                       (nor the part-major order of single-request
+                                       splits) */
 #define BD_ATTN_FLAG_FWD_DIRECT 8u /* bf16 forward without the transposed V copy (the
                                        default; kept for callers that set it) */
 #define BD_ATTN_FLAG_FWD_VT     16u /* bf16 forward through a transposed copy of V (a
