@@ -81,10 +81,15 @@ def parse():
 
 
 def src_hash(files):
+    """Hash of a kernel's source files and of the compiler flags they are built with
+    (a flag can change the machine code as much as an edit)."""
+    from block_diffusion_attention_amd import build as _build
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "block_diffusion_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+        if f.endswith(".hip"):
+            h.update(" ".join(_build.HIP_FLAGS + _build.HIP_FILE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 
@@ -93,7 +98,7 @@ KERNEL_SOURCES = {
     "transpose_v": ["attn_fwd_vt.hip", "kcommon.h", "kernels.h"],
     "dkdv": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "dkdv_masked": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
-    "dq": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
+    "dq": ["attn_dq.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "bwd_pre": ["attn_bwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "merge": ["attn_fwd.hip", "kcommon.h", "bd_records.h", "kernels.h"],
     "aec_entropy": ["aec.hip", "aec.h"],

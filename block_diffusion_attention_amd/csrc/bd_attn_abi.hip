@@ -148,6 +148,7 @@ bd_attn_status bd_attn_device_check_errors(uint64_t* count, int reset) {
   hipError_t e = bdattn::device_errors_fwd(&n, reset != 0);
   if (e == hipSuccess) e = bdattn::device_errors_fwd_vt(&n, reset != 0);
   if (e == hipSuccess) e = bdattn::device_errors_bwd(&n, reset != 0);
+  if (e == hipSuccess) e = bdattn::device_errors_dq(&n, reset != 0);
   if (e == hipSuccess) e = bdattn::device_errors_f32(&n, reset != 0);
   if (bd_attn_status st = hip_status(e, "device check counters")) return st;
   *count = n;

@@ -100,6 +100,7 @@ hipError_t launch_dq_f32(const BwdArgs& a, int head_dim, int grid, hipStream_t s
 hipError_t device_errors_fwd(uint64_t* count, bool reset);
 hipError_t device_errors_fwd_vt(uint64_t* count, bool reset);
 hipError_t device_errors_bwd(uint64_t* count, bool reset);
+hipError_t device_errors_dq(uint64_t* count, bool reset);
 hipError_t device_errors_f32(uint64_t* count, bool reset);
 
 }  // namespace bdattn
