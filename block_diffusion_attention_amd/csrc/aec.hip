@@ -342,9 +342,9 @@ __global__ void __launch_bounds__(kThreads) aec_grad_kernel(AecArgs a) {
     const float lp = x - lse;
     return -c * ex2(lp * kL2E) * (lp + H);
   };
-  for (int64_t i = threadIdx.x; i < nvec; i += kThreads) {
+  auto grad_vec = [&](const u32x4& w) {
     float x[EPV];
-    unpack<BF16>(__builtin_nontemporal_load(vp + i), x);
+    unpack<BF16>(w, x);
     u32x4 o;
     if constexpr (BF16) {
 #pragma unroll
@@ -353,8 +353,20 @@ __global__ void __launch_bounds__(kThreads) aec_grad_kernel(AecArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[k] = __builtin_bit_cast(uint32_t, grad(x[k]));
     }
-    op[i] = o;
+    return o;
+  };
+  // eight 16-byte loads in flight per thread, all issued before the batch's stores
+  // (each element is read and written by the same thread, so dlogits may be the
+  // logits buffer itself)
+  int64_t i = threadIdx.x;
+  for (; i + 7 * kThreads < nvec; i += 8 * kThreads) {
+    u32x4 w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = __builtin_nontemporal_load(vp + i + k * kThreads);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) op[i + k * kThreads] = grad_vec(w[k]);
   }
+  for (; i < nvec; i += kThreads) op[i] = grad_vec(__builtin_nontemporal_load(vp + i));
   if (threadIdx.x < tail) {
     const int64_t e = nvec * EPV + threadIdx.x;
     if constexpr (BF16) {
