@@ -387,8 +387,9 @@ int32_t bd_aec_kernels(const bd_aec_desc* desc);
  * The captured source means are constants. lse, hbar and h_state are the outputs
  * of bd_aec_fwd on the same inputs; grad_loss is a device scalar. state_rows must
  * be non-decreasing (states own disjoint row ranges). Launches "aec_grad_coef" (one
- * workgroup) and "aec_grad" (one pass over the logits). ws: bd_aec_workspace
- * bytes (required). Errors as bd_aec_fwd. */
+ * workgroup) and "aec_grad" (one pass over the logits). dlogits may be the logits
+ * buffer itself (in place; columns past V then keep the logits); otherwise the two
+ * must not overlap. ws: bd_aec_workspace bytes (required). Errors as bd_aec_fwd. */
 bd_attn_status bd_aec_bwd(const bd_aec_desc* desc, const void* logits, const uint8_t* unresolved,
                           const int32_t* state_rows, const int32_t* pair_next,
                           const float* pair_h_source, const float* pair_weight, const float* lse,

@@ -196,3 +196,35 @@ def test_backward_deterministic():
     wl = W.aec_workload(13, n_states=4, block=16)
     a, c = _run_bwd(wl, 3.0), _run_bwd(wl, 3.0)
     assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("vocab,stride", [(151936, 151936), (50257, 50264)])
+def test_backward_in_place(vocab, stride):
+    """dlogits may be the logits buffer itself: every element is read and written by
+    the same thread, all of a thread's loads of a batch before its stores. The
+    in-place result equals the out-of-place one bit for bit (columns past the
+    vocabulary keep the logits in place)."""
+    import ctypes
+    wl = W.aec_workload(14, n_states=4, block=16, vocab=vocab, row_stride=stride, dtype="bf16")
+    _say(f"case backward in place {wl.name} stride {stride}")
+    dev = "cuda"
+    logits = torch.from_numpy(wl.logits).to(dev).to(torch.bfloat16).contiguous()
+    t = lambda x, ty: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(ty)
+    kw = dict(unresolved=t(wl.unresolved, torch.uint8), state_rows=t(wl.state_rows, torch.int32),
+              pair_next=t(wl.pair_next, torch.int32), pair_h_source=t(wl.pair_h_source, torch.float32),
+              pair_weight=t(wl.pair_weight, torch.float32), rho=wl.rho, gate_max=wl.gate_max)
+    lse, hbar, hs, _loss = b.aec_fwd(logits, vocab, **kw)
+    g = torch.tensor([2.5], dtype=torch.float32, device=dev)
+    ref = b.aec_bwd(logits, vocab, lse=lse, hbar=hbar, h_state=hs, grad_loss=g, **kw)
+    inplace = logits.clone()
+    n, s = inplace.shape
+    d = b.aec_desc(n, vocab, s, inplace.dtype, hs.numel(), kw["pair_next"].numel(), wl.rho, wl.gate_max)
+    ws = torch.empty(max(16, b.aec_workspace_bytes(d)), dtype=torch.uint8, device=dev)
+    st = b._lib.bd_aec_bwd(ctypes.byref(d), b._ptr(inplace), b._ptr(kw["unresolved"]), b._ptr(kw["state_rows"]),
+                           b._ptr(kw["pair_next"]), b._ptr(kw["pair_h_source"]), b._ptr(kw["pair_weight"]),
+                           b._ptr(lse), b._ptr(hbar), b._ptr(hs), b._ptr(g), b._ptr(inplace), b._ptr(ws),
+                           b._stream(inplace.device))
+    assert st == b.OK, b._lib.bd_attn_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.equal(inplace[:, :vocab].view(torch.int16), ref[:, :vocab].view(torch.int16))
+    assert torch.equal(inplace[:, vocab:].view(torch.int16), logits[:, vocab:].view(torch.int16))
