@@ -89,10 +89,12 @@ __device__ __forceinline__ void unpack(const u32x4& w, float (&x)[BF16 ? 8 : 4])
   }
 }
 
-__device__ __forceinline__ void finish(const Acc& a, int vocab, float* lse, float* hbar) {
+__device__ __forceinline__ float finish(const Acc& a, int vocab, float* lse, float* hbar) {
   const float l2s = log2f(a.s);
   *lse = (a.m + l2s) * kLN2;
-  *hbar = (l2s - a.u / a.s) / log2f((float)vocab);
+  const float h = (l2s - a.u / a.s) / log2f((float)vocab);
+  *hbar = h;
+  return h;
 }
 
 template <bool BF16>
@@ -306,6 +308,172 @@ __global__ void __launch_bounds__(kThreads) aec_grad_coef_kernel(AecArgs a) {
   }
 }
 
+// ---------------------------------------------------------- LDS-resident forms
+// The two single-workgroup kernels above chain several dependent memory round
+// trips (partials -> entropies -> state means -> pairs; pairs -> D -> state
+// gradients -> row coefficients), partly through values they have just written.
+// For batches whose rows and states fit in LDS these forms request every input at
+// the start (one round trip) and keep the intermediates in LDS; every sum runs in
+// the same order as in the kernels above.
+constexpr int kLdsRows = 8192;
+constexpr int kLdsStates = 1024;
+
+__device__ float lds_state_mean(const int* rows, const unsigned char* unres, const float* hbar, int n_rows, int s,
+                                int lane) {
+  const int lo = min(max(rows[s], 0), n_rows);
+  const int hi = min(max(rows[s + 1], lo), n_rows);
+  float sum = 0.f, cnt = 0.f;
+  for (int i = lo + lane; i < hi; i += 64)
+    if (unres[i]) { sum += hbar[i]; cnt += 1.f; }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sum += __shfl_xor(sum, off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  return cnt > 0.f ? sum / cnt : __builtin_nanf("");
+}
+
+// States and the unresolved flags of the rows, into LDS (nothing when S = 0).
+__device__ __forceinline__ void stage_states(const AecArgs& a, int* rows, unsigned char* unres) {
+  if (a.n_states == 0) return;
+  for (int s = threadIdx.x; s <= a.n_states; s += kThreads) rows[s] = a.state_rows[s];
+  for (int r = threadIdx.x; r < a.n_rows; r += kThreads) unres[r] = a.unresolved[r];
+}
+
+__global__ void __launch_bounds__(kThreads) aec_reduce_lds_kernel(AecArgs a) {
+  __shared__ float s_hbar[kLdsRows];
+  __shared__ unsigned char s_unres[kLdsRows];
+  __shared__ int s_rows[kLdsStates + 1];
+  __shared__ float s_hstate[kLdsStates];
+  __shared__ float rn[kThreads], rd[kThreads];
+  const int tid = threadIdx.x;
+  int n0 = -1;                                      // this thread's first pair
+  float hs0 = 0.f, w0 = 0.f;
+  if (tid < a.n_pairs) { n0 = a.pair_next[tid]; hs0 = a.pair_h_source[tid]; w0 = a.pair_weight[tid]; }
+  stage_states(a, s_rows, s_unres);
+  if (a.nsplit > 1) {
+    for (int row = tid; row < a.n_rows; row += kThreads) {
+      const float* p = a.part + (int64_t)row * a.nsplit * 3;
+      Acc t{p[0], p[1], p[2]};
+      for (int k = 1; k < a.nsplit; ++k) merge(t, Acc{p[3 * k], p[3 * k + 1], p[3 * k + 2]});
+      s_hbar[row] = finish(t, a.vocab, a.lse + row, a.hbar + row);
+    }
+  } else {
+    for (int row = tid; row < a.n_rows; row += kThreads) s_hbar[row] = a.hbar[row];
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int s = wave; s < a.n_states; s += kThreads / 64) {
+    const float m = lds_state_mean(s_rows, s_unres, s_hbar, a.n_rows, s, lane);
+    if (lane == 0) { a.h_state[s] = m; s_hstate[s] = m; }
+  }
+  __syncthreads();
+  float num = 0.f, den = 0.f;
+  for (int p = tid; p < a.n_pairs; p += kThreads) {
+    const int n = p == tid ? n0 : a.pair_next[p];
+    const float hs = p == tid ? hs0 : a.pair_h_source[p];
+    if (n < 0 || n >= a.n_states || !__builtin_isfinite(hs) || !(hs <= a.gate_max)) continue;
+    const float hn = s_hstate[n];
+    if (!__builtin_isfinite(hn)) continue;
+    const float w = p == tid ? w0 : a.pair_weight[p];
+    const float h = fmaxf(0.f, hn - (1.f - a.rho) * hs);
+    num = fmaf(w * h, h, num);
+    den += w;
+  }
+  rn[tid] = num;
+  rd[tid] = den;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      rn[tid] += rn[tid + off];
+      rd[tid] += rd[tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) a.loss[0] = rd[0] > 0.f ? rn[0] / rd[0] : 0.f;
+}
+
+// A pair's gate and hinge against state means in LDS (pair_kept's rule).
+__device__ __forceinline__ bool lds_pair_kept(const AecArgs& a, const float* hstate, int n, float hs, float w_in,
+                                              float* w, float* hinge) {
+  if (n < 0 || n >= a.n_states || !__builtin_isfinite(hs) || !(hs <= a.gate_max)) return false;
+  const float hn = hstate[n];
+  if (!__builtin_isfinite(hn)) return false;
+  *w = w_in;
+  *hinge = fmaxf(0.f, hn - (1.f - a.rho) * hs);
+  return true;
+}
+
+__global__ void __launch_bounds__(kThreads) aec_grad_coef_lds_kernel(AecArgs a) {
+  __shared__ float red[kThreads];
+  __shared__ int tnext[kPairTile];
+  __shared__ float tcontrib[kPairTile];
+  __shared__ float s_hstate[kLdsStates], s_sgrad[kLdsStates];
+  __shared__ int s_rows[kLdsStates + 1];
+  __shared__ unsigned char s_unres[kLdsRows];
+  const int tid = threadIdx.x;
+  int n0 = -1;
+  float hs0 = 0.f, w0 = 0.f;
+  if (tid < a.n_pairs) { n0 = a.pair_next[tid]; hs0 = a.pair_h_source[tid]; w0 = a.pair_weight[tid]; }
+  for (int s = tid; s < a.n_states; s += kThreads) s_hstate[s] = a.h_state[s];
+  stage_states(a, s_rows, s_unres);
+  const float gl = a.grad_loss[0];
+  __syncthreads();
+  auto pair_at = [&](int p, int* n, float* hs, float* w) {
+    if (p == tid) { *n = n0; *hs = hs0; *w = w0; }
+    else { *n = a.pair_next[p]; *hs = a.pair_h_source[p]; *w = a.pair_weight[p]; }
+  };
+  float den = 0.f;
+  for (int p = tid; p < a.n_pairs; p += kThreads) {
+    int n;
+    float hs, wi, w, h;
+    pair_at(p, &n, &hs, &wi);
+    if (lds_pair_kept(a, s_hstate, n, hs, wi, &w, &h)) den += w;
+  }
+  red[tid] = den;
+  for (int i = tid; i < a.n_rows; i += kThreads) a.row_coef[i] = 0.f;
+  for (int s = tid; s < a.n_states; s += kThreads) s_sgrad[s] = 0.f;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float D = red[0];
+  const float scale = D > 0.f ? 2.f * gl / D : 0.f;
+  for (int p0 = 0; p0 < a.n_pairs; p0 += kPairTile) {
+    const int np = min(kPairTile, a.n_pairs - p0);
+    __syncthreads();                                  // the previous tile is consumed
+    for (int q = tid; q < np; q += kThreads) {
+      int n;
+      float hs, wi, w = 0.f, h = 0.f;
+      pair_at(p0 + q, &n, &hs, &wi);
+      const bool kept = lds_pair_kept(a, s_hstate, n, hs, wi, &w, &h);
+      tnext[q] = kept ? n : -1;
+      tcontrib[q] = scale * w * h;
+    }
+    __syncthreads();
+    for (int q = 0; q < np; ++q) {
+      const int n = tnext[q];
+      if (n >= 0 && n % kThreads == tid) s_sgrad[n] += tcontrib[q];
+    }
+  }
+  __syncthreads();
+  for (int s = tid; s < a.n_states; s += kThreads) a.state_grad[s] = s_sgrad[s];
+  const int lane = tid & 63, wave = tid >> 6;
+  const float inv_lnv = 1.f / logf((float)a.vocab);
+  for (int s = wave; s < a.n_states; s += kThreads / 64) {
+    const int lo = min(max(s_rows[s], 0), a.n_rows);
+    const int hi = min(max(s_rows[s + 1], lo), a.n_rows);
+    float cnt = 0.f;
+    for (int i = lo + lane; i < hi; i += 64) cnt += s_unres[i] ? 1.f : 0.f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    const float c = cnt > 0.f ? s_sgrad[s] / cnt * inv_lnv : 0.f;
+    for (int i = lo + lane; i < hi; i += 64)
+      if (s_unres[i]) a.row_coef[i] = c;
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v;
@@ -389,12 +557,18 @@ hipError_t launch_aec_entropy(const AecArgs& a, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_aec_reduce(const AecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(aec_reduce_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  if (a.n_rows <= kLdsRows && a.n_states <= kLdsStates)
+    hipLaunchKernelGGL(aec_reduce_lds_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(aec_reduce_kernel, dim3(1), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_aec_grad_coef(const AecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(aec_grad_coef_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  if (a.n_rows <= kLdsRows && a.n_states <= kLdsStates)
+    hipLaunchKernelGGL(aec_grad_coef_lds_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(aec_grad_coef_kernel, dim3(1), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

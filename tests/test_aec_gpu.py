@@ -228,3 +228,36 @@ def test_backward_in_place(vocab, stride):
     torch.cuda.synchronize()
     assert torch.equal(inplace[:, :vocab].view(torch.int16), ref[:, :vocab].view(torch.int16))
     assert torch.equal(inplace[:, vocab:].view(torch.int16), logits[:, vocab:].view(torch.int16))
+
+
+@pytest.mark.parametrize("n_states,block", [(1100, 8), (100, 90)])
+def test_batches_past_the_lds_forms(n_states, block):
+    """Batches with more than 1024 states or more than 8192 rows take the global-memory
+    forms of the two single-workgroup kernels (the LDS-resident forms cover smaller
+    ones): forward and gradient against the oracle, with more than 256 pairs so that
+    the pair loops run past their first batch."""
+    wl = W.aec_workload(15, n_states=n_states, block=block, vocab=64, states_per_response=4)
+    assert len(wl.unresolved) > 8192 or n_states > 1024
+    assert len(wl.pair_next) > 256 or n_states <= 256
+    _say(f"case {wl.name}: {n_states} states x {block} rows")
+    _check(wl, _run(wl), _ref(wl))
+    scale, g1 = _grad_scale(wl)
+    got = _run_bwd(wl, scale)
+    assert_close("aec:dlogits", got[:, :wl.vocab], scale * g1, "bf16")
+
+
+def test_lds_forms_with_many_pairs():
+    """The LDS-resident forms with more than 256 pairs (pairs past each thread's
+    first one are read in the loop) and more than one 2048-pair tile of the
+    gradient's state sums (the pair list repeated four times): forward and gradient
+    against the oracle."""
+    wl = W.aec_workload(16, n_states=1000, block=8, vocab=64, states_per_response=1000)
+    wl.pair_next = np.tile(wl.pair_next, 4)
+    wl.pair_h_source = np.tile(wl.pair_h_source, 4)
+    wl.pair_weight = np.tile(wl.pair_weight, 4) * np.float32(0.25)
+    assert len(wl.unresolved) <= 8192 and len(wl.pair_next) > 2048
+    _say(f"case {wl.name}: {len(wl.pair_next)} pairs")
+    _check(wl, _run(wl), _ref(wl))
+    scale, g1 = _grad_scale(wl)
+    got = _run_bwd(wl, scale)
+    assert_close("aec:dlogits", got[:, :wl.vocab], scale * g1, "bf16")
