@@ -65,6 +65,16 @@ _lib.bd_attn_plan_sizes.argtypes = [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.
 _lib.bd_attn_plan_serialize.argtypes = [_vp, _vp, _sz]
 _lib.bd_attn_plan_check.argtypes = [_vp, _vp, _sz]
 _lib.bd_attn_device_check_errors.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_int]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("split", "split_tiles", "split_grid", "fwd_vt", "dkdv_masked",
+                                              "debug_checks")] + \
+               [(n, ctypes.c_int64) for n in ("query_tiles", "key_tiles", "fwd_workgroups", "dq_workgroups",
+                                              "dkdv_workgroups", "dkdv_split_tiles")]
+
+
+_lib.bd_attn_plan_info.argtypes = [_vp, ctypes.POINTER(PlanInfo)]
 _lib.bd_attn_plan_upload.argtypes = [_vp, _vp, _vp]
 _lib.bd_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.bd_attn_bwd.argtypes = [_vp] * 13
@@ -80,7 +90,7 @@ _lib.bd_attn_last_error.restype = ctypes.c_char_p
 _lib.bd_attn_version.restype = ctypes.c_char_p
 for _f in ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_attn_plan_upload",
            "bd_attn_fwd", "bd_attn_bwd", "bd_attn_fwd_timed", "bd_attn_bwd_timed", "bd_attn_plan_destroy",
-           "bd_attn_fwd_noalloc", "bd_attn_plan_check", "bd_attn_device_check_errors"):
+           "bd_attn_fwd_noalloc", "bd_attn_plan_check", "bd_attn_device_check_errors", "bd_attn_plan_info"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -157,7 +167,7 @@ EXPORTED = ("bd_attn_plan", "bd_attn_plan_sizes", "bd_attn_plan_serialize", "bd_
             "bd_attn_plan_kernel_name", "bd_attn_plan_destroy", "bd_attn_last_error", "bd_attn_version",
             "bd_attn_pack", "bd_aec_workspace", "bd_aec_fwd", "bd_aec_fwd_timed", "bd_aec_kernels",
             "bd_aec_bwd", "bd_aec_bwd_timed", "bd_attn_fwd_noalloc", "bd_attn_plan_check",
-            "bd_attn_device_check_errors")
+            "bd_attn_device_check_errors", "bd_attn_plan_info")
 
 # size of the fixed forward workspace of bd_attn_fwd_noalloc (BD_ATTN_NOALLOC_WS_BYTES)
 NOALLOC_WS_BYTES = 32 << 20
@@ -274,6 +284,12 @@ class Plan:
     def kernel_names(self, backward: bool):
         bw = 1 if backward else 0
         return [_lib.bd_attn_plan_kernel_name(self.handle, bw, i).decode() for i in range(self.kernels(backward))]
+
+    def info(self) -> dict:
+        """The plan's scheduling choices and list sizes (bd_attn_plan_info)."""
+        r = PlanInfo()
+        _check(_lib.bd_attn_plan_info(self.handle, ctypes.byref(r)))
+        return {n: getattr(r, n) for n, _ in PlanInfo._fields_}
 
     def host_blob(self):
         buf = (ctypes.c_int32 * (self.meta_bytes // 4))()

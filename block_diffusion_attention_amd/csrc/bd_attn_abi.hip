@@ -398,6 +398,30 @@ const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int3
   return kernel_name(plan->p, backward != 0, i);
 }
 
+bd_attn_status bd_attn_plan_info(bd_attn_plan_t plan, bd_attn_plan_info_t* out) {
+  if (!plan) return fail(BD_ATTN_EINVAL, "plan is NULL");
+  if (!out) return fail(BD_ATTN_EINVAL, "out is NULL");
+  const Plan& p = plan->p;
+  bd_attn_plan_info_t r{};
+  r.split = p.split ? 1 : 0;
+  r.split_tiles = 0;
+  for (const auto& it : p.split_items)
+    if (it.kvh >= 0) r.split_tiles = std::max<int32_t>(r.split_tiles, it.kt_end - it.kt_begin);
+  r.split_grid = p.grid_parts > 0 ? 1 : 0;
+  r.fwd_vt = p.use_vt ? 1 : 0;
+  r.dkdv_masked = p.dkdv_masked ? 1 : 0;
+  r.debug_checks = p.checks ? 1 : 0;
+  r.query_tiles = (int64_t)p.qtiles.size();
+  r.key_tiles = (int64_t)p.ktiles.size();
+  r.fwd_workgroups = (int64_t)(p.desc.dtype != BD_ATTN_BF16 ? p.dq_items.size()
+                               : p.split ? p.split_items.size() : p.fwd_items.size());
+  r.dq_workgroups = (int64_t)p.dq_items.size();
+  r.dkdv_workgroups = (int64_t)p.bwd_items.size();
+  r.dkdv_split_tiles = (int64_t)p.bwd_merge.size();
+  *out = r;
+  return BD_ATTN_OK;
+}
+
 bd_attn_status bd_attn_plan_destroy(bd_attn_plan_t plan) {
   delete plan;
   return BD_ATTN_OK;

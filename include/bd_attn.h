@@ -258,6 +258,29 @@ int32_t bd_attn_plan_kernels(bd_attn_plan_t plan, int32_t backward);
  * is static. */
 const char* bd_attn_plan_kernel_name(bd_attn_plan_t plan, int32_t backward, int32_t i);
 
+/* The scheduling choices a plan made (all filled by bd_attn_plan_info). */
+typedef struct {
+  int32_t split;              /* 1: the forward splits key ranges (partials + merge) */
+  int32_t split_tiles;        /* key tiles (of 64 keys) per split part, 0 if not split */
+  int32_t split_grid;         /* 1: the split is a regular grid (one query tile, kv heads a
+                                 multiple of 8, part-major launch order): its workgroups
+                                 compute their part from their index instead of loading
+                                 their record */
+  int32_t fwd_vt;             /* 1: the forward goes through the transposed V copy */
+  int32_t dkdv_masked;        /* 1: dK/dV applies per-score row limits */
+  int32_t debug_checks;       /* 1: the kernels check their records (BD_ATTN_FLAG_DEBUG_CHECKS) */
+  int64_t query_tiles;        /* query tiles (up to 128 rows of one segment) */
+  int64_t key_tiles;          /* key tiles (up to 128 keys of one segment) */
+  int64_t fwd_workgroups;     /* workgroups of the forward attention kernel */
+  int64_t dq_workgroups;      /* workgroups of the dQ kernel */
+  int64_t dkdv_workgroups;    /* workgroups of the dK/dV kernel */
+  int64_t dkdv_split_tiles;   /* key tiles whose chunks are split over several workgroups */
+} bd_attn_plan_info_t;
+
+/* Fills *out with the plan's scheduling choices and list sizes (host only).
+ * Errors: EINVAL if plan or out is NULL. */
+bd_attn_status bd_attn_plan_info(bd_attn_plan_t plan, bd_attn_plan_info_t* out);
+
 /* ---------------------------------------------------------------------------
  * Host packer (ORL section 3.2 "Packed and cost-balanced state training",
  * appendix D.3): builds replay rows from captured denoising states and assigns

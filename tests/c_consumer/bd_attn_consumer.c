@@ -126,10 +126,15 @@ int main(int argc, char** argv) {
   expect(bd_attn_plan_serialize(plan, meta_host, meta_bytes - 4), BD_ATTN_EWORKSPACE, "plan_serialize(short)");
   free(meta_host);
 
+  bd_attn_plan_info_t info;
+  expect(bd_attn_plan_info(plan, &info), BD_ATTN_OK, "plan_info");
+  expect(bd_attn_plan_info(plan, NULL), BD_ATTN_EINVAL, "plan_info(NULL)");
   printf("{\"version\": \"%s\", \"tq\": %lld, \"tk\": %lld, \"meta_bytes\": %zu, \"ws_fwd\": %zu, "
-         "\"ws_bwd\": %zu, \"pairs\": %lld, \"fwd_kernels\": %d, \"bwd_kernels\": %d}\n",
+         "\"ws_bwd\": %zu, \"pairs\": %lld, \"fwd_kernels\": %d, \"bwd_kernels\": %d, \"split\": %d, "
+         "\"dkdv_masked\": %d, \"fwd_workgroups\": %lld, \"dkdv_workgroups\": %lld}\n",
          bd_attn_version(), (long long)tq, (long long)tk, meta_bytes, ws_fwd, ws_bwd, (long long)pairs,
-         (int)bd_attn_plan_kernels(plan, 0), (int)bd_attn_plan_kernels(plan, 1));
+         (int)bd_attn_plan_kernels(plan, 0), (int)bd_attn_plan_kernels(plan, 1), (int)info.split,
+         (int)info.dkdv_masked, (long long)info.fwd_workgroups, (long long)info.dkdv_workgroups);
   fflush(stdout);
 
   if (gpu_out) {

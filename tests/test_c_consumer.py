@@ -51,6 +51,9 @@ def test_c_program_plans_and_checks_on_the_host():
     assert (info["meta_bytes"], info["ws_fwd"], info["ws_bwd"]) == (p.meta_bytes, p.ws_fwd_bytes, p.ws_bwd_bytes)
     assert info["pairs"] == p.visible_pairs == orc.visible_pairs(META)
     assert (info["fwd_kernels"], info["bwd_kernels"]) == (p.kernels(False), p.kernels(True))
+    pi = p.info()
+    assert {k: info[k] for k in ("split", "dkdv_masked", "fwd_workgroups", "dkdv_workgroups")} == {
+        k: pi[k] for k in ("split", "dkdv_masked", "fwd_workgroups", "dkdv_workgroups")}
 
 
 def _read_bf16(raw, n, shape):

@@ -211,6 +211,7 @@ def test_regular_split_grid_reads_no_records():
         _say(f"case regular split grid: workload {k}")
         meta = W.config_meta(k, np.random.default_rng(k))
         plan, ref = C.run_case(b, meta, 0)
+        assert plan.info()["split_grid"] == (1 if grid else 0)
         blob = plan.host_blob()
         secs = C._sections(blob)
         so = C._rec(blob, secs, "split", 0)
@@ -244,6 +245,7 @@ def test_single_request_steps_on_the_regular_grid(shape):
     wl = W.random_workload(np.random.default_rng(ctx + hq), meta, sigma=0.5, with_do=False)
     gpu, plan = run_gpu(wl, backward=False)
     assert "merge" in plan.kernel_names(False)
+    assert plan.info()["split_grid"] == (1 if hkv % 8 == 0 else 0)
     _compare(wl, gpu, run_oracle(wl, backward=False))
     plan, ref = C.run_case(b, meta, 0)
     blob = plan.host_blob()

@@ -32,6 +32,32 @@ def test_exports_every_declared_function():
     assert set(b.EXPORTED) == names
 
 
+def test_plan_info_reports_the_plans_choices():
+    """bd_attn_plan_info against the decoded work lists and the documented rules."""
+    def info_and_lists(k, flags=0):
+        p = b.Plan(config_meta(k, np.random.default_rng(k)), flags)
+        return p.info(), decode(p.host_blob())
+
+    i2, r2 = info_and_lists(2)                                 # one request's denoising step
+    assert (i2["split"], i2["split_grid"], i2["split_tiles"]) == (1, 1, 2)
+    assert i2["fwd_workgroups"] == len(r2["split"]) and i2["query_tiles"] == len(r2["qtiles"]) == 1
+    assert b.Plan(config_meta(2, np.random.default_rng(2)), b.FLAG_NO_XCD).info()["split_grid"] == 0
+    i6, _ = info_and_lists(6)                                  # two query tiles: records
+    assert (i6["split"], i6["split_grid"]) == (1, 0)
+    i3, r3 = info_and_lists(3)                                 # packed replay
+    assert (i3["split"], i3["split_tiles"], i3["dkdv_masked"], i3["dkdv_split_tiles"]) == (0, 0, 0, 0)
+    assert (i3["fwd_workgroups"], i3["dq_workgroups"], i3["dkdv_workgroups"]) == (
+        len(r3["fwd"]), len(r3["dq"]), len(r3["bwd"]))
+    assert i3["key_tiles"] == len(r3["ktiles"])
+    i4, r4 = info_and_lists(4)                                 # staircase: split key tiles
+    assert i4["dkdv_split_tiles"] == len(r4["bmerge"]) > 0
+    assert info_and_lists(4, b.FLAG_FWD_VT)[0]["fwd_vt"] == 1 and i4["fwd_vt"] == 0
+    assert info_and_lists(4, b.FLAG_DEBUG_CHECKS)[0]["debug_checks"] == 1 and i4["debug_checks"] == 0
+    i1, r1 = info_and_lists(1)                                 # fp32: the forward runs the dQ items
+    assert i1["fwd_workgroups"] == i1["dq_workgroups"] == len(r1["dq"])
+    assert b._lib.bd_attn_plan_info(None, None) == b.EINVAL
+
+
 def test_device_check_query_rejects_null_and_flag_is_accepted():
     # no HIP call is made for a NULL count
     assert b._lib.bd_attn_device_check_errors(None, 0) == b.EINVAL
