@@ -133,6 +133,78 @@ def traffic_from_profiles(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def useful_flop(D, Hq, pairs, backward):
+    """Useful FLOPs of one step: 4*D per visible (query row, key) pair and query head
+    for the forward (S = Q K^T, then P V), and 10*D more for the backward (S
+    recomputed, dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K)."""
+    return (4.0 + (10.0 if backward else 0.0)) * D * Hq * pairs
+
+
+def pass_rates(avg_ms, fwd_names, bwd_names, D, Hq, pairs, peak):
+    """Useful rate of each pass on its own: the forward's 4*D and the backward's 10*D
+    FLOP per visible pair and query head, over the summed average durations of that
+    pass's kernels (bwd_names None: forward only)."""
+    fwd_ms = sum(avg_ms[n] for n in fwd_names)
+    passes = {"fwd": {"ms": round(fwd_ms, 4),
+                      "useful_tflops": round(4.0 * D * Hq * pairs / (fwd_ms * 1e-3) / 1e12, 2)}}
+    if bwd_names is not None:
+        bwd_ms = sum(avg_ms[n] for n in bwd_names)
+        passes["bwd"] = {"ms": round(bwd_ms, 4),
+                         "useful_tflops": round(10.0 * D * Hq * pairs / (bwd_ms * 1e-3) / 1e12, 2)}
+    for p_ in passes.values():
+        p_["pct_of_peak"] = round(100.0 * p_["useful_tflops"] / peak, 2)
+    return passes
+
+
+def kernel_work(k, dtype, D, Hq, Hkv, tq, tk, pairs):
+    """Algorithmic work per launch of each kernel, as (bound, FLOPs or bytes).
+
+    MFMA kernels count the products they execute per visible pair and query head
+    (forward 4*D; dK/dV 8*D: S, dP, dV, dK; dQ 6*D: S, dP, dQ). The serving steps'
+    forward is priced in the bytes it must read (Q, K, V once each); its O and LSE
+    leave through the split partials and the merge."""
+    esz = 2 if dtype == "bf16" else 4
+    q_bytes = tq * Hq * D * esz
+    kv_bytes = tk * Hkv * D * esz
+    algo = {
+        "fwd": ("mfma", 4.0 * D * Hq * pairs),
+        "dkdv": ("mfma", 8.0 * D * Hq * pairs),
+        "dq": ("mfma", 6.0 * D * Hq * pairs),
+        "bwd_pre": ("hbm", 2.0 * q_bytes + 3.0 * tq * Hq * 4),
+        "merge": ("hbm", q_bytes + tq * Hq * 4),
+        "transpose_v": ("hbm", 2.0 * kv_bytes),
+    }
+    if k in FWD_ONLY:   # the serving steps are bandwidth-bound: their forward is priced in bytes
+        algo["fwd"] = ("hbm", float(q_bytes + 2 * kv_bytes))
+    algo["dkdv_masked"] = algo["dkdv"]
+    return algo
+
+
+def roofline(avg_ms, algo, peak, k):
+    """Roofline object of the dominant kernel (largest mean duration): its algorithmic
+    work per launch over its mean launch duration, against the bf16 MFMA or HBM peak."""
+    dom = max(avg_ms, key=lambda n: avg_ms[n])
+    bound, work = algo[dom]
+    dur_s = avg_ms[dom] * 1e-3
+    if bound == "mfma":
+        achieved = work / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4),
+                # the products the kernel itself executes, which for the two backward
+                # kernels (8*D and 6*D per pair) sum to more than the pass's useful 10*D
+                "work_kind": "executed MFMA FLOPs of this kernel"}
+    else:
+        achieved = work / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "work_kind": "compulsory bytes of this kernel"}
+    roof["kernel"] = dom
+    roof["work_per_launch"] = work
+    roof["avg_launch_ms"] = round(avg_ms[dom], 4)
+    roof["traffic"] = traffic_from_profiles(dom, k)
+    return roof
+
+
 KERNEL_SYMBOLS = {"fwd": "fwd_", "merge": "merge_kernel", "bwd_pre": "bwd_pre_kernel",
                   "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel", "transpose_v": "transpose_v_kernel",
                   "aec_entropy": "aec_entropy_kernel", "aec_grad": "aec_grad_kernel"}
@@ -690,56 +762,12 @@ def main():
 
     D, Hq = m.head_dim, m.num_q_heads
     pairs = plan.visible_pairs
-    useful = (4.0 + (10.0 if backward else 0.0)) * D * Hq * pairs
+    useful = useful_flop(D, Hq, pairs, backward)
     value = useful / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if m.dtype == "bf16" else PEAK_FP32_TFLOPS
-    # useful rate of each pass on its own: the forward's 4*D and the backward's
-    # 10*D FLOP per visible (row, key) pair and q head, over the summed average
-    # durations of that pass's kernels
-    fwd_ms = sum(avg_ms[n] for n in fwd_names)
-    passes = {"fwd": {"ms": round(fwd_ms, 4),
-                      "useful_tflops": round(4.0 * D * Hq * pairs / (fwd_ms * 1e-3) / 1e12, 2)}}
-    if backward:
-        bwd_ms = sum(avg_ms[n] for n in bwd_names)
-        passes["bwd"] = {"ms": round(bwd_ms, 4),
-                         "useful_tflops": round(10.0 * D * Hq * pairs / (bwd_ms * 1e-3) / 1e12, 2)}
-    for p_ in passes.values():
-        p_["pct_of_peak"] = round(100.0 * p_["useful_tflops"] / peak, 2)
-
-    # algorithmic work per launch of each kernel
-    esz = 2 if m.dtype == "bf16" else 4
-    q_bytes = plan.tq * Hq * D * esz
-    kv_bytes = plan.tk * m.num_kv_heads * D * esz
-    algo = {
-        "fwd": ("mfma", 4.0 * D * Hq * pairs),
-        "dkdv": ("mfma", 8.0 * D * Hq * pairs),
-        "dq": ("mfma", 6.0 * D * Hq * pairs),
-        "bwd_pre": ("hbm", 2.0 * q_bytes + 3.0 * plan.tq * Hq * 4),
-        "merge": ("hbm", q_bytes + plan.tq * Hq * 4),
-        "transpose_v": ("hbm", 2.0 * kv_bytes),
-    }
-    if k in FWD_ONLY:   # the serving steps are bandwidth-bound: their forward is priced in bytes
-        algo["fwd"] = ("hbm", float(q_bytes + 2 * kv_bytes))
-    algo["dkdv_masked"] = algo["dkdv"]
-    dom = max(avg_ms, key=lambda n: avg_ms[n])
-    bound, work = algo[dom]
-    dur_s = avg_ms[dom] * 1e-3
-    if bound == "mfma":
-        achieved = work / dur_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4),
-                # the products the kernel itself executes, which for the two backward
-                # kernels (8*D and 6*D per pair) sum to more than the pass's useful 10*D
-                "work_kind": "executed MFMA FLOPs of this kernel"}
-    else:
-        achieved = work / dur_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "work_kind": "compulsory bytes of this kernel"}
-    roof["kernel"] = dom
-    roof["work_per_launch"] = work
-    roof["avg_launch_ms"] = round(avg_ms[dom], 4)
-    roof["traffic"] = traffic_from_profiles(dom, k)
+    passes = pass_rates(avg_ms, fwd_names, bwd_names if backward else None, D, Hq, pairs, peak)
+    algo = kernel_work(k, m.dtype, D, Hq, m.num_kv_heads, plan.tq, plan.tk, pairs)
+    roof = roofline(avg_ms, algo, peak, k)
     # rocprofv3 counters of the kernels (profiles/mfma.json; null when stale or absent)
     counters = {n: mfma_from_profiles(n, k) for n in avg_ms if algo.get(n, ("",))[0] == "mfma"}
 
