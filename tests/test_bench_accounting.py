@@ -139,3 +139,76 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert r.stdout == ""
     assert "exactly one GPU" in r.stderr
+
+
+CC_HEADER = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+             "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+             "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+DKDV = "void bdattn::(anonymous namespace)::dkdv_bf16_kernel<128, false, false>(bdattn::BwdArgs)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>, std::array<char*, 3ul> >(int)"
+
+
+def _write_csv(path, header, rows):
+    import csv
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _cc_row(dispatch, kernel, counter, value, t0, t1):
+    return [dispatch, dispatch, "Agent 1", 1, 1, 1, 256, 1, kernel, 256, 0, 0, 128, 0, 32, counter, value, t0, t1]
+
+
+def test_summary_of_profiler_output(tmp_path, monkeypatch, capsys):
+    """The profile summaries' arithmetic on synthetic rocprofv3 output: the copy
+    probe's scale factor and the bytes per launch it gives, and the MFMA busy
+    fraction, clock and executed FLOPs of a kernel."""
+    import argparse
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "src_hash", lambda files: "h")
+    monkeypatch.setattr(bench, "MFMA_STATS", {})
+    (tmp_path / "profiles").mkdir()
+    # kernel statistics
+    _write_csv(tmp_path / "kt" / "run_kernel_stats.csv",
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+               [[DKDV, 3, 3600000, 1200000, 70.0, 1100000, 1300000]])
+    # FETCH_SIZE (KiB per dispatch): the 256 MiB copy probe's largest dispatch counts
+    # 2 x 256 MiB, so the scale factor is 0.5; dK/dV counts 1000 and 1200 KiB in its
+    # two dispatches
+    probe = 2 * 256 * 1024.0
+    _write_csv(tmp_path / "fs" / "run_counter_collection.csv", CC_HEADER,
+               [_cc_row(1, COPY, "FETCH_SIZE", 4.0, 0, 10),
+                _cc_row(2, COPY, "FETCH_SIZE", probe, 0, 10),
+                _cc_row(3, DKDV, "FETCH_SIZE", 1000.0, 0, 10),
+                _cc_row(4, DKDV, "FETCH_SIZE", 1200.0, 0, 10)])
+    args = argparse.Namespace(summarize=[str(tmp_path / "kt"), str(tmp_path / "fs")], command="cmd",
+                              copy_probe_mb=256, summary_out=str(tmp_path / "s.md"), mfma_key=None,
+                              traffic_key="dkdv@3")
+    bench.summarize(args)
+    text = (tmp_path / "s.md").read_text()
+    assert "| bdattn::dkdv_bf16_kernel<128, false, false> | 3 | 1200.00 | 1100.00 | 1300.00 | 70.0 |" in text
+    assert "FETCH_SIZE=0.5000" in text
+    rec = json.loads((tmp_path / "profiles" / "traffic.json").read_text())["dkdv@3"]
+    assert rec["bytes_per_launch"] == pytest.approx(1100.0 * 1024 * 0.5)
+    assert rec["src_sha256"] == "h" and rec["command"] == "cmd"
+    # MFMA counters of two dispatches of 1 ms: GRBM_GUI_ACTIVE summed over the 8 XCDs
+    # is 8 x 1.7e6 cycles (1.7 GHz), the 1,024 SIMDs were MFMA-busy for half of them,
+    # and 2e9 MFMA operations of 512 FLOPs each ran
+    cyc = 1.7e6
+    rows = []
+    for d in (1, 2):
+        for name, val in (("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * cyc * 1024), ("GRBM_GUI_ACTIVE", 8 * cyc),
+                          ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 2e9)):
+            rows.append(_cc_row(d, DKDV, name, val, 0, 1000000))
+    _write_csv(tmp_path / "mf" / "run_counter_collection.csv", CC_HEADER, rows)
+    args = argparse.Namespace(summarize=[str(tmp_path / "mf")], command="cmd2", copy_probe_mb=0,
+                              summary_out=None, mfma_key=["dkdv@3"], traffic_key=None)
+    bench.summarize(args)
+    m = json.loads((tmp_path / "profiles" / "mfma.json").read_text())["dkdv@3"]
+    assert m["mfma_busy"] == 0.5
+    assert m["clock_ghz"] == 1.7
+    assert m["executed_tflops"] == pytest.approx(2e9 * 512 / 1e-3 / 1e12, abs=0.1)
+    assert m["profiled_us"] == 1000.0
+    assert m["src_sha256"] == "h"
