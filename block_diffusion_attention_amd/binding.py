@@ -24,6 +24,7 @@ FLAG_NO_SPLIT, FLAG_FORCE_SPLIT, FLAG_NO_XCD, FLAG_FWD_DIRECT, FLAG_FWD_VT = 1, 
 FLAG_CLEAN_CAUSAL = 32
 FLAG_CHECK_PLAN = 64
 FLAG_DEBUG_CHECKS = 128
+FLAG_DKDV_RUNS = 1 << 16
 
 
 def flag_split_tiles(n: int) -> int:

@@ -22,17 +22,24 @@ namespace bdattn {
 namespace {
 
 constexpr int kNumXcd = 8;
+// dK/dV key tiles per run under BD_ATTN_FLAG_DKDV_RUNS (see launch_order).
+constexpr int kDkdvRun = 4;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Orders work items for launch: workgroup i is dispatched to XCD i % 8. Items
 // of one affinity class (same segment and kv head, i.e. the same K/V or Q/dO
 // rows) are kept on one XCD so they share its L2; classes go to XCDs
-// largest-total-first; inside an XCD items run largest-cost-first. Falls back to
-// one global largest-cost-first order when the class split is unbalanced.
+// largest-total-first; inside an XCD items run largest-cost-first. With run > 1,
+// the largest remaining item of an XCD opens a run that also takes the next
+// run - 1 largest remaining items of its class, so that items of one class start
+// together and read the same rows at about the same time (under the plain order,
+// each segment has about one dK/dV key tile per cost level, so the tiles running
+// at one time come from different segments). Falls back to one global
+// largest-cost-first order when the class split is unbalanced.
 // Returns item indices, -1 for empty slots.
 std::vector<int32_t> launch_order(const std::vector<int64_t>& cost,
-                                  const std::vector<int64_t>& cls, bool xcd_groups) {
+                                  const std::vector<int64_t>& cls, bool xcd_groups, int run = 1) {
   const int64_t n = (int64_t)cost.size();
   std::vector<int32_t> idx(n);
   std::iota(idx.begin(), idx.end(), 0);
@@ -69,6 +76,31 @@ std::vector<int32_t> launch_order(const std::vector<int64_t>& cost,
 
   std::vector<std::vector<int32_t>> per(kNumXcd);
   for (int32_t i : idx) per[cx[cls[i]]].push_back(i);       // idx is already cost-sorted
+  if (run > 1) {
+    // A class lives on one XCD, and both lists keep idx's order, so the first item
+    // of a class not yet placed is the XCD's first item not yet placed when it
+    // opens a run.
+    std::vector<std::vector<int32_t>> of_cls(ncls);
+    for (int32_t i : idx) of_cls[cls[i]].push_back(i);
+    std::vector<size_t> next(ncls, 0);
+    std::vector<char> placed(n, 0);
+    for (auto& lst : per) {
+      std::vector<int32_t> out;
+      out.reserve(lst.size());
+      for (int32_t i : lst) {
+        if (placed[i]) continue;
+        const int64_t c = cls[i];
+        for (int taken = 0; taken < run && next[c] < of_cls[c].size(); ++next[c]) {
+          const int32_t k = of_cls[c][next[c]];
+          if (placed[k]) continue;
+          placed[k] = 1;
+          out.push_back(k);
+          ++taken;
+        }
+      }
+      lst.swap(out);
+    }
+  }
   size_t rows = 0;
   for (auto& p : per) rows = std::max(rows, p.size());
   std::vector<int32_t> out(rows * kNumXcd, -1);
@@ -484,7 +516,7 @@ bd_attn_status build_plan(const bd_attn_desc* d, Plan* P, std::string* err) {
     }
     p.n_dkv_slots = slots;
     if ((int64_t)Hkv * (slots + 1) + Hkv > INT32_MAX) { *err = "too many dK/dV partial slots"; return BD_ATTN_EUNSUPPORTED; }
-    auto ord = launch_order(cost, cls, xcd);
+    auto ord = launch_order(cost, cls, xcd, (d->flags & BD_ATTN_FLAG_DKDV_RUNS) ? kDkdvRun : 1);
     for (int32_t o : ord) p.bwd_items.push_back(o < 0 ? BwdItem{-1, 0, 0, 0} : raw[o]);
   }
 

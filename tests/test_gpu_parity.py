@@ -539,6 +539,22 @@ def test_backward_is_deterministic():
         assert np.array_equal(g1[n], g2[n]), n
 
 
+def test_dkdv_runs_order_gives_the_same_bits():
+    # Each dK/dV workgroup owns its key tile (no atomics), so launching the items in
+    # runs of one class (BD_ATTN_FLAG_DKDV_RUNS) must reproduce the default's
+    # outputs bit for bit. A 16-segment pack, on which the two orders differ.
+    rng = np.random.default_rng(46)
+    n = rng.integers(2, 17, size=16)
+    meta = W.Meta([int(32 * x) for x in n], [0] * 16, [[int(x)] for x in n], 32, 32, 8, 128, "bf16")
+    assert b.Plan(meta, b.FLAG_DKDV_RUNS).host_blob() != b.Plan(meta).host_blob()
+    wl = W.random_workload(rng, meta, sigma=0.5)
+    _say(f"case dK/dV runs order tq={meta.tq} tk={meta.tk}")
+    g1, _ = run_gpu(wl)
+    g2, _ = run_gpu(wl, flags=b.FLAG_DKDV_RUNS)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(g1[name], g2[name]), name
+
+
 def test_autograd_function():
     rng = np.random.default_rng(45)
     meta = W.Meta([128], [0], [[1, 4]], 32, 4, 1, 64, "bf16")

@@ -479,7 +479,7 @@ def _sections(blob):
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 6])
-@pytest.mark.parametrize("flags", [0, b.FLAG_NO_XCD, b.FLAG_FORCE_SPLIT, b.FLAG_NO_SPLIT])
+@pytest.mark.parametrize("flags", [0, b.FLAG_NO_XCD, b.FLAG_FORCE_SPLIT, b.FLAG_NO_SPLIT, b.FLAG_DKDV_RUNS])
 def test_plan_self_check_accepts_every_plan(k, flags):
     meta = config_meta(k, np.random.default_rng(k))
     p = b.Plan(meta, flags | b.FLAG_CHECK_PLAN)   # bd_attn_plan runs the check itself
@@ -563,3 +563,57 @@ def test_transposed_v_copy_only_below_its_offset_range():
     n = (1 << 30) // 128                         # keys at which D * tk_pad * 2 reaches 2^31
     big = Meta([n], [n], [[n // 32]], 32, 4, 1, 128, "bf16")   # canvas-only: few query tiles
     assert "transpose_v" not in b.Plan(big, b.FLAG_FWD_VT).kernel_names(False)
+
+
+def _bwd_launch(meta, flags):
+    """dK/dV items in launch order as (XCD, class, cost, record); None for empty slots."""
+    import bisect
+    rec = decode(b.Plan(meta, flags).host_blob())
+    G = meta.num_q_heads // meta.num_kv_heads
+    qct = 64 // G
+    cpc = -(-meta.block_size // qct)
+    koff = meta.k_offsets()
+    out = []
+    for i, it in enumerate(rec["bwd"]):
+        if it[0] < 0:
+            out.append(None)
+            continue
+        kt = rec["ktiles"][it[0]]
+        nall = -(-int(kt[4]) // qct) + int(kt[7]) * cpc
+        cost = min(int(it[3]), nall) - min(int(it[2]), nall)
+        seg = bisect.bisect_right(koff, int(kt[0])) - 1
+        out.append((i % 8, (seg, int(it[1]) % meta.num_kv_heads), cost, tuple(int(x) for x in it)))
+    return rec, out
+
+
+def test_dkdv_runs_flag_reorders_the_dkdv_items_only():
+    """BD_ATTN_FLAG_DKDV_RUNS: the same dK/dV items on the same XCDs, only launched
+    in runs of one (segment, kv head) class; every other record is unchanged."""
+    meta = config_meta(3, np.random.default_rng(3))
+    rec0, d0 = _bwd_launch(meta, 0)
+    rec1, d1 = _bwd_launch(meta, b.FLAG_DKDV_RUNS)
+    for name in ("qtiles", "fwd", "split", "merge", "dq", "ktiles", "canvq", "bmerge"):
+        assert np.array_equal(rec0[name], rec1[name]), name
+    live0 = [x for x in d0 if x is not None]
+    live1 = [x for x in d1 if x is not None]
+    assert sorted(x[3] for x in live0) == sorted(x[3] for x in live1)
+    assert [x[3] for x in live0] != [x[3] for x in live1]
+    switches = []
+    for x in range(8):
+        s0 = [e for e in d0 if e is not None and e[0] == x]
+        s1 = [e for e in d1 if e is not None and e[0] == x]
+        assert sorted(e[3] for e in s0) == sorted(e[3] for e in s1)      # same XCD
+        assert s1[0][2] == max(e[2] for e in s1)                          # opens with the largest
+        for cls in {e[1] for e in s1}:                                    # a class largest first
+            costs = [e[2] for e in s1 if e[1] == cls]
+            assert costs == sorted(costs, reverse=True)
+        switches.append((sum(a[1] != c[1] for a, c in zip(s0, s0[1:])),
+                         sum(a[1] != c[1] for a, c in zip(s1, s1[1:]))))
+    # runs of up to 4 tiles of a class: far fewer class switches on each XCD
+    assert all(n1 * 2 < n0 for n0, n1 in switches), switches
+
+
+def test_dkdv_runs_flag_keeps_single_segment_order():
+    # one segment: each XCD holds one class, whose items are already in launch order
+    meta = config_meta(4, np.random.default_rng(4))
+    assert b.Plan(meta, b.FLAG_DKDV_RUNS).host_blob() == b.Plan(meta).host_blob()
