@@ -180,6 +180,13 @@ def kernel_work(k, dtype, D, Hq, Hkv, tq, tk, pairs):
     return algo
 
 
+def step_bytes(dtype, D, Hq, Hkv, tq, tk):
+    """Compulsory HBM bytes of one forward call: Q, K and V read once, O and LSE
+    written once (9,048,064 B for the single-request denoising step)."""
+    esz = 2 if dtype == "bf16" else 4
+    return 2 * tq * Hq * D * esz + 2 * tk * Hkv * D * esz + tq * Hq * 4
+
+
 def roofline(avg_ms, algo, peak, k):
     """Roofline object of the dominant kernel (largest mean duration): its algorithmic
     work per launch over its mean launch duration, against the bf16 MFMA or HBM peak."""
@@ -397,7 +404,7 @@ def _summarize_sq(rows):
 COLD_SETS = 48      # distinct input sets a cold serving-step run rotates over
 
 
-def cold_serving(plan, q, k, v, o, lse, fwd_names, algo, steps):
+def cold_serving(plan, q, k, v, o, lse, fwd_names, algo, steps, step_b):
     """The serving step with its inputs out of cache: the forward rotates over
     COLD_SETS distinct copies of Q, K, V (and outputs), several hundred MB in all,
     more than the last-level cache holds, so every call reads its Q/K/V from HBM.
@@ -429,7 +436,19 @@ def cold_serving(plan, q, k, v, o, lse, fwd_names, algo, steps):
     return {"buffer_sets": COLD_SETS, "bytes_rotated": per_set * COLD_SETS, "steps": n,
             "ms_per_step": round(ms_step, 4), "kernels_ms": {name: round(t, 4) for name, t in kern.items()},
             "fwd_GBps": round(fwd_bytes / (kern["fwd"] * 1e-3) / 1e9, 1),
-            "step_GBps": round(fwd_bytes / (ms_step * 1e-3) / 1e9, 1)}
+            "step_GBps": round(step_b / (ms_step * 1e-3) / 1e9, 1)}
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(wl, budget_s):
@@ -467,6 +486,7 @@ def cpu_baseline(wl, budget_s):
         "value": flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{len(done)} of {len(order)} (segment, kv head) slices ({frac:.1%} of the work), "
                   f"{'fwd+bwd' if backward else 'fwd'}, fp64 numpy, {t_total:.1f} s",
@@ -521,7 +541,8 @@ def pack_bench(args):
         t0 = time.perf_counter()
         po.pack(clean.tolist(), off.tolist(), states, B, G, 1, 1, 4)
         to = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": round(N / to, 1), "unit": "states/s", "cores": 1, "kind": "oracle",
+        out["cpu_baseline"] = {"value": round(N / to, 1), "unit": "states/s", "cores": 1,
+                               "cpu_model": cpu_model(), "kind": "oracle",
                                "sample": f"the whole batch ({N} states), pure Python, {to:.2f} s"}
     print(json.dumps(out), flush=True)
 
@@ -642,7 +663,7 @@ def aec_bench(args):
                             [], [], [], wl.rho, wl.gate_max)
         to = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": round(rows * V * 2 / to / 1e9, 3), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle", "sample": f"{rows} of {N} rows (normalizer and entropy"
+                               "cpu_model": cpu_model(), "kind": "oracle", "sample": f"{rows} of {N} rows (normalizer and entropy"
                                                            f"{', then the gradient' if backward else ''}), "
                                                            f"fp64 numpy, {to:.2f} s"}
     print(json.dumps(out), flush=True)
@@ -771,7 +792,13 @@ def main():
     # rocprofv3 counters of the kernels (profiles/mfma.json; null when stale or absent)
     counters = {n: mfma_from_profiles(n, k) for n in avg_ms if algo.get(n, ("",))[0] == "mfma"}
 
-    cold = cold_serving(plan, q, kk, v, o, lse, fwd_names, algo, K) if k in FWD_ONLY else None
+    serving = None
+    if k in FWD_ONLY:   # the step's compulsory bytes over its time, hot and cold
+        sb = step_bytes(m.dtype, D, Hq, m.num_kv_heads, plan.tq, plan.tk)
+        serving = {"compulsory_bytes": sb, "GBps": round(sb / (ms_step * 1e-3) / 1e9, 1),
+                   "pct_of_hbm": round(100.0 * sb / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+    cold = cold_serving(plan, q, kk, v, o, lse, fwd_names, algo, K, serving["compulsory_bytes"]) \
+        if k in FWD_ONLY else None
 
     if args.copy_probe_mb:
         n = args.copy_probe_mb * 2**20 // 4
@@ -820,6 +847,8 @@ def main():
     }
     if any(v is not None for v in counters.values()):
         out["mfma_counters"] = counters
+    if serving is not None:
+        out["step_bytes"] = serving
     if cold is not None:
         out["cold"] = cold
     print(json.dumps(out), flush=True)

@@ -212,3 +212,16 @@ def test_summary_of_profiler_output(tmp_path, monkeypatch, capsys):
     assert m["executed_tflops"] == pytest.approx(2e9 * 512 / 1e-3 / 1e12, abs=0.1)
     assert m["profiled_us"] == 1000.0
     assert m["src_sha256"] == "h"
+
+
+def test_denoising_step_compulsory_bytes():
+    # Q (32 x 32 x 128 bf16) and O read/written once, K and V (2,080 x 8 x 128 bf16) read
+    # once, LSE (32 x 32 fp32) written once: the step's GB/s is these bytes over its time
+    meta, plan = _plan(2)
+    assert bench.step_bytes("bf16", 128, 32, 8, plan.tq, plan.tk) == 9048064
+    assert bench.step_bytes("fp32", 64, 2, 1, 80, 80) == 2 * 80 * 2 * 64 * 4 + 2 * 80 * 64 * 4 + 80 * 2 * 4
+
+
+def test_cpu_model_is_named():
+    name = bench.cpu_model()
+    assert name is None or (isinstance(name, str) and name)
