@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kNumXcd = 8;
 // dK/dV key tiles per run under BD_ATTN_FLAG_DKDV_RUNS (see launch_order).
-constexpr int kDkdvRun = 4;
+constexpr int kDkdvRun = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

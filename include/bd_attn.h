@@ -108,15 +108,15 @@ typedef enum { BD_ATTN_BF16 = 0, BD_ATTN_FP32 = 1 } bd_attn_dtype;
                                          CHECK_PLAN */
 #define BD_ATTN_FLAG_SPLIT_TILES(n) ((((uint32_t)(n)) & 0xffu) << 8)
 #define BD_ATTN_FLAG_DKDV_RUNS (1u << 16) /* dK/dV: launch the key tiles of one (segment,
-                                       kv head) in runs of 4 on one XCD, so that tiles
+                                       kv head) in runs of 8 on one XCD, so that tiles
                                        walking the same query chunks start together and
                                        fetch each chunk into the XCD's L2 once. On packs
-                                       of many segments the kernel fetches less than half
-                                       the HBM bytes, but runs slower on MI355X (8 % on
-                                       the 16-segment packed replay), so it is off by
-                                       default: for callers that share HBM bandwidth with
-                                       other work. No effect with NO_XCD, or when the
-                                       plan falls back to one global order. */
+                                       of many segments the kernel fetches about a third
+                                       of the HBM bytes, but runs slower on MI355X (about
+                                       8 % on the 16-segment packed replay), so it is off
+                                       by default: for callers that share HBM bandwidth
+                                       with other work. No effect with NO_XCD, or when
+                                       the plan falls back to one global order. */
 
 typedef struct bd_attn_plan_s* bd_attn_plan_t;
 

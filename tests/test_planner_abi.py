@@ -609,7 +609,7 @@ def test_dkdv_runs_flag_reorders_the_dkdv_items_only():
             assert costs == sorted(costs, reverse=True)
         switches.append((sum(a[1] != c[1] for a, c in zip(s0, s0[1:])),
                          sum(a[1] != c[1] for a, c in zip(s1, s1[1:]))))
-    # runs of up to 4 tiles of a class: far fewer class switches on each XCD
+    # runs of up to 8 tiles of a class: far fewer class switches on each XCD
     assert all(n1 * 2 < n0 for n0, n1 in switches), switches
 
 
