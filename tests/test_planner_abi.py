@@ -617,3 +617,11 @@ def test_dkdv_runs_flag_keeps_single_segment_order():
     # one segment: each XCD holds one class, whose items are already in launch order
     meta = config_meta(4, np.random.default_rng(4))
     assert b.Plan(meta, b.FLAG_DKDV_RUNS).host_blob() == b.Plan(meta).host_blob()
+
+
+@pytest.mark.parametrize("k", [3, 5])
+def test_dkdv_runs_flag_has_no_effect_without_xcd_grouping(k):
+    # the runs are formed inside each XCD's list; with NO_XCD there is one global order
+    meta = config_meta(k, np.random.default_rng(k))
+    assert (b.Plan(meta, b.FLAG_NO_XCD | b.FLAG_DKDV_RUNS).host_blob() ==
+            b.Plan(meta, b.FLAG_NO_XCD).host_blob())
